@@ -1,0 +1,38 @@
+"""CPU oracle for the Flint MoE feed-forward layer — TEST INFRASTRUCTURE ONLY.
+
+This package is the plain, slow, fp64 reference that the HIP path is graded
+against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import it.  The product path
+(``sparse_expert_gemv_amd``) never imports, links or calls anything here, and
+this package never imports the product path: the two share no code.  The only
+module both sides use is ``synth`` (seeded input generation, no layer
+arithmetic).
+
+Pins (tests marked ``not gpu`` in ``tests/test_oracle_*.py``): every function
+below is checked against something other than itself — closed forms, brute
+force over all subsets on tiny inputs, structured weights whose output has a
+closed form, invariants of the layer (shared-expert-only output, permutation
+equivariance, batch independence, linearity), special cases that reduce to a
+dense mixture, and the FP8/FP4 code tables of the format definitions.
+
+Parity unpinned: agreement with Recursive's own runtime at the real Flint
+shape cannot be checked here (neither that runtime nor trained weights are
+available); the pages print no worked numeric example of the layer.
+"""
+
+from .moe import (  # noqa: F401
+    OracleLayer,
+    TokenResult,
+    bf16_to_f64,
+    router_logits,
+    sigmoid,
+    silu,
+    select_topk,
+    routing_weights,
+    expert_forward,
+    moe_token,
+    moe_forward,
+    bucket,
+    route_all,
+)
+from .nvfp4 import e2m1_to_f64, e4m3fn_to_f64, nvfp4_dequant  # noqa: F401

@@ -1,0 +1,159 @@
+"""Seeded synthetic Flint-shaped MoE layers.
+
+Shapes follow the layer the pages describe: hidden size 2048 ("vLLM Day-0
+Support for Recursive's Flint", section "Flint Model Architecture"), 256 routed
+experts with sigmoid top-6 routing plus one shared expert (same page and
+section, "MoE Structure" bullet; also "Flint on Arc Pro B70", section "Setup").
+The expert intermediate size is not printed on the pages; 512 is the reading
+that makes the stated parameter totals (39.8B total, 2.5B active) come out.
+
+Value distributions (the pages publish no weights):
+  router weight  bf16 [E, H]          ~ N(0, 0.02)
+  expert w13     bf16 [2*I, H]        ~ N(0, 0.02)   rows [0, I) gate, [I, 2I) up
+  expert w2      bf16 [H, I]          ~ N(0, 0.02)
+  router bias    fp32 [E]             ~ N(0, 1)      (skewed-load workload only)
+  x              bf16 [T, H]          ~ N(0, 1)
+
+Every tensor has its own random stream, spawned from one integer seed in a
+fixed order, so any single tensor can be regenerated without the others:
+  child 0            router weight
+  child 1, 2         shared expert w13, w2
+  child 3+2e, 4+2e   routed expert e w13, w2
+  child 3+2E         router bias
+Activations use a separate SeedSequence keyed by (seed, T, x_seed).
+
+fp32 -> bf16 conversion is round-to-nearest-even on the bit pattern.
+"""
+
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+import os
+
+import numpy as np
+
+FLINT_HIDDEN = 2048
+FLINT_N_EXPERTS = 256
+FLINT_TOP_K = 6
+FLINT_INTER = 512
+
+WEIGHT_STD = 0.02
+X_STD = 1.0
+BIAS_STD = 1.0
+
+_X_DOMAIN = 0x5EED_0001  # keeps activation streams apart from weight streams
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    hidden: int = FLINT_HIDDEN
+    n_experts: int = FLINT_N_EXPERTS
+    top_k: int = FLINT_TOP_K
+    inter: int = FLINT_INTER
+
+
+def _normal_bf16(seq: np.random.SeedSequence, shape, std: float) -> np.ndarray:
+    rng = np.random.default_rng(seq)
+    v = rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
+    v *= np.float32(std)
+    return f32_to_bf16_bits(v).reshape(shape)
+
+
+class SyntheticLayer:
+    """One seeded MoE layer.  Tensors are generated on first use and cached."""
+
+    def __init__(self, seed: int = 0, shape: LayerShape = LayerShape()):
+        self.seed = int(seed)
+        self.shape = shape
+        E = shape.n_experts
+        self._children = np.random.SeedSequence(self.seed).spawn(4 + 2 * E)
+        self._cache: dict = {}
+
+    # -- single tensors ---------------------------------------------------
+    def router_w(self) -> np.ndarray:
+        """bf16 bits [E, H]."""
+        key = "router_w"
+        if key not in self._cache:
+            s = self.shape
+            self._cache[key] = _normal_bf16(self._children[0], (s.n_experts, s.hidden), WEIGHT_STD)
+        return self._cache[key]
+
+    def router_bias(self) -> np.ndarray:
+        """fp32 [E] ~ N(0, 1): the skewed-load workload's per-expert offset."""
+        key = "router_b"
+        if key not in self._cache:
+            E = self.shape.n_experts
+            rng = np.random.default_rng(self._children[3 + 2 * E])
+            self._cache[key] = (rng.standard_normal(E, dtype=np.float32) * np.float32(BIAS_STD)).astype(np.float32)
+        return self._cache[key]
+
+    def _child_w13(self, e: int):
+        return self._children[1] if e < 0 else self._children[3 + 2 * e]
+
+    def _child_w2(self, e: int):
+        return self._children[2] if e < 0 else self._children[4 + 2 * e]
+
+    def w13(self, e: int) -> np.ndarray:
+        """bf16 bits [2I, H] of routed expert e, or of the shared expert if e < 0."""
+        s = self.shape
+        return _normal_bf16(self._child_w13(e), (2 * s.inter, s.hidden), WEIGHT_STD)
+
+    def w2(self, e: int) -> np.ndarray:
+        """bf16 bits [H, I] of routed expert e, or of the shared expert if e < 0."""
+        s = self.shape
+        return _normal_bf16(self._child_w2(e), (s.hidden, s.inter), WEIGHT_STD)
+
+    # -- whole banks --------------------------------------------------------
+    def routed_banks(self, threads: int | None = None):
+        """(w13 [E, 2I, H], w2 [E, H, I]) bf16 bits, generated in parallel."""
+        if "banks" not in self._cache:
+            s = self.shape
+            E = s.n_experts
+            w13 = np.empty((E, 2 * s.inter, s.hidden), dtype=np.uint16)
+            w2 = np.empty((E, s.hidden, s.inter), dtype=np.uint16)
+
+            def fill(e):
+                w13[e] = self.w13(e)
+                w2[e] = self.w2(e)
+
+            n = threads or min(8, os.cpu_count() or 1)
+            with ThreadPoolExecutor(max_workers=n) as ex:
+                list(ex.map(fill, range(E)))
+            self._cache["banks"] = (w13, w2)
+        return self._cache["banks"]
+
+    def shared(self):
+        """(w13 [2I, H], w2 [H, I]) bf16 bits of the shared expert."""
+        if "shared" not in self._cache:
+            self._cache["shared"] = (self.w13(-1), self.w2(-1))
+        return self._cache["shared"]
+
+    def expert(self, e: int):
+        """(w13, w2) bf16 bits of expert e (shared if e < 0), from the bank when built."""
+        if e < 0:
+            return self.shared()
+        if "banks" in self._cache:
+            w13, w2 = self._cache["banks"]
+            return w13[e], w2[e]
+        return self.w13(e), self.w2(e)
+
+
+def make_x(T: int, hidden: int = FLINT_HIDDEN, seed: int = 0, x_seed: int = 0) -> np.ndarray:
+    """bf16 bits [T, H] ~ N(0, 1), keyed by (seed, T, x_seed)."""
+    seq = np.random.SeedSequence([_X_DOMAIN, int(seed), int(T), int(x_seed)])
+    return _normal_bf16(seq, (int(T), int(hidden)), X_STD)
