@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the Flint MoE feed-forward layer on one MI355X.
+
+One step = one whole layer forward (router GEMV, sigmoid top-6, bucketing,
+gate/up GEMV with SiLU-and-mul, down GEMV with the weighted combine) over one
+batch of T tokens, through the C ABI, on the seeded synthetic layer.
+
+To measure HBM rather than the 256 MB Infinity Cache, the layer is cloned
+into several device copies and step i runs on copy i mod copies.  The K
+timed steps are captured in one HIP graph and replayed once, bracketed by
+synchronisation and HIP events on the replay stream.  Per-kernel durations
+come from a separate eager pass of K steps that records HIP events between
+the kernels (flint_moe_forward_timed).
+
+Prints ONE JSON line.  Default workload: decode T=8 (bf16).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "µs per MoE layer forward at T=1/8/32 + achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+H, E, K_TOP, I = 2048, 256, 6, 512
+EXPERT_W13_BYTES = 2 * I * H * 2           # 4,194,304
+EXPERT_W2_BYTES = H * I * 2                # 2,097,152
+ROUTER_BYTES = E * H * 2                   # 1,048,576
+
+WORKLOADS = {
+    "decode_t1": dict(T=1, bias=False),
+    "decode_t8": dict(T=8, bias=False),
+    "decode_t32_skewed": dict(T=32, bias=True),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode_t8", choices=sorted(WORKLOADS))
+    p.add_argument("--copies", type=int, default=32, help="device copies of the layer")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
+                   help="CPU time budget of the oracle baseline (0 disables it)")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="also run a device copy of this many MiB (FETCH_SIZE calibration)")
+    return p.parse_args()
+
+
+def cpu_baseline(syn, x_bits, bias, budget_s):
+    """The oracle, as it stands, on the same tokens: whole-layer forwards until
+    the time budget is used (at least two)."""
+    from oracle import OracleLayer, moe_forward
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()
+                       if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    layer = OracleLayer(H, E, K_TOP, I, syn.router_w(), syn.router_bias() if bias else None,
+                        syn.expert)
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while len(times) < 2 or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        moe_forward(layer, x_bits)
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    med = times[len(times) // 2]
+    T = x_bits.shape[0]
+    return {"value": med * 1e6, "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} whole-layer forwards of the same {T} tokens "
+                      f"(fp64 numpy, per-token loop); median",
+            "tokens_per_s": T / med}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert parallelism is a design note, not code). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import numpy as np
+    import torch
+
+    import sparse_expert_gemv_amd as sg
+    from synth import SyntheticLayer, make_x
+    from synth.device import upload_bf16
+
+    wl = WORKLOADS[args.workload]
+    T, bias = wl["T"], wl["bias"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    log(f"workload {args.workload}: generating seeded layer {args.seed}")
+    syn = SyntheticLayer(args.seed)
+    syn.routed_banks()
+    base = upload_bf16(syn, dev, with_bias=bias)
+    copies = []
+    for c in range(args.copies):
+        t = base if c == 0 else {k: (None if v is None else v.clone()) for k, v in base.items()}
+        copies.append(sg.DeviceWeights(t["router_w"], t["router_b"], sg.DeviceBank(t["w13"], t["w2"]),
+                                       sg.DeviceBank(t["sh_w13"], t["sh_w2"])))
+    torch.cuda.synchronize()
+    log(f"{args.copies} layer copies resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+
+    moe = sg.FlintMoE(max_tokens=max(T, 1))
+    x_bits = make_x(T, seed=args.seed, x_seed=0)
+    x = sg.bf16_tensor(x_bits, dev)
+    out = torch.empty_like(x)
+    ids = torch.empty((T, K_TOP), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, K_TOP), dtype=torch.float32, device=dev)
+    ws = moe.new_workspace(T, dev)
+    ws_bytes = ws.numel()
+    structs = [c.struct() for c in copies]
+    ptrs = (int(x.data_ptr()), int(out.data_ptr()), int(ids.data_ptr()), int(wts.data_ptr()),
+            int(ws.data_ptr()))
+
+    def step(i, stream_handle):
+        st = moe.forward_raw(structs[i % len(structs)], ptrs[0], T, ptrs[1], ptrs[2], ptrs[3],
+                             ptrs[4], ws_bytes, stream_handle)
+        if st != sg.FLINT_OK:
+            raise sg.FlintError(st, moe.last_error())
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        step(i, stream.cuda_stream)
+    torch.cuda.synchronize()
+    lay = moe.workspace_layout(T)
+    n_active = int(ws[lay["n_active"]:lay["n_active"] + 4].cpu().numpy().view(np.int32)[0])
+    log(f"warmup done: |U| = {n_active}")
+
+    # Per-kernel durations: K eager steps with HIP events between the kernels.
+    n_ev = 8
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    nk = 0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st, nk = moe.forward_timed_raw(structs[i % len(structs)], ptrs[0], T, ptrs[1], ptrs[2],
+                                       ptrs[3], ptrs[4], ws_bytes, stream.cuda_stream,
+                                       [e.cuda_event for e in evs[i]])
+        if st != sg.FLINT_OK:
+            raise sg.FlintError(st, moe.last_error())
+    torch.cuda.synchronize()
+    eager_wall = (time.perf_counter() - t0) / args.steps
+    kern_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nk)]
+                        for i in range(args.steps)])
+    kern_us = kern_ms.mean(axis=0) * 1e3
+    names = ["router_topk_shared", "gateup_routed", "down_combine"][:nk]
+    log("eager per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_us)))
+
+    # Timed region: one graph replay of exactly K steps.
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step(0, side.cuda_stream)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(args.steps):
+            step(i, cap)
+    torch.cuda.synchronize()
+    g.replay()                       # upload + first launch, untimed
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    us_step = ms_total * 1e3 / args.steps
+    log(f"graph: {us_step:.2f} us/step over {args.steps} steps")
+
+    layer_bytes = ROUTER_BYTES + (n_active + 1) * (EXPERT_W13_BYTES + EXPERT_W2_BYTES) + 2 * T * H * 2
+    gateup_bytes = n_active * EXPERT_W13_BYTES
+    gateup_us = float(kern_us[1])
+    achieved = gateup_bytes / (gateup_us * 1e-6) / 1e9
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n} bytes done")
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_step, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"flint_moe_{args.workload}", "T": T, "hidden": H,
+                   "n_experts": E, "top_k": K_TOP, "inter": I, "shared_experts": 1,
+                   "router_bias": bias, "seed": args.seed, "n_active": n_active,
+                   "layer_copies": args.copies, "timing": "one HIP-graph replay of K steps"},
+        "tokens_per_s": round(T / (us_step * 1e-6), 1),
+        "layer_algorithmic_bytes": layer_bytes,
+        "layer_GBps": round(layer_bytes / (us_step * 1e-6) / 1e9, 1),
+        "layer_hbm_frac": round(layer_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels_us_eager": {n: round(float(v), 3) for n, v in zip(names, kern_us)},
+        "eager_wall_us_per_step": round(eager_wall * 1e6, 2),
+        "roofline": {"kernel": "gateup_routed", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": gateup_bytes,
+                     "avg_launch_us": round(gateup_us, 3)},
+    }
+    if rank == 0 and args.cpu_baseline_seconds > 0:
+        log("timing the oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(syn, x_bits, bias, args.cpu_baseline_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

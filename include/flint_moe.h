@@ -1,0 +1,184 @@
+/*
+ * flint_moe.h — C ABI of the MI355X (gfx950) Flint MoE feed-forward layer.
+ *
+ * The layer, as the pages define it:
+ *   - hidden size 2048; 256 routed experts chosen by sigmoid top-6 routing,
+ *     plus one always-on shared expert ("vLLM Day-0 Support for Recursive's
+ *     Flint", section "Flint Model Architecture", bullet "MoE Structure";
+ *     "Flint on Arc Pro B70", section "Setup"; "RecursiveSI/flint — vLLM
+ *     serving recipe", section "Guide / Overview");
+ *   - the router and expert GEMVs read only the selected experts' weights
+ *     (Day-0 page, section "Optimization Strategies", bullet "Small-batch MoE
+ *     Kernels");
+ *   - each expert is SwiGLU with SiLU(g) = g / (1 + exp(-g)) ("Flint on Arc
+ *     Pro B70", section "norm.py: Triton kernels that assumed CUDA");
+ *   - routed outputs are combined by their routing weights and added to the
+ *     shared expert's output (Day-0 page, section "Optimization Strategies",
+ *     bullet "Low-Latency Decode Path");
+ *   - the NVFP4 checkpoint runs weight-only (W4A16) with bf16 activations
+ *     (Day-0 page, section "Flint Model Overview and Capabilities").
+ *
+ * For token t with bf16 input x_t[H]:
+ *   z_e   = sum_k Wr[e,k] x_t[k] + b_e                    (fp32 accumulate)
+ *   s_e   = 1 / (1 + exp(-z_e))
+ *   S_t   = the top_k experts by s_e, ties to the lower index
+ *   w_j   = s_{S_j} / sum_i s_{S_i}   (renormalize = 1)  else s_{S_j};  times routed_scale
+ *   h_e   = silu(W13_e[0:I] x_t) * (W13_e[I:2I] x_t)       (fp32, never rounded)
+ *   out_t = W2_sh h_sh + sum_j w_j W2_{S_j} h_{S_j}          (fp32, rounded once to bf16, RNE)
+ *
+ * Conventions for every call:
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - "device" pointers point to memory on the GPU that is current when the
+ *     call is made; the library never dereferences them on the host.
+ *   - The caller owns every buffer (weights, x, out, routing outputs,
+ *     workspace).  The library allocates no device memory.
+ *   - flint_moe_forward is asynchronous: it validates its arguments on the
+ *     host, enqueues kernels on `stream` and returns.  Argument errors are
+ *     reported before anything is enqueued; a failed launch returns
+ *     FLINT_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - A context may be used by one stream at a time; a workspace may be used
+ *     by one forward at a time.  Forwards that overlap on one workspace race.
+ */
+#ifndef FLINT_MOE_H
+#define FLINT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct flint_moe_ctx flint_moe_ctx; /* opaque, host memory */
+
+typedef enum flint_status {
+  FLINT_OK = 0,
+  FLINT_ERR_INVALID_ARG = 1, /* NULL / misaligned / out-of-range argument */
+  FLINT_ERR_UNSUPPORTED = 2, /* shape or format this build has no kernels for */
+  FLINT_ERR_WORKSPACE = 3,   /* workspace smaller than flint_moe_workspace_bytes() */
+  FLINT_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} flint_status;
+
+typedef enum flint_weight_format {
+  FLINT_W_BF16 = 0,  /* bf16 weights */
+  FLINT_W_NVFP4 = 1  /* E2M1 elements, E4M3FN scale per 16 K-elements, fp32 scale per tensor */
+} flint_weight_format;
+
+/* Host struct, copied by flint_moe_init. */
+typedef struct flint_moe_config {
+  int32_t hidden;       /* H: must be 2048 */
+  int32_t n_experts;    /* E: 1..256 routed experts (256 for Flint) */
+  int32_t top_k;        /* k: 1..min(8, E) (6 for Flint) */
+  int32_t inter;        /* I: must be 512 (the shared expert has the same shape) */
+  int32_t max_tokens;   /* >= 1: largest T a forward may be called with */
+  int32_t renormalize;  /* 1: w_j = s_j / sum of the k selected scores; 0: w_j = s_j */
+  float routed_scale;   /* multiplies every routed weight (1.0 for Flint); finite */
+  int32_t format;       /* flint_weight_format */
+} flint_moe_config;
+
+/* One bank of experts, n tensors stacked on the leading axis (n = E for the
+ * routed bank, n = 1 for the shared expert).  All device pointers, 16-byte
+ * aligned.
+ *   BF16 : w13 = bf16 [n][2I][H]   rows [0,I) gate, [I,2I) up; K (= H) contiguous
+ *          w2  = bf16 [n][H][I]    K (= I) contiguous
+ *          scale / gscale pointers ignored (may be NULL)
+ *   NVFP4: w13 = uint8 [n][2I][H/2]  two E2M1 codes per byte, even k in the
+ *                                    low nibble, nibble bit 3 = sign
+ *          w2  = uint8 [n][H][I/2]
+ *          w13_scale = uint8 [n][2I][H/16], w2_scale = uint8 [n][H][I/16]
+ *                      E4M3FN, one per 16 consecutive K elements
+ *          w13_gscale, w2_gscale = fp32 [n], one per tensor
+ *          element value = e2m1(code) * e4m3(scale) * gscale            */
+typedef struct flint_expert_bank {
+  const void* w13;
+  const void* w2;
+  const uint8_t* w13_scale;
+  const uint8_t* w2_scale;
+  const float* w13_gscale;
+  const float* w2_gscale;
+} flint_expert_bank;
+
+typedef struct flint_moe_weights {
+  const uint16_t* router_w; /* device, bf16 [E][H], row-major; bf16 in every format */
+  const float* router_b;    /* device, fp32 [E] added to the logit before the sigmoid, or NULL */
+  flint_expert_bank routed; /* n = E */
+  flint_expert_bank shared; /* n = 1 */
+} flint_moe_weights;
+
+/* Byte offsets of the regions of a workspace sized for T tokens.  Exposed so
+ * that tests can read the intermediate results of one forward (a region is
+ * valid once the forward that wrote it has completed). */
+typedef struct flint_moe_ws_layout {
+  size_t total_bytes;
+  size_t header;    /* uint32 [256]: completion counters (must be zero before first use) */
+  size_t logits;    /* fp32 [T][E]: z (router GEMV + bias) */
+  size_t topk_ids;  /* int32 [T][k]: selected experts in rank order */
+  size_t topk_w;    /* fp32 [T][k]: routing weights */
+  size_t n_active;  /* int32 [1]: |U|, the number of distinct selected experts */
+  size_t active;    /* int32 [E]: U, ascending */
+  size_t counts;    /* int32 [E]: slots per expert */
+  size_t offsets;   /* int32 [E+1]: exclusive prefix sum of counts */
+  size_t slots;     /* int32 [T*k]: slot ids s = t*k + j grouped by expert (ascending),
+                       ascending within an expert */
+  size_t h;         /* fp32 [T*k + T][I]: h of slot s in row s; h of the shared expert
+                       for token t in row T*k + t */
+  size_t extra;     /* path-private scratch (prefill-sized T only) */
+} flint_moe_ws_layout;
+
+/* Validate `cfg` and create a context.  Touches no GPU state.
+ * Returns INVALID_ARG for NULL pointers or out-of-range fields, UNSUPPORTED
+ * for shapes other than H = 2048, I = 512.  *ctx_out is set only on FLINT_OK. */
+flint_status flint_moe_init(const flint_moe_config* cfg, flint_moe_ctx** ctx_out);
+
+/* Bytes of workspace a forward of T tokens needs (0 for T <= 0 or NULL ctx).
+ * The first 1024 bytes (the header) must be zero before the workspace is used
+ * for the first time; every completed forward leaves them zero again. */
+size_t flint_moe_workspace_bytes(const flint_moe_ctx* ctx, int32_t T);
+
+/* Fill `layout` with the region offsets of a workspace for T tokens. */
+flint_status flint_moe_workspace_layout(const flint_moe_ctx* ctx, int32_t T,
+                                        flint_moe_ws_layout* layout);
+
+/* One layer forward over T tokens.
+ *   x         device bf16 [T][H] (16-byte aligned)
+ *   out       device bf16 [T][H] (16-byte aligned; must not overlap x)
+ *   topk_ids  device int32 [T][k] or NULL: receives the selected experts
+ *   topk_w    device fp32  [T][k] or NULL: receives their routing weights
+ *   workspace device, >= flint_moe_workspace_bytes(ctx, T) bytes, 256-byte aligned
+ *   stream    hipStream_t (passed as void*; NULL = the null stream)
+ * T == 0 is a no-op returning FLINT_OK.  T < 0 or T > max_tokens: INVALID_ARG.
+ * NaN/Inf inputs are not checked. */
+flint_status flint_moe_forward(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                               const uint16_t* x, int32_t T, uint16_t* out,
+                               int32_t* topk_ids, float* topk_w,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* flint_moe_forward with per-kernel timing, for measurement.  `events` holds
+ * n_events hipEvent_t handles (passed as void*) created by the caller; event
+ * i is recorded on `stream` before kernel i of the chosen path and event
+ * n_kernels after the last one, so (event i, event i+1) brackets kernel i.
+ * *n_kernels receives the number of kernels the path launched.  Requires
+ * n_events >= 8.  Same arguments, validation and results as
+ * flint_moe_forward otherwise. */
+flint_status flint_moe_forward_timed(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                     const uint16_t* x, int32_t T, uint16_t* out,
+                                     int32_t* topk_ids, float* topk_w, void* workspace,
+                                     size_t workspace_bytes, void* stream,
+                                     void* const* events, int32_t n_events, int32_t* n_kernels);
+
+/* Release a context.  NULL is allowed. */
+void flint_moe_destroy(flint_moe_ctx* ctx);
+
+/* Static name of a status code. */
+const char* flint_moe_status_string(flint_status s);
+
+/* Human-readable reason for the last non-OK status returned with this
+ * context ("" if none).  Valid until the next call with the context. */
+const char* flint_moe_last_error(const flint_moe_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLINT_MOE_H */

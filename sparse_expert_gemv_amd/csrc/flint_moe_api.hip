@@ -1,0 +1,251 @@
+// Host side of the C ABI declared in include/flint_moe.h: argument
+// validation, workspace layout and the choice of kernel path.  Everything
+// here runs on the CPU; the kernels it enqueues are in the other .hip files.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "flint_kernels.h"
+#include "flint_moe.h"
+
+#define FLINT_API extern "C" __attribute__((visibility("default")))
+
+struct flint_moe_ctx {
+  flint_moe_config cfg;
+  std::string last_error;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kHeaderBytes = flint::kHeaderWords * sizeof(uint32_t);
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L) {
+  const size_t t = (size_t)T, E = (size_t)c.n_experts, k = (size_t)c.top_k, I = (size_t)c.inter;
+  size_t o = 0;
+  std::memset(L, 0, sizeof(*L));
+  L->header = o;   o = align_up(o + kHeaderBytes);
+  L->logits = o;   o = align_up(o + t * E * sizeof(float));
+  L->topk_ids = o; o = align_up(o + t * k * sizeof(int32_t));
+  L->topk_w = o;   o = align_up(o + t * k * sizeof(float));
+  L->n_active = o; o = align_up(o + sizeof(int32_t));
+  L->active = o;   o = align_up(o + E * sizeof(int32_t));
+  L->counts = o;   o = align_up(o + E * sizeof(int32_t));
+  L->offsets = o;  o = align_up(o + (E + 1) * sizeof(int32_t));
+  L->slots = o;    o = align_up(o + t * k * sizeof(int32_t));
+  L->h = o;        o = align_up(o + (t * k + t) * I * sizeof(float));
+  L->extra = o;
+  L->total_bytes = o;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+flint_status fail(flint_moe_ctx* ctx, flint_status s, const std::string& why) {
+  if (ctx) ctx->last_error = why;
+  return s;
+}
+
+flint_status check_config(const flint_moe_config& c, std::string* why) {
+  char buf[256];
+  if (c.hidden <= 0 || c.inter <= 0 || c.n_experts <= 0 || c.top_k <= 0 || c.max_tokens <= 0) {
+    *why = "hidden, inter, n_experts, top_k and max_tokens must be positive";
+    return FLINT_ERR_INVALID_ARG;
+  }
+  if (c.top_k > c.n_experts) {
+    *why = "top_k exceeds n_experts";
+    return FLINT_ERR_INVALID_ARG;
+  }
+  if (c.renormalize != 0 && c.renormalize != 1) {
+    *why = "renormalize must be 0 or 1";
+    return FLINT_ERR_INVALID_ARG;
+  }
+  if (!std::isfinite(c.routed_scale)) {
+    *why = "routed_scale must be finite";
+    return FLINT_ERR_INVALID_ARG;
+  }
+  if (c.format != FLINT_W_BF16 && c.format != FLINT_W_NVFP4) {
+    *why = "unknown weight format";
+    return FLINT_ERR_INVALID_ARG;
+  }
+  if (c.hidden != flint::kHidden || c.inter != flint::kInter || c.n_experts > flint::kMaxExperts ||
+      c.top_k > flint::kMaxTopK) {
+    std::snprintf(buf, sizeof buf,
+                  "no kernels for hidden=%d inter=%d n_experts=%d top_k=%d "
+                  "(built for hidden=%d, inter=%d, n_experts<=%d, top_k<=%d)",
+                  c.hidden, c.inter, c.n_experts, c.top_k, flint::kHidden, flint::kInter,
+                  flint::kMaxExperts, flint::kMaxTopK);
+    *why = buf;
+    return FLINT_ERR_UNSUPPORTED;
+  }
+  if (c.format == FLINT_W_NVFP4) {
+    *why = "NVFP4 weights are not supported by this build";
+    return FLINT_ERR_UNSUPPORTED;
+  }
+  return FLINT_OK;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+FLINT_API flint_status flint_moe_init(const flint_moe_config* cfg, flint_moe_ctx** ctx_out) {
+  if (!cfg || !ctx_out) return FLINT_ERR_INVALID_ARG;
+  std::string why;
+  const flint_status s = check_config(*cfg, &why);
+  if (s != FLINT_OK) return s;
+  flint_moe_ctx* ctx = new (std::nothrow) flint_moe_ctx;
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  ctx->cfg = *cfg;
+  *ctx_out = ctx;
+  return FLINT_OK;
+}
+
+FLINT_API size_t flint_moe_workspace_bytes(const flint_moe_ctx* ctx, int32_t T) {
+  if (!ctx || T <= 0) return 0;
+  flint_moe_ws_layout L;
+  compute_layout(ctx->cfg, T, &L);
+  return L.total_bytes;
+}
+
+FLINT_API flint_status flint_moe_workspace_layout(const flint_moe_ctx* ctx, int32_t T,
+                                                  flint_moe_ws_layout* layout) {
+  if (!ctx || !layout || T <= 0) return FLINT_ERR_INVALID_ARG;
+  compute_layout(ctx->cfg, T, layout);
+  return FLINT_OK;
+}
+
+namespace {
+
+flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const uint16_t* x,
+                          int32_t T, uint16_t* out, int32_t* topk_ids, float* topk_w,
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          flint::StageEvents* ev) {
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  ctx->last_error.clear();
+  const flint_moe_config& c = ctx->cfg;
+  if (T < 0 || T > c.max_tokens) {
+    char buf[128];
+    std::snprintf(buf, sizeof buf, "T=%d outside [0, max_tokens=%d]", T, c.max_tokens);
+    return fail(ctx, FLINT_ERR_INVALID_ARG, buf);
+  }
+  if (T == 0) return FLINT_OK;
+  if (!w || !x || !out || !workspace)
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "weights, x, out and workspace must be non-NULL");
+  if (!w->router_w || !w->routed.w13 || !w->routed.w2 || !w->shared.w13 || !w->shared.w2)
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "router and expert weight pointers must be non-NULL");
+  const void* p16[] = {w->router_w, w->routed.w13, w->routed.w2, w->shared.w13, w->shared.w2, x, out};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return fail(ctx, FLINT_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (w->router_b && !aligned(w->router_b, 4))
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "router_b must be 4-byte aligned");
+  if ((topk_ids && !aligned(topk_ids, 4)) || (topk_w && !aligned(topk_w, 4)))
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "topk_ids / topk_w must be 4-byte aligned");
+  if (!aligned(workspace, kAlign))
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t act_bytes = (size_t)T * c.hidden * sizeof(uint16_t);
+  if (ranges_overlap(x, act_bytes, out, act_bytes))
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "out overlaps x");
+
+  flint_moe_ws_layout L;
+  compute_layout(c, T, &L);
+  if (workspace_bytes < L.total_bytes) {
+    char buf[160];
+    std::snprintf(buf, sizeof buf, "workspace of %zu bytes, %zu needed for T=%d", workspace_bytes,
+                  L.total_bytes, T);
+    return fail(ctx, FLINT_ERR_WORKSPACE, buf);
+  }
+  if (T > flint::kDecodeMaxT)
+    return fail(ctx, FLINT_ERR_UNSUPPORTED, "T above the decode path's limit needs the prefill path");
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  flint::LayerArgs a{};
+  a.x = x;
+  a.out = out;
+  a.router_w = w->router_w;
+  a.router_b = w->router_b;
+  a.routed = {static_cast<const uint8_t*>(w->routed.w13), static_cast<const uint8_t*>(w->routed.w2),
+              w->routed.w13_scale, w->routed.w2_scale, w->routed.w13_gscale, w->routed.w2_gscale};
+  a.shared = {static_cast<const uint8_t*>(w->shared.w13), static_cast<const uint8_t*>(w->shared.w2),
+              w->shared.w13_scale, w->shared.w2_scale, w->shared.w13_gscale, w->shared.w2_gscale};
+  a.ids_out = topk_ids;
+  a.wts_out = topk_w;
+  a.ws.header = reinterpret_cast<uint32_t*>(ws + L.header);
+  a.ws.logits = reinterpret_cast<float*>(ws + L.logits);
+  a.ws.ids = reinterpret_cast<int32_t*>(ws + L.topk_ids);
+  a.ws.wts = reinterpret_cast<float*>(ws + L.topk_w);
+  a.ws.n_active = reinterpret_cast<int32_t*>(ws + L.n_active);
+  a.ws.active = reinterpret_cast<int32_t*>(ws + L.active);
+  a.ws.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  a.ws.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  a.ws.slots = reinterpret_cast<int32_t*>(ws + L.slots);
+  a.ws.h = reinterpret_cast<float*>(ws + L.h);
+  a.ws.extra = ws + L.extra;
+  a.T = T;
+  a.E = c.n_experts;
+  a.k = c.top_k;
+  a.renormalize = c.renormalize;
+  a.routed_scale = c.routed_scale;
+  a.nvfp4 = c.format == FLINT_W_NVFP4;
+
+  (void)hipGetLastError();  // do not report an earlier, unrelated failure
+  const hipError_t err = flint::launch_decode_bf16(a, static_cast<hipStream_t>(stream), ev);
+  if (err != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(err));
+  return FLINT_OK;
+}
+
+}  // namespace
+
+FLINT_API flint_status flint_moe_forward(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                         const uint16_t* x, int32_t T, uint16_t* out,
+                                         int32_t* topk_ids, float* topk_w, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return forward_impl(ctx, w, x, T, out, topk_ids, topk_w, workspace, workspace_bytes, stream,
+                      nullptr);
+}
+
+FLINT_API flint_status flint_moe_forward_timed(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                               const uint16_t* x, int32_t T, uint16_t* out,
+                                               int32_t* topk_ids, float* topk_w, void* workspace,
+                                               size_t workspace_bytes, void* stream,
+                                               void* const* events, int32_t n_events,
+                                               int32_t* n_kernels) {
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  if (!events || n_events < 8 || !n_kernels)
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "events (>= 8) and n_kernels are required");
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return fail(ctx, FLINT_ERR_INVALID_ARG, "NULL event handle");
+  flint::StageEvents ev;
+  ev.events = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  ev.n = n_events;
+  const flint_status s = forward_impl(ctx, w, x, T, out, topk_ids, topk_w, workspace,
+                                      workspace_bytes, stream, &ev);
+  *n_kernels = ev.used > 0 ? ev.used - 1 : 0;
+  return s;
+}
+
+FLINT_API void flint_moe_destroy(flint_moe_ctx* ctx) { delete ctx; }
+
+FLINT_API const char* flint_moe_status_string(flint_status s) {
+  switch (s) {
+    case FLINT_OK: return "FLINT_OK";
+    case FLINT_ERR_INVALID_ARG: return "FLINT_ERR_INVALID_ARG";
+    case FLINT_ERR_UNSUPPORTED: return "FLINT_ERR_UNSUPPORTED";
+    case FLINT_ERR_WORKSPACE: return "FLINT_ERR_WORKSPACE";
+    case FLINT_ERR_HIP: return "FLINT_ERR_HIP";
+  }
+  return "FLINT_ERR_UNKNOWN";
+}
+
+FLINT_API const char* flint_moe_last_error(const flint_moe_ctx* ctx) {
+  return ctx ? ctx->last_error.c_str() : "";
+}

@@ -1,0 +1,240 @@
+"""ctypes binding of ``libflint_moe.so`` (argument marshalling only).
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+``include/flint_moe.h``; this module only converts PyTorch tensors into the
+pointers and sizes that ABI takes.  PyTorch provides device memory and the
+current stream.  There is no fallback: if the library is missing, loading it
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libflint_moe.so")
+
+FLINT_OK = 0
+FLINT_ERR_INVALID_ARG = 1
+FLINT_ERR_UNSUPPORTED = 2
+FLINT_ERR_WORKSPACE = 3
+FLINT_ERR_HIP = 4
+
+FLINT_W_BF16 = 0
+FLINT_W_NVFP4 = 1
+
+HEADER_BYTES = 1024
+
+# Symbols the header declares; tests check the library exports each of them.
+ABI_SYMBOLS = (
+    "flint_moe_init",
+    "flint_moe_workspace_bytes",
+    "flint_moe_workspace_layout",
+    "flint_moe_forward",
+    "flint_moe_forward_timed",
+    "flint_moe_destroy",
+    "flint_moe_status_string",
+    "flint_moe_last_error",
+)
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("routed_scale", ctypes.c_float), ("format", ctypes.c_int32)]
+
+
+class ExpertBank(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("w13_gscale", ctypes.c_void_p), ("w2_gscale", ctypes.c_void_p)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+                ("routed", ExpertBank), ("shared", ExpertBank)]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("total_bytes", "header", "logits", "topk_ids", "topk_w", "n_active",
+                 "active", "counts", "offsets", "slots", "h", "extra")]
+
+
+class FlintError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m sparse_expert_gemv_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.flint_moe_init.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(P)]
+    lib.flint_moe_init.restype = ctypes.c_int
+    lib.flint_moe_workspace_bytes.argtypes = [P, ctypes.c_int32]
+    lib.flint_moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.flint_moe_workspace_layout.argtypes = [P, ctypes.c_int32, ctypes.POINTER(WsLayout)]
+    lib.flint_moe_workspace_layout.restype = ctypes.c_int
+    lib.flint_moe_forward.argtypes = [P, ctypes.POINTER(Weights), P, ctypes.c_int32, P, P, P, P,
+                                      ctypes.c_size_t, P]
+    lib.flint_moe_forward.restype = ctypes.c_int
+    lib.flint_moe_forward_timed.argtypes = [P, ctypes.POINTER(Weights), P, ctypes.c_int32, P, P, P,
+                                            P, ctypes.c_size_t, P, ctypes.POINTER(P),
+                                            ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.flint_moe_forward_timed.restype = ctypes.c_int
+    lib.flint_moe_destroy.argtypes = [P]
+    lib.flint_moe_destroy.restype = None
+    lib.flint_moe_status_string.argtypes = [ctypes.c_int]
+    lib.flint_moe_status_string.restype = ctypes.c_char_p
+    lib.flint_moe_last_error.argtypes = [P]
+    lib.flint_moe_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().flint_moe_status_string(status).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a tensor (None for None)."""
+    return None if t is None else int(t.data_ptr())
+
+
+@dataclass
+class DeviceBank:
+    """Tensors of one expert bank (bf16: w13, w2; NVFP4: + scales and gscales)."""
+    w13: object
+    w2: object
+    w13_scale: object = None
+    w2_scale: object = None
+    w13_gscale: object = None
+    w2_gscale: object = None
+
+    def struct(self) -> ExpertBank:
+        return ExpertBank(_ptr(self.w13), _ptr(self.w2), _ptr(self.w13_scale),
+                          _ptr(self.w2_scale), _ptr(self.w13_gscale), _ptr(self.w2_gscale))
+
+
+@dataclass
+class DeviceWeights:
+    router_w: object            # bf16 [E, H]
+    router_b: object            # fp32 [E] or None
+    routed: DeviceBank
+    shared: DeviceBank
+
+    def struct(self) -> Weights:
+        return Weights(_ptr(self.router_w), _ptr(self.router_b), self.routed.struct(),
+                       self.shared.struct())
+
+
+class FlintMoE:
+    """One layer configuration (a ``flint_moe_ctx``)."""
+
+    def __init__(self, hidden=2048, n_experts=256, top_k=6, inter=512, max_tokens=64,
+                 renormalize=True, routed_scale=1.0, fmt=FLINT_W_BF16):
+        self.lib = load_library()
+        self.cfg = Config(hidden, n_experts, top_k, inter, max_tokens, int(bool(renormalize)),
+                          float(routed_scale), int(fmt))
+        h = ctypes.c_void_p()
+        st = self.lib.flint_moe_init(ctypes.byref(self.cfg), ctypes.byref(h))
+        if st != FLINT_OK:
+            raise FlintError(st, f"flint_moe_init: {status_string(st)}")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.flint_moe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def top_k(self) -> int:
+        return self.cfg.top_k
+
+    def workspace_bytes(self, T: int) -> int:
+        return int(self.lib.flint_moe_workspace_bytes(self.handle, T))
+
+    def workspace_layout(self, T: int) -> dict:
+        L = WsLayout()
+        st = self.lib.flint_moe_workspace_layout(self.handle, T, ctypes.byref(L))
+        if st != FLINT_OK:
+            raise FlintError(st, f"flint_moe_workspace_layout: {status_string(st)}")
+        return {n: getattr(L, n) for n, _ in WsLayout._fields_}
+
+    def last_error(self) -> str:
+        return self.lib.flint_moe_last_error(self.handle).decode()
+
+    def forward_raw(self, weights: Weights, x_ptr, T, out_ptr, ids_ptr, w_ptr, ws_ptr, ws_bytes,
+                    stream_ptr) -> int:
+        """The C call with raw addresses; returns the status code."""
+        return self.lib.flint_moe_forward(self.handle, ctypes.byref(weights), x_ptr, T, out_ptr,
+                                          ids_ptr, w_ptr, ws_ptr, ws_bytes, stream_ptr)
+
+    def forward_timed_raw(self, weights: Weights, x_ptr, T, out_ptr, ids_ptr, w_ptr, ws_ptr,
+                          ws_bytes, stream_ptr, event_handles) -> tuple:
+        """The timed C call; returns (status, number of kernels launched)."""
+        n = len(event_handles)
+        arr = (ctypes.c_void_p * n)(*event_handles)
+        nk = ctypes.c_int32(0)
+        st = self.lib.flint_moe_forward_timed(self.handle, ctypes.byref(weights), x_ptr, T, out_ptr,
+                                              ids_ptr, w_ptr, ws_ptr, ws_bytes, stream_ptr, arr, n,
+                                              ctypes.byref(nk))
+        return st, nk.value
+
+    def forward(self, weights: DeviceWeights, x, out, topk_ids=None, topk_w=None, workspace=None,
+                stream=None, weights_struct: Optional[Weights] = None) -> None:
+        """out[T, H] = layer(x[T, H]); tensors on the current device.  Raises on error."""
+        import torch
+        T = int(x.shape[0])
+        if workspace is None:
+            workspace = self.new_workspace(T, x.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        ws = weights_struct if weights_struct is not None else weights.struct()
+        st = self.forward_raw(ws, _ptr(x), T, _ptr(out), _ptr(topk_ids), _ptr(topk_w),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              stream.cuda_stream)
+        if st != FLINT_OK:
+            raise FlintError(st, f"flint_moe_forward: {status_string(st)}: {self.last_error()}")
+
+    def new_workspace(self, T: int, device):
+        """A zero-filled workspace for up to T tokens (the header must start at zero)."""
+        import torch
+        n = max(self.workspace_bytes(T), HEADER_BYTES)
+        return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def bf16_tensor(bits, device):
+    """Upload a numpy uint16 array of bf16 bit patterns as a torch.bfloat16 tensor."""
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).to(device).view(torch.bfloat16)
+
+
+def bf16_bits(t):
+    """Download a torch.bfloat16 tensor as numpy uint16 bit patterns."""
+    import numpy as np
+    return t.detach().contiguous().view(dtype=__import__("torch").int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,100 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments on the host before anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_expert_gemv_amd as sg
+from sparse_expert_gemv_amd.flint_moe import Config, Weights, ExpertBank
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"\b(flint_moe_\w+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sg.load_library()
+    decl = declared_symbols()
+    assert decl, "no declarations found"
+    assert decl == set(sg.ABI_SYMBOLS) | (decl - set(sg.ABI_SYMBOLS))
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert sg.status_string(0) == "FLINT_OK"
+    assert sg.status_string(3) == "FLINT_ERR_WORKSPACE"
+    assert sg.status_string(99) == "FLINT_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=1024), sg.FLINT_ERR_UNSUPPORTED),
+    (dict(inter=256), sg.FLINT_ERR_UNSUPPORTED),
+    (dict(n_experts=300), sg.FLINT_ERR_UNSUPPORTED),
+    (dict(top_k=9, n_experts=16), sg.FLINT_ERR_UNSUPPORTED),
+    (dict(top_k=7, n_experts=6), sg.FLINT_ERR_INVALID_ARG),
+    (dict(max_tokens=0), sg.FLINT_ERR_INVALID_ARG),
+    (dict(routed_scale=float("nan")), sg.FLINT_ERR_INVALID_ARG),
+    (dict(fmt=7), sg.FLINT_ERR_INVALID_ARG),
+])
+def test_init_rejects(kw, status):
+    with pytest.raises(sg.FlintError) as e:
+        sg.FlintMoE(**kw)
+    assert e.value.status == status
+
+
+def test_init_null_and_destroy_null():
+    lib = sg.load_library()
+    assert lib.flint_moe_init(None, None) == sg.FLINT_ERR_INVALID_ARG
+    lib.flint_moe_destroy(None)
+
+
+def test_workspace_sizes_grow_with_T():
+    m = sg.FlintMoE(max_tokens=64)
+    assert m.workspace_bytes(0) == 0
+    sizes = [m.workspace_bytes(T) for T in (1, 2, 8, 64)]
+    assert sizes == sorted(sizes) and sizes[0] > 1024
+    lay = m.workspace_layout(8)
+    offs = [lay[k] for k in ("header", "logits", "topk_ids", "topk_w", "n_active", "active",
+                             "counts", "offsets", "slots", "h", "extra")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay["h"] + (8 * 6 + 8) * 512 * 4 <= lay["total_bytes"]
+
+
+def _fake_weights(base=1 << 20):
+    b = ExpertBank(base, base + 4096, None, None, None, None)
+    return Weights(base + 8192, None, b, b)
+
+
+def test_forward_host_validation_without_gpu():
+    """Every one of these returns before any HIP call (no GPU needed)."""
+    m = sg.FlintMoE(max_tokens=8)
+    W = _fake_weights()
+    x, out, ws = 1 << 30, 1 << 31, 1 << 32
+    need = m.workspace_bytes(4)
+    f = lambda **k: m.forward_raw(k.get("w", W), k.get("x", x), k.get("T", 4), k.get("out", out),
+                                  None, None, k.get("ws", ws), k.get("nbytes", need), None)
+    assert f(T=-1) == sg.FLINT_ERR_INVALID_ARG
+    assert f(T=9) == sg.FLINT_ERR_INVALID_ARG and "max_tokens" in m.last_error()
+    assert f(x=None) == sg.FLINT_ERR_INVALID_ARG
+    assert f(x=x + 2) == sg.FLINT_ERR_INVALID_ARG and "aligned" in m.last_error()
+    assert f(out=x + 4096) == sg.FLINT_ERR_INVALID_ARG and "overlaps" in m.last_error()
+    assert f(ws=ws + 16) == sg.FLINT_ERR_INVALID_ARG
+    assert f(nbytes=need - 1) == sg.FLINT_ERR_WORKSPACE
+    bad = _fake_weights()
+    bad.routed.w2 = None
+    assert f(w=bad) == sg.FLINT_ERR_INVALID_ARG
+    assert m.forward_raw(W, None, 0, None, None, None, None, 0, None) == sg.FLINT_OK
+    lib = sg.load_library()
+    assert lib.flint_moe_forward(None, None, None, 1, None, None, None, None, 0, None) == \
+        sg.FLINT_ERR_INVALID_ARG

@@ -1,0 +1,162 @@
+"""GPU parity of the decode-sized (T <= 64) bf16 path against the fp64 oracle.
+
+Full Flint shape (H 2048, 256 experts, top-6, I 512, shared expert), seeded
+synthetic layer.  Every call goes through the C ABI.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import OracleLayer, bf16_to_f64, bucket, moe_forward  # noqa: E402
+from oracle.grading import TOL_BF16, grade  # noqa: E402
+from synth import SyntheticLayer, make_x  # noqa: E402
+from synth.device import upload_bf16  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_expert_gemv_amd as sg
+    say("generating seeded layer")
+    syn = SyntheticLayer(SEED)
+    syn.routed_banks()
+    t = upload_bf16(syn, "cuda", with_bias=True)
+    bank = sg.DeviceBank(t["w13"], t["w2"])
+    shared = sg.DeviceBank(t["sh_w13"], t["sh_w2"])
+    W = sg.DeviceWeights(t["router_w"], None, bank, shared)
+    Wb = sg.DeviceWeights(t["router_w"], t["router_b"], bank, shared)
+    L = OracleLayer(2048, 256, 6, 512, syn.router_w(), None, syn.expert)
+    Lb = OracleLayer(2048, 256, 6, 512, syn.router_w(), syn.router_bias(), syn.expert)
+    return dict(sg=sg, syn=syn, t=t, W=W, Wb=Wb, L=L, Lb=Lb)
+
+
+def run(dev, x_bits, bias=False, renormalize=True, routed_scale=1.0, moe=None, ws=None):
+    sg = dev["sg"]
+    T = x_bits.shape[0]
+    moe = moe or sg.FlintMoE(max_tokens=64, renormalize=renormalize, routed_scale=routed_scale)
+    x = sg.bf16_tensor(x_bits, "cuda")
+    out = torch.empty_like(x)
+    ids = torch.full((T, 6), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((T, 6), dtype=torch.float32, device="cuda")
+    ws = ws if ws is not None else moe.new_workspace(T, "cuda")
+    moe.forward(dev["Wb"] if bias else dev["W"], x, out, ids, w, ws)
+    torch.cuda.synchronize()
+    return dict(out=sg.bf16_bits(out), ids=ids.cpu().numpy(), w=w.cpu().numpy(), ws=ws, moe=moe)
+
+
+def ws_region(r, name, T, dtype, count):
+    lay = r["moe"].workspace_layout(T)
+    b = r["ws"][lay[name]:lay[name] + count * np.dtype(dtype).itemsize].cpu().numpy()
+    return b.view(dtype)
+
+
+@pytest.mark.parametrize("T,bias,x_seed", [(1, False, 0), (8, False, 0), (32, True, 0),
+                                           (2, False, 1), (3, True, 2), (13, False, 3),
+                                           (47, True, 4), (64, False, 5), (64, True, 6)])
+def test_decode_matches_oracle(dev, T, bias, x_seed):
+    say(f"decode parity T={T} bias={bias} x_seed={x_seed}")
+    xb = make_x(T, seed=SEED, x_seed=x_seed)
+    r = run(dev, xb, bias=bias)
+    res = moe_forward(dev["Lb"] if bias else dev["L"], xb)
+    g = grade(r["out"], r["ids"], res, tol=TOL_BF16)
+    print(g)
+    assert g.ok, str(g)
+    # routing weights of the graded tokens, in rank order
+    for t, rr in enumerate(res):
+        if t in g.excluded:
+            continue
+        assert r["ids"][t].tolist() == rr.ids.tolist()
+        np.testing.assert_allclose(r["w"][t], rr.weights, rtol=2e-6, atol=1e-7)
+
+
+def test_intermediates_t8(dev):
+    """Logits, bucketing (bit-exact on the device's own ids) and h."""
+    T = 8
+    say("intermediates T=8")
+    xb = make_x(T, seed=SEED, x_seed=0)
+    r = run(dev, xb)
+    res = moe_forward(dev["L"], xb)
+    logits = ws_region(r, "logits", T, np.float32, T * 256).reshape(T, 256)
+    for t, rr in enumerate(res):
+        np.testing.assert_allclose(logits[t], rr.logits, rtol=0, atol=2e-5)
+    b = bucket(r["ids"], 256)
+    n_active = int(ws_region(r, "n_active", T, np.int32, 1)[0])
+    assert n_active == len(b["active"])
+    np.testing.assert_array_equal(ws_region(r, "active", T, np.int32, n_active), b["active"])
+    np.testing.assert_array_equal(ws_region(r, "counts", T, np.int32, 256), b["counts"])
+    np.testing.assert_array_equal(ws_region(r, "offsets", T, np.int32, 257), b["offsets"])
+    np.testing.assert_array_equal(ws_region(r, "slots", T, np.int32, T * 6), b["slots"])
+    h = ws_region(r, "h", T, np.float32, (T * 6 + T) * 512).reshape(T * 7, 512)
+    for t, rr in enumerate(res):
+        scale = np.max(np.abs(rr.h_shared))
+        np.testing.assert_allclose(h[T * 6 + t], rr.h_shared, rtol=0, atol=1e-5 * scale)
+        for j in range(6):
+            np.testing.assert_allclose(h[t * 6 + j], rr.h_routed[j], rtol=0,
+                                       atol=1e-5 * np.max(np.abs(rr.h_routed[j])))
+
+
+def test_bitwise_deterministic_and_batch_independent(dev):
+    say("determinism + batch independence T=8")
+    xb = make_x(8, seed=SEED, x_seed=7)
+    a = run(dev, xb)
+    b = run(dev, xb)
+    np.testing.assert_array_equal(a["out"], b["out"])
+    for t in (0, 3, 7):
+        one = run(dev, xb[t:t + 1])
+        np.testing.assert_array_equal(one["out"][0], a["out"][t])
+        assert one["ids"][0].tolist() == a["ids"][t].tolist()
+
+
+def test_routed_scale_zero_gives_shared_expert(dev):
+    say("routed_scale=0 T=5")
+    xb = make_x(5, seed=SEED, x_seed=8)
+    r = run(dev, xb, routed_scale=0.0)
+    res = moe_forward(dev["L"], xb, routed_scale=0.0)
+    g = grade(r["out"], r["ids"], res)
+    assert g.ok, str(g)
+    assert np.all(r["w"] == 0)
+
+
+def test_renormalize_off(dev):
+    say("renormalize off T=4")
+    xb = make_x(4, seed=SEED, x_seed=9)
+    r = run(dev, xb, renormalize=False)
+    res = moe_forward(dev["L"], xb, renormalize=False)
+    g = grade(r["out"], r["ids"], res)
+    assert g.ok, str(g)
+    for t, rr in enumerate(res):
+        np.testing.assert_allclose(r["w"][t], rr.weights, rtol=2e-6)
+
+
+def test_workspace_reuse_across_T(dev):
+    """One workspace, calls of decreasing and increasing T: the header is left
+    at zero by every forward."""
+    say("workspace reuse T=32,1,8")
+    sg = dev["sg"]
+    moe = sg.FlintMoE(max_tokens=64)
+    ws = moe.new_workspace(64, "cuda")
+    for T, xs in ((32, 10), (1, 11), (8, 12)):
+        xb = make_x(T, seed=SEED, x_seed=xs)
+        r = run(dev, xb, moe=moe, ws=ws)
+        g = grade(r["out"], r["ids"], moe_forward(dev["L"], xb))
+        assert g.ok, (T, str(g))
+        hdr = ws[:1024].cpu().numpy()
+        assert not hdr.any()
+
+
+def test_zero_tokens_is_noop(dev):
+    sg = dev["sg"]
+    moe = sg.FlintMoE(max_tokens=64)
+    st = moe.forward_raw(dev["W"].struct(), None, 0, None, None, None, None, 0, None)
+    assert st == sg.FLINT_OK
