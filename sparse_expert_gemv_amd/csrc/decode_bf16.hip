@@ -115,6 +115,7 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
 
 // Top-k of token t by score, one wave.  Ranks on the logit (the sigmoid is
 // strictly increasing), ties to the lower expert index: key = (logit, ~e).
+// Logits were written by other blocks of this launch: coherent loads.
 __device__ void topk_token(const LayerArgs& a, int t) {
   const int lane = threadIdx.x & (kWave - 1);
   const int E = a.E, k = a.k;
@@ -124,7 +125,7 @@ __device__ void topk_token(const LayerArgs& a, int t) {
     const int e = lane * 4 + q;
     key[q] = 0;
     if (e < E) {
-      const float z = a.ws.logits[(size_t)t * E + e];
+      const float z = load_coherent(a.ws.logits + (size_t)t * E + e);
       key[q] = ((uint64_t)ord_f32(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
     }
   }
@@ -135,14 +136,8 @@ __device__ void topk_token(const LayerArgs& a, int t) {
     zsel[j] = 0.f;
     isel[j] = 0;
     if (j < k) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint64_t o = __shfl_xor(best, off);
-        best = o > best ? o : best;
-      }
+      const uint64_t best =
+          wave_max_u64(max_u64(max_u64(key[0], key[1]), max_u64(key[2], key[3])));
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (key[q] == best) key[q] = 0;
@@ -161,8 +156,8 @@ __device__ void topk_token(const LayerArgs& a, int t) {
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j < k && lane == j) {
       const float w = (a.renormalize ? s[j] / sum : s[j]) * a.routed_scale;
-      a.ws.ids[t * k + j] = isel[j];
-      a.ws.wts[t * k + j] = w;
+      store_coherent(a.ws.ids + t * k + j, isel[j]);
+      store_coherent(a.ws.wts + t * k + j, w);
       if (a.ids_out) a.ids_out[t * k + j] = isel[j];
       if (a.wts_out) a.wts_out[t * k + j] = w;
     }
@@ -185,7 +180,7 @@ __device__ void bucket_all(const LayerArgs& a, void* smem) {
   for (int i = tid; i < kMaxExperts * kMaskWords; i += blockDim.x) occ[i] = 0;
   __syncthreads();
   for (int s = tid; s < nslots; s += blockDim.x) {
-    const int e = a.ws.ids[s];
+    const int e = load_coherent(a.ws.ids + s);
     atomicAdd(&cnt[e], 1);
     atomicOr(&occ[e * kMaskWords + (s >> 5)], 1u << (s & 31));
   }
@@ -200,16 +195,8 @@ __device__ void bucket_all(const LayerArgs& a, void* smem) {
       sc += c[q];
       sf += c[q] > 0;
     }
-    int ic = sc, iff = sf;  // inclusive scans over lanes
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int oc = __shfl_up(ic, d);
-      const int of = __shfl_up(iff, d);
-      if (lane >= d) {
-        ic += oc;
-        iff += of;
-      }
-    }
+    const int ic = wave_incl_scan(sc);   // inclusive scans over lanes
+    const int iff = wave_incl_scan(sf);
     int o = ic - sc, act = iff - sf;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -229,7 +216,7 @@ __device__ void bucket_all(const LayerArgs& a, void* smem) {
   }
   __syncthreads();
   for (int s = tid; s < nslots; s += blockDim.x) {
-    const int e = a.ws.ids[s];
+    const int e = load_coherent(a.ws.ids + s);
     const uint32_t* m = occ + e * kMaskWords;
     int rank = __popc(m[s >> 5] & ((1u << (s & 31)) - 1u));
     for (int w = 0; w < (s >> 5); ++w) rank += __popc(m[w]);
@@ -277,33 +264,14 @@ __global__ __launch_bounds__(256) void router_topk_shared_kernel(LayerArgs a, in
     acc[r] = wave_sum_lane63(acc[r]);
     const int e = e0 + r;
     if (lane == kWave - 1 && e < a.E)
-      a.ws.logits[(size_t)t * a.E + e] = acc[r] + (a.router_b ? a.router_b[e] : 0.f);
+      store_coherent(a.ws.logits + (size_t)t * a.E + e,
+                     acc[r] + (a.router_b ? a.router_b[e] : 0.f));
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = ticket_acq_rel(&a.ws.header[kTokCounterBase + t]);
-    s_last = prev == (uint32_t)(blocks_per_token - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-
-  // Last router block of token t: every logit of t is visible.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (threadIdx.x == 0) store_release_zero(&a.ws.header[kTokCounterBase + t]);
+  // The last router block of token t sees every logit of t.
+  if (!last_block_ticket(&a.ws.header[kTokCounterBase + t], blocks_per_token, &s_last)) return;
   if (wave == 0) topk_token(a, t);
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = ticket_acq_rel(&a.ws.header[0]);
-    s_last = prev == (uint32_t)(a.T - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-
-  // Last token: every token's selection is visible.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (threadIdx.x == 0) store_release_zero(&a.ws.header[0]);
+  // The last token to finish sees every token's selection.
+  if (!last_block_ticket(&a.ws.header[0], a.T, &s_last)) return;
   bucket_all(a, smem);
 }
 
@@ -319,6 +287,41 @@ __global__ __launch_bounds__(256) void gateup_routed_kernel(LayerArgs a) {
   gateup_block(w13, unit * kPairsPerBlock, cnt, RoutedList{a.ws.slots + off, a.k}, a.x, a.ws.h, xs);
 }
 
+// The w2 rows [r0, r0 + 8) of one item (an active expert, or the shared
+// expert as the last item): one 16-byte vector per row per lane.
+struct DownItem {
+  const uint16_t* w2;
+  const int32_t* list;  // routed: slot ids; shared: nullptr (tokens 0..T-1)
+  int cnt;
+};
+
+__device__ __forceinline__ DownItem down_item(const LayerArgs& a, int item, int nA) {
+  DownItem it;
+  if (item < nA) {
+    const int e = a.ws.active[item];
+    it.w2 = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)e * H * I;
+    it.list = a.ws.slots + a.ws.offsets[e];
+    it.cnt = a.ws.counts[e];
+  } else {
+    it.w2 = reinterpret_cast<const uint16_t*>(a.shared.w2);
+    it.list = nullptr;
+    it.cnt = a.T;
+  }
+  return it;
+}
+
+__device__ __forceinline__ void load_rows(u32x4 (&wv)[kDownRows], const uint16_t* w2, int r0,
+                                          int lane) {
+#pragma unroll
+  for (int r = 0; r < kDownRows; ++r)
+    wv[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I)[lane];
+}
+
+// Each block owns output rows [r0, r0 + 8).  Waves take the items (active
+// experts, then the shared expert) round-robin, keeping the next item's rows
+// in flight while the current one is reduced.  Per (slot, row) the 64-lane
+// partial dot products are summed in a fixed tree and parked in LDS; the
+// block then combines shared + sum_j w_j * routed_j in a fixed order.
 __global__ __launch_bounds__(kDownThreads) void down_combine_kernel(LayerArgs a) {
   __shared__ float part[(kMaxTopK + 1) * kDecodeMaxT * kDownRows];
   const int lane = threadIdx.x & (kWave - 1);
@@ -328,40 +331,37 @@ __global__ __launch_bounds__(kDownThreads) void down_combine_kernel(LayerArgs a)
   const int T = a.T, k = a.k;
   const int nA = *a.ws.n_active;
 
-  for (int item = wave; item <= nA; item += kWaves) {
-    const bool shared = item == nA;
-    const uint16_t* w2;
-    const int32_t* list = nullptr;
-    int cnt;
-    if (!shared) {
-      const int e = a.ws.active[item];
-      w2 = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)e * H * I;
-      list = a.ws.slots + a.ws.offsets[e];
-      cnt = a.ws.counts[e];
-    } else {
-      w2 = reinterpret_cast<const uint16_t*>(a.shared.w2);
-      cnt = T;
-    }
-    u32x4 wv[kDownRows];
+  int item = wave;
+  u32x4 cur[kDownRows], nxt[kDownRows];
+  DownItem it{}, it_next{};
+  if (item <= nA) {
+    it_next = down_item(a, item, nA);
+    load_rows(nxt, it_next.w2, r0, lane);
+  }
+  for (; item <= nA; item += kWaves) {
+    it = it_next;
 #pragma unroll
-    for (int r = 0; r < kDownRows; ++r)
-      wv[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I)[lane];
-    for (int j = 0; j < cnt; ++j) {
-      const int hrow = shared ? T * k + j : list[j];
+    for (int r = 0; r < kDownRows; ++r) cur[r] = nxt[r];
+    if (item + kWaves <= nA) {
+      it_next = down_item(a, item + kWaves, nA);
+      load_rows(nxt, it_next.w2, r0, lane);
+    }
+    for (int j = 0; j < it.cnt; ++j) {
+      const int hrow = it.list ? it.list[j] : T * k + j;
       const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)hrow * I) + lane * 2;
       const f32x4 h0 = hp[0], h1 = hp[1];
       float acc[kDownRows];
 #pragma unroll
       for (int r = 0; r < kDownRows; ++r) {
-        float s = bf16_lo(wv[r].x) * h0.x;
-        s = fmaf(bf16_hi(wv[r].x), h0.y, s);
-        s = fmaf(bf16_lo(wv[r].y), h0.z, s);
-        s = fmaf(bf16_hi(wv[r].y), h0.w, s);
-        s = fmaf(bf16_lo(wv[r].z), h1.x, s);
-        s = fmaf(bf16_hi(wv[r].z), h1.y, s);
-        s = fmaf(bf16_lo(wv[r].w), h1.z, s);
-        s = fmaf(bf16_hi(wv[r].w), h1.w, s);
-        acc[r] = wave_sum_lane63(s);
+        float v = bf16_lo(cur[r].x) * h0.x;
+        v = fmaf(bf16_hi(cur[r].x), h0.y, v);
+        v = fmaf(bf16_lo(cur[r].y), h0.z, v);
+        v = fmaf(bf16_hi(cur[r].y), h0.w, v);
+        v = fmaf(bf16_lo(cur[r].z), h1.x, v);
+        v = fmaf(bf16_hi(cur[r].z), h1.y, v);
+        v = fmaf(bf16_lo(cur[r].w), h1.z, v);
+        v = fmaf(bf16_hi(cur[r].w), h1.w, v);
+        acc[r] = wave_sum_lane63(v);
       }
       if (lane == kWave - 1)
 #pragma unroll

@@ -63,14 +63,82 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   return v;
 }
 
-// Device-scope (all XCDs) completion ticket: returns the previous count.
-// Release of this block's earlier global writes, acquire of the others'.
-__device__ __forceinline__ uint32_t ticket_acq_rel(uint32_t* counter) {
-  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+// Cross-block hand-off without whole-L2 writeback/invalidate: values that
+// another block reads in the same launch are stored and loaded as relaxed
+// agent-scope atomics (write-through / coherent-level accesses, "sc1"); a
+// block drains its own outstanding memory operations (s_waitcnt 0) and
+// synchronises before taking a completion ticket, so every value it stored
+// is visible device-wide when the ticket is counted.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void store_release_zero(uint32_t* counter) {
-  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void drain_memory_ops() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Block-wide completion ticket: all threads drain their stores, then thread 0
+// counts the block in; returns true (to every thread) in the block that
+// completes the count of `expected` blocks, after resetting the counter.
+__device__ __forceinline__ bool last_block_ticket(uint32_t* counter, uint32_t expected,
+                                                  int* s_flag) {
+  drain_memory_ops();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == expected - 1;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// DPP move of a 64-bit value (two 32-bit halves).
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, kCtrl, kRowMask, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), kCtrl, kRowMask, 0xF, true);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the 64 lanes, returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp64<0xB1>(v));
+  v = max_u64(v, dpp64<0x4E>(v));
+  v = max_u64(v, dpp64<0x141>(v));
+  v = max_u64(v, dpp64<0x140>(v));
+  v = max_u64(v, dpp64<0x142, 0xA>(v));
+  v = max_u64(v, dpp64<0x143, 0xC>(v));
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, true);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, true);  // row_bcast:31
+  return v;
 }
 
 }  // namespace flint
