@@ -108,21 +108,26 @@ typedef struct flint_moe_weights {
 
 /* Byte offsets of the regions of a workspace sized for T tokens.  Exposed so
  * that tests can read the intermediate results of one forward (a region is
- * valid once the forward that wrote it has completed). */
+ * valid once the forward that wrote it has completed).  Lists that the
+ * kernels build with atomics (the union U and the per-expert slot lists) are
+ * in no particular order; the layer output does not depend on that order. */
 typedef struct flint_moe_ws_layout {
   size_t total_bytes;
-  size_t header;    /* uint32 [256]: completion counters (must be zero before first use) */
+  size_t header;    /* uint32 [1024]: counters; zero before first use and after every
+                       completed forward, except word 4 (see error_word) */
+  size_t error_word;/* uint32 inside the header: nonzero once a bounded wait of the
+                       fused decode kernel timed out (results of that forward are
+                       invalid); sticky until the caller clears it */
   size_t logits;    /* fp32 [T][E]: z (router GEMV + bias) */
   size_t topk_ids;  /* int32 [T][k]: selected experts in rank order */
   size_t topk_w;    /* fp32 [T][k]: routing weights */
-  size_t n_active;  /* int32 [1]: |U|, the number of distinct selected experts */
-  size_t active;    /* int32 [E]: U, ascending */
-  size_t counts;    /* int32 [E]: slots per expert */
-  size_t offsets;   /* int32 [E+1]: exclusive prefix sum of counts */
-  size_t slots;     /* int32 [T*k]: slot ids s = t*k + j grouped by expert (ascending),
-                       ascending within an expert */
+  size_t n_active;  /* int32 inside the header: |U| while a forward runs (reset to 0 at its end) */
+  size_t active;    /* int32 [E]: U, first |U| entries */
+  size_t counts;    /* int32 [E] inside the header: slots per expert while a forward runs */
+  size_t lists;     /* int32 [E][T]: slot ids s = t*k + j routed to expert e */
   size_t h;         /* fp32 [T*k + T][I]: h of slot s in row s; h of the shared expert
                        for token t in row T*k + t */
+  size_t y;         /* fp32 [T*k + T][H]: unweighted down projection of each h row */
   size_t extra;     /* path-private scratch (prefill-sized T only) */
 } flint_moe_ws_layout;
 
@@ -132,7 +137,7 @@ typedef struct flint_moe_ws_layout {
 flint_status flint_moe_init(const flint_moe_config* cfg, flint_moe_ctx** ctx_out);
 
 /* Bytes of workspace a forward of T tokens needs (0 for T <= 0 or NULL ctx).
- * The first 1024 bytes (the header) must be zero before the workspace is used
+ * The first 4096 bytes (the header) must be zero before the workspace is used
  * for the first time; every completed forward leaves them zero again. */
 size_t flint_moe_workspace_bytes(const flint_moe_ctx* ctx, int32_t T);
 

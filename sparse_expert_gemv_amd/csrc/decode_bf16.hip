@@ -1,18 +1,29 @@
-// Decode-sized (T <= 64) bf16 path of the Flint MoE layer on gfx950.
+// Decode-sized (T <= 64) bf16 path of the Flint MoE layer on gfx950: the
+// whole layer in one launch.
 //
-// Three launches on the caller's stream:
-//   1. router_topk_shared : router GEMV (bf16 x bf16 -> fp32) for every token;
-//      the last router block of a token picks its top-k by sigmoid score and
-//      writes the routing weights; the last token to finish buckets all
-//      (token, rank) slots by expert.  Extra blocks of the same launch run the
-//      shared expert's gate/up GEMV, which needs nothing but x.
-//   2. gateup_routed      : fused gate/up GEMV + SiLU-and-mul over the union
-//      of selected experts; each expert's 4 MiB of w13 rows is streamed once
-//      for all of its tokens.
-//   3. down_combine       : down GEMV of every active expert and the shared
-//      expert; each block owns 8 output rows, scales by the routing weights
-//      and reduces across experts in a fixed order (no atomics), then rounds
-//      once to bf16.
+// The layer is cut into work items of ~64 KiB of weights each, in an order
+// where an item only ever waits for items before it:
+//   router    (token t, 16 router rows)   T * ceil(E/16) items
+//   shared    (8 gate/up row pairs of the shared expert, all T tokens)  64
+//   gate/up   (active expert a, 8 row pairs)   max|U| * 64
+//   down      (expert, 64 output rows): the shared expert first, then each
+//             active expert                   (1 + max|U|) * 32
+// Block b takes items b, b + G, b + 2G, ... (G = resident blocks), so the
+// phases overlap: the shared expert streams while tokens are routed, the
+// down rows of early experts stream while later experts finish gate/up.
+// Hand-offs between blocks use completion counters in the workspace header
+// and coherent (write-through) stores/loads, never whole-cache flushes:
+//   - the last router item of token t picks its top-k and appends its slots
+//     to the per-expert lists (the first slot of an expert also appends the
+//     expert to the union U); the last token to finish raises routing-done;
+//   - gate/up item (a, .) waits for routing-done; 64 finished items of a
+//     complete expert a's h;
+//   - down item (a, tile) waits for expert a's h and writes y for its rows;
+//     the last of the |U| + 1 down items of a tile combines the tile:
+//     out = y_shared + sum_j w_j y_j in a fixed order, rounded once to bf16;
+//   - the last block to run out of items resets every counter to zero.
+// Every wait is bounded; a timeout sets an error word instead of hanging.
+//
 // What is computed follows "vLLM Day-0 Support for Recursive's Flint"
 // (section "Flint Model Architecture", bullet "MoE Structure"; section
 // "Optimization Strategies", bullets "Small-batch MoE Kernels" and
@@ -27,41 +38,83 @@ namespace {
 
 constexpr int H = kHidden;
 constexpr int I = kInter;
+constexpr int kThreads = 256;
 constexpr int kVecH = H / 8;                  // 16-byte vectors per H row (256)
 constexpr int kVecPerLaneH = kVecH / kWave;   // 4
-constexpr int kRouterRowsPerBlock = 16;       // 4 waves x 4 rows
-constexpr int kPairsPerBlock = 8;             // gate/up unit: 8 (gate, up) row pairs
-constexpr int kUnitsPerExpert = I / kPairsPerBlock;  // 64
+constexpr int kRouterRowsPerItem = 16;        // 4 waves x 4 rows
+constexpr int kPairsPerItem = 8;              // gate/up item: 8 (gate, up) row pairs
+constexpr int kUnitsPerExpert = I / kPairsPerItem;  // 64
+constexpr int kTileRows = 64;                 // down item: 64 output rows (16 per wave)
+constexpr int kRowsPerWave = kTileRows / 4;
+constexpr int kTiles = H / kTileRows;         // 32
 constexpr int kXChunk = 8;                    // tokens staged in LDS at a time
-constexpr int kDownRows = 8;                  // output rows per down block
-constexpr int kDownThreads = 512;
+constexpr uint32_t kSpinLimit = 1u << 18;  // ~0.3 s of polling
 
 static_assert(H % (8 * kWave) == 0, "H must be a multiple of 512");
 static_assert(I == 8 * kWave, "down GEMV maps one 16-byte vector of a w2 row per lane");
+static_assert(kTiles <= 32, "tile tickets");
 
-// Slot list of one routed expert: entry j is slot s = t*k + rank.
-struct RoutedList {
-  const int32_t* slots;
-  int k;
-  __device__ int token(int j) const { return slots[j] / k; }
-  __device__ int hrow(int j) const { return slots[j]; }
+struct Plan {
+  int G;            // blocks in the grid
+  int rg;           // router items per token
+  int n_router;     // T * rg
+  int g_shared;     // first shared gate/up item
+  int g_routed;     // first routed gate/up item
+  int d_shared;     // first down item (shared expert)
+  int d_routed;     // first routed down item
+  int n_items;
+  int max_active;   // min(E, T*k)
 };
 
-// All T tokens of the shared expert; h rows follow the T*k routed rows.
-struct SharedList {
-  int base;
-  __device__ int token(int j) const { return j; }
-  __device__ int hrow(int j) const { return base + j; }
+// ---------------------------------------------------------------- waiting
+
+// Thread 0 polls `*p >= target` with a bounded number of sleeps; the result
+// is broadcast to the block.  A timeout raises the sticky error word.
+__device__ __forceinline__ void block_wait(const uint32_t* p, uint32_t target, uint32_t* err) {
+  if (threadIdx.x == 0) {
+    uint32_t it = 0;
+    while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (++it == kSpinLimit) {
+        __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+// Every thread drains its stores, then thread 0 adds 1 to *counter.
+__device__ __forceinline__ void block_signal(uint32_t* counter) {
+  drain_memory_ops();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int32_t bcast_load(const uint32_t* p, int* s_val) {
+  if (threadIdx.x == 0) *s_val = (int)__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int v = *s_val;
+  __syncthreads();
+  return v;
+}
+
+// ---------------------------------------------------------------- gate/up
+
+// Token list of one gate/up item, staged in LDS: x row and h row per entry.
+struct TokenList {
+  const int16_t* tok;  // LDS
+  const int16_t* hrow; // LDS
 };
 
 // One block (4 waves) computes h = silu(gate) * up for the row pairs
 // [p0, p0 + 8) of one expert, for `count` tokens.  Wave w owns pairs
 // p0 + 2w and p0 + 2w + 1: four 4 KiB rows held in registers while the
 // tokens' x vectors stream through LDS.
-template <class List>
-__device__ __forceinline__ void gateup_block(const uint16_t* __restrict__ w13, int p0, int count,
-                                             const List& list, const uint16_t* __restrict__ x,
-                                             float* __restrict__ h, u32x4* xs) {
+__device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ w13, int p0, int count,
+                                            const TokenList& list, const uint16_t* __restrict__ x,
+                                            float* h, u32x4* xs) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int p = p0 + 2 * wave;
@@ -79,10 +132,10 @@ __device__ __forceinline__ void gateup_block(const uint16_t* __restrict__ w13, i
   for (int c0 = 0; c0 < count; c0 += kXChunk) {
     const int n = min(kXChunk, count - c0);
     __syncthreads();
-    for (int q = threadIdx.x; q < n * kVecH; q += blockDim.x) {
+    for (int q = threadIdx.x; q < n * kVecH; q += kThreads) {
       const int j = q / kVecH;
       const int col = q - j * kVecH;
-      xs[q] = reinterpret_cast<const u32x4*>(x + (size_t)list.token(c0 + j) * H)[col];
+      xs[q] = reinterpret_cast<const u32x4*>(x + (size_t)list.tok[c0 + j] * H)[col];
     }
     __syncthreads();
     for (int j = 0; j < n; ++j) {
@@ -96,13 +149,15 @@ __device__ __forceinline__ void gateup_block(const uint16_t* __restrict__ w13, i
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = wave_sum_lane63(acc[r]);
       if (lane == kWave - 1) {
-        float* hr = h + (size_t)list.hrow(c0 + j) * I + p;
-        hr[0] = silu(acc[0]) * acc[2];
-        hr[1] = silu(acc[1]) * acc[3];
+        float* hr = h + (size_t)list.hrow[c0 + j] * I + p;
+        store_coherent(hr, silu(acc[0]) * acc[2]);
+        store_coherent(hr + 1, silu(acc[1]) * acc[3]);
       }
     }
   }
 }
+
+// ---------------------------------------------------------------- routing
 
 // Order-preserving map of fp32 onto uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t ord_f32(float f) {
@@ -113,12 +168,12 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Top-k of token t by score, one wave.  Ranks on the logit (the sigmoid is
-// strictly increasing), ties to the lower expert index: key = (logit, ~e).
-// Logits were written by other blocks of this launch: coherent loads.
-__device__ void topk_token(const LayerArgs& a, int t) {
+// Top-k of token t by score, one wave, then the token's slots are appended
+// to the per-expert lists.  Ranks on the logit (the sigmoid is strictly
+// increasing), ties to the lower expert index: key = (logit, ~e).
+__device__ void route_token(const LayerArgs& a, int t) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int E = a.E, k = a.k;
+  const int E = a.E, k = a.k, T = a.T;
   uint64_t key[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -152,95 +207,34 @@ __device__ void topk_token(const LayerArgs& a, int t) {
     s[j] = sigmoid(zsel[j]);
     if (j < k) sum += s[j];
   }
+  uint32_t* hdr = a.ws.header;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j < k && lane == j) {
+      const int e = isel[j];
       const float w = (a.renormalize ? s[j] / sum : s[j]) * a.routed_scale;
-      store_coherent(a.ws.ids + t * k + j, isel[j]);
+      store_coherent(a.ws.ids + t * k + j, e);
       store_coherent(a.ws.wts + t * k + j, w);
-      if (a.ids_out) a.ids_out[t * k + j] = isel[j];
+      if (a.ids_out) a.ids_out[t * k + j] = e;
       if (a.wts_out) a.wts_out[t * k + j] = w;
-    }
-  }
-}
-
-// Bucket every (token, rank) slot by expert, 256 threads.  Slots of one
-// expert are placed in ascending slot order: the rank of slot s among its
-// expert's slots is the number of set bits below s in that expert's
-// occupancy mask.
-__device__ void bucket_all(const LayerArgs& a, void* smem) {
-  constexpr int kMaskWords = kDecodeMaxT * kMaxTopK / 32;  // 16
-  int* cnt = reinterpret_cast<int*>(smem);                   // [256]
-  int* off = cnt + kMaxExperts;                              // [256]
-  uint32_t* occ = reinterpret_cast<uint32_t*>(off + kMaxExperts);  // [256][16]
-  const int E = a.E;
-  const int nslots = a.T * a.k;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kMaxExperts; i += blockDim.x) cnt[i] = 0;
-  for (int i = tid; i < kMaxExperts * kMaskWords; i += blockDim.x) occ[i] = 0;
-  __syncthreads();
-  for (int s = tid; s < nslots; s += blockDim.x) {
-    const int e = load_coherent(a.ws.ids + s);
-    atomicAdd(&cnt[e], 1);
-    atomicOr(&occ[e * kMaskWords + (s >> 5)], 1u << (s & 31));
-  }
-  __syncthreads();
-  if (tid < kWave) {
-    const int lane = tid;
-    int c[4], sc = 0, sf = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      c[q] = e < E ? cnt[e] : 0;
-      sc += c[q];
-      sf += c[q] > 0;
-    }
-    const int ic = wave_incl_scan(sc);   // inclusive scans over lanes
-    const int iff = wave_incl_scan(sf);
-    int o = ic - sc, act = iff - sf;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      if (e < E) {
-        a.ws.counts[e] = c[q];
-        a.ws.offsets[e] = o;
-        off[e] = o;
-        if (c[q] > 0) a.ws.active[act++] = e;
-        o += c[q];
+      const uint32_t c = __hip_atomic_fetch_add(hdr + kHdrCounts + e, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      store_coherent(a.ws.lists + (size_t)e * T + c, t * k + j);
+      if (c == 0) {
+        const uint32_t pos = __hip_atomic_fetch_add(hdr + kHdrNActive, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        store_coherent(a.ws.active + pos, e);
       }
     }
-    if (lane == kWave - 1) {
-      a.ws.offsets[E] = ic;
-      *a.ws.n_active = iff;
-    }
-  }
-  __syncthreads();
-  for (int s = tid; s < nslots; s += blockDim.x) {
-    const int e = load_coherent(a.ws.ids + s);
-    const uint32_t* m = occ + e * kMaskWords;
-    int rank = __popc(m[s >> 5] & ((1u << (s & 31)) - 1u));
-    for (int w = 0; w < (s >> 5); ++w) rank += __popc(m[w]);
-    a.ws.slots[off[e] + rank] = s;
   }
 }
 
-__global__ __launch_bounds__(256) void router_topk_shared_kernel(LayerArgs a, int n_router_blocks,
-                                                                 int blocks_per_token) {
-  __shared__ u32x4 smem[kXChunk * kVecH];  // 32 KiB: x staging or bucketing tables
-  __shared__ int s_last;
-
-  if ((int)blockIdx.x >= n_router_blocks) {
-    const int unit = blockIdx.x - n_router_blocks;
-    gateup_block(reinterpret_cast<const uint16_t*>(a.shared.w13), unit * kPairsPerBlock, a.T,
-                 SharedList{a.T * a.k}, a.x, a.ws.h, smem);
-    return;
-  }
-
+__device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_flag) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int t = blockIdx.x / blocks_per_token;
-  const int g = blockIdx.x - t * blocks_per_token;
-  const int e0 = g * kRouterRowsPerBlock + wave * 4;
+  const int t = item / P.rg;
+  const int g = item - t * P.rg;
+  const int e0 = g * kRouterRowsPerItem + wave * 4;
 
   const u32x4* xr = reinterpret_cast<const u32x4*>(a.x + (size_t)t * H);
   u32x4 xv[kVecPerLaneH];
@@ -267,133 +261,203 @@ __global__ __launch_bounds__(256) void router_topk_shared_kernel(LayerArgs a, in
       store_coherent(a.ws.logits + (size_t)t * a.E + e,
                      acc[r] + (a.router_b ? a.router_b[e] : 0.f));
   }
-  // The last router block of token t sees every logit of t.
-  if (!last_block_ticket(&a.ws.header[kTokCounterBase + t], blocks_per_token, &s_last)) return;
-  if (wave == 0) topk_token(a, t);
-  // The last token to finish sees every token's selection.
-  if (!last_block_ticket(&a.ws.header[0], a.T, &s_last)) return;
-  bucket_all(a, smem);
+  uint32_t* hdr = a.ws.header;
+  // The last router item of token t sees every logit of t.
+  if (!last_block_ticket(hdr + kHdrTokTicket + t, P.rg, s_flag)) return;
+  if (wave == 0) route_token(a, t);
+  // The last token to finish sees every token's slots.
+  if (!last_block_ticket(hdr + kHdrTokensDone, a.T, s_flag)) return;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(hdr + kHdrRoutingDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(256) void gateup_routed_kernel(LayerArgs a) {
-  __shared__ u32x4 xs[kXChunk * kVecH];
-  const int ai = blockIdx.x / kUnitsPerExpert;
-  const int unit = blockIdx.x - ai * kUnitsPerExpert;
-  if (ai >= *a.ws.n_active) return;
-  const int e = a.ws.active[ai];
-  const int off = a.ws.offsets[e];
-  const int cnt = a.ws.counts[e];
-  const uint16_t* w13 = reinterpret_cast<const uint16_t*>(a.routed.w13) + (size_t)e * 2 * I * H;
-  gateup_block(w13, unit * kPairsPerBlock, cnt, RoutedList{a.ws.slots + off, a.k}, a.x, a.ws.h, xs);
-}
+// ---------------------------------------------------------------- down
 
-// The w2 rows [r0, r0 + 8) of one item (an active expert, or the shared
-// expert as the last item): one 16-byte vector per row per lane.
-struct DownItem {
-  const uint16_t* w2;
-  const int32_t* list;  // routed: slot ids; shared: nullptr (tokens 0..T-1)
-  int cnt;
-};
-
-__device__ __forceinline__ DownItem down_item(const LayerArgs& a, int item, int nA) {
-  DownItem it;
-  if (item < nA) {
-    const int e = a.ws.active[item];
-    it.w2 = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)e * H * I;
-    it.list = a.ws.slots + a.ws.offsets[e];
-    it.cnt = a.ws.counts[e];
-  } else {
-    it.w2 = reinterpret_cast<const uint16_t*>(a.shared.w2);
-    it.list = nullptr;
-    it.cnt = a.T;
-  }
-  return it;
-}
-
-__device__ __forceinline__ void load_rows(u32x4 (&wv)[kDownRows], const uint16_t* w2, int r0,
-                                          int lane) {
-#pragma unroll
-  for (int r = 0; r < kDownRows; ++r)
-    wv[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I)[lane];
-}
-
-// Each block owns output rows [r0, r0 + 8).  Waves take the items (active
-// experts, then the shared expert) round-robin, keeping the next item's rows
-// in flight while the current one is reduced.  Per (slot, row) the 64-lane
-// partial dot products are summed in a fixed tree and parked in LDS; the
-// block then combines shared + sum_j w_j * routed_j in a fixed order.
-__global__ __launch_bounds__(kDownThreads) void down_combine_kernel(LayerArgs a) {
-  __shared__ float part[(kMaxTopK + 1) * kDecodeMaxT * kDownRows];
+// Down item: rows [r0, r0 + 64) of one expert's w2 (wave w: 16 rows, one
+// 16-byte vector per row per lane), for each of the expert's slots:
+// y[hrow][row] = w2[row] . h[hrow], summed over the 64 lanes in a fixed tree.
+__device__ __forceinline__ void down_rows(const uint16_t* __restrict__ w2, int r0, int count,
+                                          const int16_t* hrows, const float* h, float* y) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  constexpr int kWaves = kDownThreads / kWave;
-  const int r0 = blockIdx.x * kDownRows;
-  const int T = a.T, k = a.k;
-  const int nA = *a.ws.n_active;
-
-  int item = wave;
-  u32x4 cur[kDownRows], nxt[kDownRows];
-  DownItem it{}, it_next{};
-  if (item <= nA) {
-    it_next = down_item(a, item, nA);
-    load_rows(nxt, it_next.w2, r0, lane);
+  const int rw = r0 + wave * kRowsPerWave;
+  u32x4 wv[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r)
+    wv[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(rw + r) * I)[lane];
+  for (int j = 0; j < count; ++j) {
+    // Keep the weights packed across slots: widening all 16 rows to fp32
+    // once would cost 128 registers.
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) asm volatile("" : "+v"(wv[r]));
+    const int hr = hrows[j];
+    const float* hp = h + (size_t)hr * I + lane * 8;
+    float hv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) hv[q] = load_coherent(hp + q);
+    float acc[kRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      float v = bf16_lo(wv[r].x) * hv[0];
+      v = fmaf(bf16_hi(wv[r].x), hv[1], v);
+      v = fmaf(bf16_lo(wv[r].y), hv[2], v);
+      v = fmaf(bf16_hi(wv[r].y), hv[3], v);
+      v = fmaf(bf16_lo(wv[r].z), hv[4], v);
+      v = fmaf(bf16_hi(wv[r].z), hv[5], v);
+      v = fmaf(bf16_lo(wv[r].w), hv[6], v);
+      v = fmaf(bf16_hi(wv[r].w), hv[7], v);
+      acc[r] = wave_sum_lane63(v);
+    }
+    if (lane == kWave - 1) {
+      float* yr = y + (size_t)hr * H + rw;
+#pragma unroll
+      for (int r = 0; r < kRowsPerWave; ++r) store_coherent(yr + r, acc[r]);
+    }
   }
-  for (; item <= nA; item += kWaves) {
-    it = it_next;
-#pragma unroll
-    for (int r = 0; r < kDownRows; ++r) cur[r] = nxt[r];
-    if (item + kWaves <= nA) {
-      it_next = down_item(a, item + kWaves, nA);
-      load_rows(nxt, it_next.w2, r0, lane);
-    }
-    for (int j = 0; j < it.cnt; ++j) {
-      const int hrow = it.list ? it.list[j] : T * k + j;
-      const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)hrow * I) + lane * 2;
-      const f32x4 h0 = hp[0], h1 = hp[1];
-      float acc[kDownRows];
-#pragma unroll
-      for (int r = 0; r < kDownRows; ++r) {
-        float v = bf16_lo(cur[r].x) * h0.x;
-        v = fmaf(bf16_hi(cur[r].x), h0.y, v);
-        v = fmaf(bf16_lo(cur[r].y), h0.z, v);
-        v = fmaf(bf16_hi(cur[r].y), h0.w, v);
-        v = fmaf(bf16_lo(cur[r].z), h1.x, v);
-        v = fmaf(bf16_hi(cur[r].z), h1.y, v);
-        v = fmaf(bf16_lo(cur[r].w), h1.z, v);
-        v = fmaf(bf16_hi(cur[r].w), h1.w, v);
-        acc[r] = wave_sum_lane63(v);
+}
+
+// out rows [r0, r0 + 64) of every token: shared + sum_j w_j * y_j, fixed order.
+__device__ void combine_tile(const LayerArgs& a, int r0) {
+  const int T = a.T, k = a.k;
+  for (int q = threadIdx.x; q < T * kTileRows; q += kThreads) {
+    const int t = q / kTileRows;
+    const int r = r0 + (q - t * kTileRows);
+    float o = load_coherent(a.ws.y + (size_t)(T * k + t) * H + r);
+    for (int j = 0; j < k; ++j)
+      o = fmaf(load_coherent(a.ws.wts + t * k + j),
+               load_coherent(a.ws.y + (size_t)(t * k + j) * H + r), o);
+    a.out[(size_t)t * H + r] = f32_to_bf16_rne(o);
+  }
+}
+
+// ---------------------------------------------------------------- kernel
+
+__global__ __launch_bounds__(kThreads) void moe_decode_kernel(LayerArgs a, Plan P) {
+  __shared__ u32x4 xs[kXChunk * kVecH];                  // 32 KiB: x staging
+  __shared__ int16_t s_tok[kDecodeMaxT], s_hrow[kDecodeMaxT];
+  __shared__ int s_flag, s_val, s_cnt;
+  uint32_t* hdr = a.ws.header;
+  uint32_t* err = hdr + kHdrError;
+  const int T = a.T, k = a.k;
+
+  for (int item = blockIdx.x; item < P.n_items; item += P.G) {
+    if (item < P.n_router) {
+      router_item(a, P, item, &s_flag);
+    } else if (item < P.g_routed) {
+      // Shared expert gate/up: all T tokens, h rows T*k + t.
+      const int unit = item - P.g_shared;
+      for (int q = threadIdx.x; q < T; q += kThreads) {
+        s_tok[q] = (int16_t)q;
+        s_hrow[q] = (int16_t)(T * k + q);
       }
-      if (lane == kWave - 1)
-#pragma unroll
-        for (int r = 0; r < kDownRows; ++r) part[hrow * kDownRows + r] = acc[r];
+      __syncthreads();
+      gateup_item(reinterpret_cast<const uint16_t*>(a.shared.w13), unit * kPairsPerItem, T,
+                  TokenList{s_tok, s_hrow}, a.x, a.ws.h, xs);
+      block_signal(hdr + kHdrSharedDone);
+    } else if (item < P.d_shared) {
+      // Routed gate/up: active index ai, unit.
+      const int ai = (item - P.g_routed) / kUnitsPerExpert;
+      const int unit = (item - P.g_routed) - ai * kUnitsPerExpert;
+      block_wait(hdr + kHdrRoutingDone, 1u, err);
+      if (ai >= bcast_load(hdr + kHdrNActive, &s_val)) continue;
+      if (threadIdx.x == 0) {
+        const int e = load_coherent(a.ws.active + ai);
+        s_val = e;
+        s_cnt = (int)__hip_atomic_load(hdr + kHdrCounts + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      const int e = s_val, cnt = s_cnt;
+      for (int q = threadIdx.x; q < cnt; q += kThreads) {
+        const int slot = load_coherent(a.ws.lists + (size_t)e * T + q);
+        s_tok[q] = (int16_t)(slot / k);
+        s_hrow[q] = (int16_t)slot;
+      }
+      __syncthreads();
+      const uint16_t* w13 = reinterpret_cast<const uint16_t*>(a.routed.w13) + (size_t)e * 2 * I * H;
+      gateup_item(w13, unit * kPairsPerItem, cnt, TokenList{s_tok, s_hrow}, a.x, a.ws.h, xs);
+      block_signal(hdr + kHdrExpertDone + ai);
+    } else {
+      // Down: (expert, 64-row tile); the shared expert's tiles come first.
+      const int di = item - P.d_shared;
+      const int ei = di / kTiles;          // 0: shared, 1 + ai: active index ai
+      const int tile = di - ei * kTiles;
+      const uint16_t* w2;
+      int cnt;
+      if (ei == 0) {
+        block_wait(hdr + kHdrSharedDone, (uint32_t)kUnitsPerExpert, err);
+        for (int q = threadIdx.x; q < T; q += kThreads) s_hrow[q] = (int16_t)(T * k + q);
+        w2 = reinterpret_cast<const uint16_t*>(a.shared.w2);
+        cnt = T;
+      } else {
+        const int ai = ei - 1;
+        block_wait(hdr + kHdrRoutingDone, 1u, err);
+        if (ai >= bcast_load(hdr + kHdrNActive, &s_val)) continue;
+        block_wait(hdr + kHdrExpertDone + ai, (uint32_t)kUnitsPerExpert, err);
+        if (threadIdx.x == 0) {
+          const int e = load_coherent(a.ws.active + ai);
+          s_val = e;
+          s_cnt = (int)__hip_atomic_load(hdr + kHdrCounts + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        const int e = s_val;
+        cnt = s_cnt;
+        for (int q = threadIdx.x; q < cnt; q += kThreads)
+          s_hrow[q] = (int16_t)load_coherent(a.ws.lists + (size_t)e * T + q);
+        w2 = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)e * H * I;
+      }
+      __syncthreads();
+      down_rows(w2, tile * kTileRows, cnt, s_hrow, a.ws.h, a.ws.y);
+      // The last of the |U| + 1 down items of this tile combines it.
+      const int n_active = bcast_load(hdr + kHdrNActive, &s_val);
+      if (last_block_ticket(hdr + kHdrTileTicket + tile, (uint32_t)(n_active + 1), &s_flag))
+        combine_tile(a, tile * kTileRows);
     }
+  }
+
+  // The last block to finish resets the per-forward counters.
+  if (!last_block_ticket(hdr + kHdrExit, (uint32_t)P.G, &s_flag)) return;
+  const int n_active = (int)__hip_atomic_load(hdr + kHdrNActive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = threadIdx.x; i < n_active; i += kThreads) {
+    const int e = load_coherent(a.ws.active + i);
+    __hip_atomic_store(hdr + kHdrCounts + e, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(hdr + kHdrExpertDone + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  for (int q = threadIdx.x; q < T * kDownRows; q += kDownThreads) {
-    const int t = q / kDownRows;
-    const int r = q - t * kDownRows;
-    float o = part[(T * k + t) * kDownRows + r];
-    for (int j = 0; j < k; ++j) o = fmaf(a.ws.wts[t * k + j], part[(t * k + j) * kDownRows + r], o);
-    a.out[(size_t)t * H + r0 + r] = f32_to_bf16_rne(o);
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(hdr + kHdrRoutingDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(hdr + kHdrNActive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(hdr + kHdrSharedDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const LayerArgs& a, hipStream_t stream, StageEvents* ev) {
+int decode_grid_limit() {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_decode_kernel, kThreads, 0) !=
+      hipSuccess)
+    return 0;
+  return cus * min(per_cu, 4);
+}
+
+hipError_t launch_decode_bf16(const LayerArgs& a, int grid_limit, hipStream_t stream,
+                              StageEvents* ev) {
+  Plan P;
+  P.rg = (a.E + kRouterRowsPerItem - 1) / kRouterRowsPerItem;
+  P.n_router = a.T * P.rg;
+  P.max_active = min(a.E, a.T * a.k);
+  P.g_shared = P.n_router;
+  P.g_routed = P.g_shared + kUnitsPerExpert;
+  P.d_shared = P.g_routed + P.max_active * kUnitsPerExpert;
+  P.d_routed = P.d_shared + kTiles;
+  P.n_items = P.d_routed + P.max_active * kTiles;
+  P.G = min(P.n_items, grid_limit);
   StageEvents none;
   StageEvents& e = ev ? *ev : none;
-  const int bpt = (a.E + kRouterRowsPerBlock - 1) / kRouterRowsPerBlock;
-  const int n_router = a.T * bpt;
   e.mark(stream);
-  hipLaunchKernelGGL(router_topk_shared_kernel, dim3(n_router + kUnitsPerExpert), dim3(256), 0,
-                     stream, a, n_router, bpt);
-  const int max_active = min(a.E, a.T * a.k);
-  e.mark(stream);
-  hipLaunchKernelGGL(gateup_routed_kernel, dim3(max_active * kUnitsPerExpert), dim3(256), 0, stream,
-                     a);
-  e.mark(stream);
-  hipLaunchKernelGGL(down_combine_kernel, dim3(H / kDownRows), dim3(kDownThreads), 0, stream, a);
+  hipLaunchKernelGGL(moe_decode_kernel, dim3(P.G), dim3(kThreads), 0, stream, a, P);
   e.mark(stream);
   return hipGetLastError();
 }

@@ -12,21 +12,30 @@ constexpr int kInter = 512;        // I
 constexpr int kMaxExperts = 256;   // E upper bound (four router scores per lane)
 constexpr int kMaxTopK = 8;
 constexpr int kDecodeMaxT = 64;    // largest T taken by the GEMV (decode) kernels
-constexpr int kHeaderWords = 256;  // workspace header: uint32 counters
-constexpr int kTokCounterBase = 64;
+constexpr int kHeaderWords = 1024;  // workspace header: uint32 counters (4 KiB)
+
+// Header words.  All are zero before a forward starts and zero after it ends.
+constexpr int kHdrTokensDone = 0;   // tokens whose selection is complete
+constexpr int kHdrRoutingDone = 1;  // 1 once every token is routed
+constexpr int kHdrNActive = 2;      // |U|
+constexpr int kHdrExit = 3;         // blocks that finished all their items
+constexpr int kHdrError = 4;        // sticky: a bounded wait timed out
+constexpr int kHdrSharedDone = 5;   // shared-expert gate/up items done
+constexpr int kHdrTokTicket = 64;   // [64]  router items done per token
+constexpr int kHdrCounts = 128;     // [256] slots routed to each expert
+constexpr int kHdrExpertDone = 384; // [256] gate/up items done per active index
+constexpr int kHdrTileTicket = 640; // [32]  down items done per 64-row output tile
 
 // Workspace regions, as device pointers.
 struct Workspace {
-  uint32_t* header;   // [0]: tokens-done counter; [64 + t]: router blocks done for token t
+  uint32_t* header;   // kHeaderWords counters (see above)
   float* logits;      // [T][E]
   int32_t* ids;       // [T][k]
   float* wts;         // [T][k]
-  int32_t* n_active;  // [1]
-  int32_t* active;    // [E]
-  int32_t* counts;    // [E]
-  int32_t* offsets;   // [E + 1]
-  int32_t* slots;     // [T*k]
+  int32_t* active;    // [E]: the union U, first n_active entries, in completion order
+  int32_t* lists;     // [E][T]: slot ids routed to expert e, first counts[e] entries
   float* h;           // [T*k + T][I]
+  float* y;           // [T*k + T][H]: per-slot down projections (unweighted)
   void* extra;
 };
 
@@ -66,6 +75,10 @@ struct StageEvents {
   }
 };
 
-hipError_t launch_decode_bf16(const LayerArgs& a, hipStream_t stream, StageEvents* ev);
+// Blocks a decode launch may use on the current device (resident capacity).
+int decode_grid_limit();
+
+hipError_t launch_decode_bf16(const LayerArgs& a, int grid_limit, hipStream_t stream,
+                              StageEvents* ev);
 
 }  // namespace flint

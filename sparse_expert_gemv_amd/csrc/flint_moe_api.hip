@@ -18,6 +18,8 @@
 struct flint_moe_ctx {
   flint_moe_config cfg;
   std::string last_error;
+  int grid_device = -1;  // device the cached decode grid limit belongs to
+  int grid_limit = 0;
 };
 
 namespace {
@@ -28,19 +30,21 @@ constexpr size_t kHeaderBytes = flint::kHeaderWords * sizeof(uint32_t);
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L) {
-  const size_t t = (size_t)T, E = (size_t)c.n_experts, k = (size_t)c.top_k, I = (size_t)c.inter;
+  const size_t t = (size_t)T, E = (size_t)c.n_experts, k = (size_t)c.top_k, I = (size_t)c.inter,
+               H = (size_t)c.hidden;
   size_t o = 0;
   std::memset(L, 0, sizeof(*L));
   L->header = o;   o = align_up(o + kHeaderBytes);
+  L->error_word = L->header + sizeof(uint32_t) * flint::kHdrError;
+  L->n_active = L->header + sizeof(uint32_t) * flint::kHdrNActive;
+  L->counts = L->header + sizeof(uint32_t) * flint::kHdrCounts;
   L->logits = o;   o = align_up(o + t * E * sizeof(float));
   L->topk_ids = o; o = align_up(o + t * k * sizeof(int32_t));
   L->topk_w = o;   o = align_up(o + t * k * sizeof(float));
-  L->n_active = o; o = align_up(o + sizeof(int32_t));
   L->active = o;   o = align_up(o + E * sizeof(int32_t));
-  L->counts = o;   o = align_up(o + E * sizeof(int32_t));
-  L->offsets = o;  o = align_up(o + (E + 1) * sizeof(int32_t));
-  L->slots = o;    o = align_up(o + t * k * sizeof(int32_t));
+  L->lists = o;    o = align_up(o + E * t * sizeof(int32_t));
   L->h = o;        o = align_up(o + (t * k + t) * I * sizeof(float));
+  L->y = o;        o = align_up(o + (t * k + t) * H * sizeof(float));
   L->extra = o;
   L->total_bytes = o;
 }
@@ -183,12 +187,10 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.ws.logits = reinterpret_cast<float*>(ws + L.logits);
   a.ws.ids = reinterpret_cast<int32_t*>(ws + L.topk_ids);
   a.ws.wts = reinterpret_cast<float*>(ws + L.topk_w);
-  a.ws.n_active = reinterpret_cast<int32_t*>(ws + L.n_active);
   a.ws.active = reinterpret_cast<int32_t*>(ws + L.active);
-  a.ws.counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  a.ws.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-  a.ws.slots = reinterpret_cast<int32_t*>(ws + L.slots);
+  a.ws.lists = reinterpret_cast<int32_t*>(ws + L.lists);
   a.ws.h = reinterpret_cast<float*>(ws + L.h);
+  a.ws.y = reinterpret_cast<float*>(ws + L.y);
   a.ws.extra = ws + L.extra;
   a.T = T;
   a.E = c.n_experts;
@@ -198,7 +200,15 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.nvfp4 = c.format == FLINT_W_NVFP4;
 
   (void)hipGetLastError();  // do not report an earlier, unrelated failure
-  const hipError_t err = flint::launch_decode_bf16(a, static_cast<hipStream_t>(stream), ev);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(ctx, FLINT_ERR_HIP, "hipGetDevice failed");
+  if (ctx->grid_device != dev) {
+    ctx->grid_limit = flint::decode_grid_limit();
+    ctx->grid_device = dev;
+  }
+  if (ctx->grid_limit <= 0) return fail(ctx, FLINT_ERR_HIP, "occupancy query failed");
+  const hipError_t err =
+      flint::launch_decode_bf16(a, ctx->grid_limit, static_cast<hipStream_t>(stream), ev);
   if (err != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(err));
   return FLINT_OK;
 }

@@ -26,7 +26,7 @@ FLINT_ERR_HIP = 4
 FLINT_W_BF16 = 0
 FLINT_W_NVFP4 = 1
 
-HEADER_BYTES = 1024
+HEADER_BYTES = 4096
 
 # Symbols the header declares; tests check the library exports each of them.
 ABI_SYMBOLS = (
@@ -61,8 +61,8 @@ class Weights(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("total_bytes", "header", "logits", "topk_ids", "topk_w", "n_active",
-                 "active", "counts", "offsets", "slots", "h", "extra")]
+                ("total_bytes", "header", "error_word", "logits", "topk_ids", "topk_w",
+                 "n_active", "active", "counts", "lists", "h", "y", "extra")]
 
 
 class FlintError(RuntimeError):

@@ -81,7 +81,7 @@ def test_decode_matches_oracle(dev, T, bias, x_seed):
 
 
 def test_intermediates_t8(dev):
-    """Logits, bucketing (bit-exact on the device's own ids) and h."""
+    """Logits, routing lists (as sets: the kernel appends with atomics), h and y."""
     T = 8
     say("intermediates T=8")
     xb = make_x(T, seed=SEED, x_seed=0)
@@ -90,13 +90,17 @@ def test_intermediates_t8(dev):
     logits = ws_region(r, "logits", T, np.float32, T * 256).reshape(T, 256)
     for t, rr in enumerate(res):
         np.testing.assert_allclose(logits[t], rr.logits, rtol=0, atol=2e-5)
+    # The counters are reset at the end of the forward; the lists and the
+    # union stay in place.  Rebuild the expected bucketing from the device ids.
     b = bucket(r["ids"], 256)
-    n_active = int(ws_region(r, "n_active", T, np.int32, 1)[0])
-    assert n_active == len(b["active"])
-    np.testing.assert_array_equal(ws_region(r, "active", T, np.int32, n_active), b["active"])
-    np.testing.assert_array_equal(ws_region(r, "counts", T, np.int32, 256), b["counts"])
-    np.testing.assert_array_equal(ws_region(r, "offsets", T, np.int32, 257), b["offsets"])
-    np.testing.assert_array_equal(ws_region(r, "slots", T, np.int32, T * 6), b["slots"])
+    nU = len(b["active"])
+    assert sorted(ws_region(r, "active", T, np.int32, nU).tolist()) == b["active"].tolist()
+    lists = ws_region(r, "lists", T, np.int32, 256 * T).reshape(256, T)
+    for e in b["active"]:
+        seg = b["slots"][b["offsets"][e]:b["offsets"][e + 1]]
+        assert sorted(lists[e][:len(seg)].tolist()) == seg.tolist()
+    hdr = ws_region(r, "header", T, np.uint32, 1024)
+    assert not hdr.any(), "header not reset"
     h = ws_region(r, "h", T, np.float32, (T * 6 + T) * 512).reshape(T * 7, 512)
     for t, rr in enumerate(res):
         scale = np.max(np.abs(rr.h_shared))
@@ -151,7 +155,7 @@ def test_workspace_reuse_across_T(dev):
         r = run(dev, xb, moe=moe, ws=ws)
         g = grade(r["out"], r["ids"], moe_forward(dev["L"], xb))
         assert g.ok, (T, str(g))
-        hdr = ws[:1024].cpu().numpy()
+        hdr = ws[:4096].cpu().numpy()
         assert not hdr.any()
 
 
