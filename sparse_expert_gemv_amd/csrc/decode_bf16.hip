@@ -407,7 +407,10 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(LayerArgs a, Plan 
       }
       __syncthreads();
       down_rows(w2, tile * kTileRows, cnt, s_hrow, a.ws.h, a.ws.y);
-      // The last of the |U| + 1 down items of this tile combines it.
+      // The last of the |U| + 1 down items of this tile combines it.  |U| is
+      // final only once routing is done (the shared expert's items do not
+      // otherwise wait for it).
+      block_wait(hdr + kHdrRoutingDone, 1u, err);
       const int n_active = bcast_load(hdr + kHdrNActive, &s_val);
       if (last_block_ticket(hdr + kHdrTileTicket + tile, (uint32_t)(n_active + 1), &s_flag))
         combine_tile(a, tile * kTileRows);
