@@ -52,6 +52,11 @@ extern "C" {
 
 typedef struct flint_moe_ctx flint_moe_ctx; /* opaque, host memory */
 
+/* Bytes at the start of every workspace that hold the kernels' completion
+ * counters.  They must be zero before a workspace is first used; every
+ * completed forward leaves them zero again (except the error word). */
+#define FLINT_MOE_WS_HEADER_BYTES 96512
+
 typedef enum flint_status {
   FLINT_OK = 0,
   FLINT_ERR_INVALID_ARG = 1, /* NULL / misaligned / out-of-range argument */
@@ -113,8 +118,8 @@ typedef struct flint_moe_weights {
  * in no particular order; the layer output does not depend on that order. */
 typedef struct flint_moe_ws_layout {
   size_t total_bytes;
-  size_t header;    /* uint32 [1024]: counters; zero before first use and after every
-                       completed forward, except word 4 (see error_word) */
+  size_t header;    /* FLINT_MOE_WS_HEADER_BYTES of uint32 counters; zero before first use
+                       and after every completed forward, except the error word */
   size_t error_word;/* uint32 inside the header: nonzero once a bounded wait of the
                        fused decode kernel timed out (results of that forward are
                        invalid); sticky until the caller clears it */
@@ -137,8 +142,9 @@ typedef struct flint_moe_ws_layout {
 flint_status flint_moe_init(const flint_moe_config* cfg, flint_moe_ctx** ctx_out);
 
 /* Bytes of workspace a forward of T tokens needs (0 for T <= 0 or NULL ctx).
- * The first 4096 bytes (the header) must be zero before the workspace is used
- * for the first time; every completed forward leaves them zero again. */
+ * Its first FLINT_MOE_WS_HEADER_BYTES (the header) must be zero before the
+ * workspace is used for the first time; every completed forward leaves them
+ * zero again. */
 size_t flint_moe_workspace_bytes(const flint_moe_ctx* ctx, int32_t T);
 
 /* Fill `layout` with the region offsets of a workspace for T tokens. */

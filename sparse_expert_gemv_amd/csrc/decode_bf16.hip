@@ -68,20 +68,31 @@ struct Plan {
 
 // ---------------------------------------------------------------- waiting
 
-// Thread 0 polls `*p >= target` with a bounded number of sleeps; the result
-// is broadcast to the block.  A timeout raises the sticky error word.
-__device__ __forceinline__ void block_wait(const uint32_t* p, uint32_t target, uint32_t* err) {
+// Thread 0 polls `*p >= target` with a bounded number of sleeps; the value
+// it saw is returned to every thread.  A timeout raises the sticky error word.
+__device__ __forceinline__ uint32_t block_wait(const uint32_t* p, uint32_t target, uint32_t* err,
+                                               int* s_val) {
   if (threadIdx.x == 0) {
-    uint32_t it = 0;
-    while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    uint32_t it = 0, v;
+    while ((v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target) {
       if (++it == kSpinLimit) {
         __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(4);
     }
+    *s_val = (int)v;
   }
   __syncthreads();
+  const uint32_t v = (uint32_t)*s_val;
+  __syncthreads();
+  return v;
+}
+
+// |U| once routing is done (each block polls one of the replicated flags).
+__device__ __forceinline__ int wait_routed(const uint32_t* hdr, uint32_t* err, int* s_val) {
+  const uint32_t* flag = hdr + kHdrRouted + (blockIdx.x % kRoutingReplicas) * kLine;
+  return (int)block_wait(flag, 1u, err, s_val) - 1;
 }
 
 // Every thread drains its stores, then thread 0 adds 1 to *counter.
@@ -90,14 +101,6 @@ __device__ __forceinline__ void block_signal(uint32_t* counter) {
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ int32_t bcast_load(const uint32_t* p, int* s_val) {
-  if (threadIdx.x == 0) *s_val = (int)__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int v = *s_val;
-  __syncthreads();
-  return v;
 }
 
 // ---------------------------------------------------------------- gate/up
@@ -263,12 +266,15 @@ __device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_
   }
   uint32_t* hdr = a.ws.header;
   // The last router item of token t sees every logit of t.
-  if (!last_block_ticket(hdr + kHdrTokTicket + t, P.rg, s_flag)) return;
+  if (!last_block_ticket(hdr + kHdrTokTicket + t * kLine, P.rg, s_flag)) return;
   if (wave == 0) route_token(a, t);
-  // The last token to finish sees every token's slots.
+  // The last token to finish sees every token's slots and publishes |U| + 1.
   if (!last_block_ticket(hdr + kHdrTokensDone, a.T, s_flag)) return;
-  if (threadIdx.x == 0)
-    __hip_atomic_store(hdr + kHdrRoutingDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x < kRoutingReplicas) {
+    const uint32_t n = __hip_atomic_load(hdr + kHdrNActive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(hdr + kHdrRouted + threadIdx.x * kLine, n + 1u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---------------------------------------------------------------- down
@@ -276,8 +282,14 @@ __device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_
 // Down item: rows [r0, r0 + 64) of one expert's w2 (wave w: 16 rows, one
 // 16-byte vector per row per lane), for each of the expert's slots:
 // y[hrow][row] = w2[row] . h[hrow], summed over the 64 lanes in a fixed tree.
+// Slots go in chunks of 16: their h rows are staged in LDS with coalesced
+// coherent loads, the results collect in LDS and leave as one batch of
+// stores, so no load waits behind this item's own write-through stores.
+constexpr int kDownChunk = 16;
+
 __device__ __forceinline__ void down_rows(const uint16_t* __restrict__ w2, int r0, int count,
-                                          const int16_t* hrows, const float* h, float* y) {
+                                          const int16_t* hrows, const float* h, float* y,
+                                          float* hs, float* ys) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rw = r0 + wave * kRowsPerWave;
@@ -285,33 +297,42 @@ __device__ __forceinline__ void down_rows(const uint16_t* __restrict__ w2, int r
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r)
     wv[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(rw + r) * I)[lane];
-  for (int j = 0; j < count; ++j) {
-    // Keep the weights packed across slots: widening all 16 rows to fp32
-    // once would cost 128 registers.
-#pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) asm volatile("" : "+v"(wv[r]));
-    const int hr = hrows[j];
-    const float* hp = h + (size_t)hr * I + lane * 8;
-    float hv[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) hv[q] = load_coherent(hp + q);
-    float acc[kRowsPerWave];
-#pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      float v = bf16_lo(wv[r].x) * hv[0];
-      v = fmaf(bf16_hi(wv[r].x), hv[1], v);
-      v = fmaf(bf16_lo(wv[r].y), hv[2], v);
-      v = fmaf(bf16_hi(wv[r].y), hv[3], v);
-      v = fmaf(bf16_lo(wv[r].z), hv[4], v);
-      v = fmaf(bf16_hi(wv[r].z), hv[5], v);
-      v = fmaf(bf16_lo(wv[r].w), hv[6], v);
-      v = fmaf(bf16_hi(wv[r].w), hv[7], v);
-      acc[r] = wave_sum_lane63(v);
+  for (int c0 = 0; c0 < count; c0 += kDownChunk) {
+    const int n = min(kDownChunk, count - c0);
+    __syncthreads();
+    for (int q = threadIdx.x; q < n * I; q += kThreads) {
+      const int j = q / I;
+      hs[q] = load_coherent(h + (size_t)hrows[c0 + j] * I + (q - j * I));
     }
-    if (lane == kWave - 1) {
-      float* yr = y + (size_t)hr * H + rw;
+    __syncthreads();
+    for (int j = 0; j < n; ++j) {
+      // Keep the weights packed across slots: widening all 16 rows to fp32
+      // once would cost 128 registers.
 #pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r) store_coherent(yr + r, acc[r]);
+      for (int r = 0; r < kRowsPerWave; ++r) asm volatile("" : "+v"(wv[r]));
+      const f32x4 h0 = *reinterpret_cast<const f32x4*>(hs + j * I + lane * 8);
+      const f32x4 h1 = *reinterpret_cast<const f32x4*>(hs + j * I + lane * 8 + 4);
+      float acc[kRowsPerWave];
+#pragma unroll
+      for (int r = 0; r < kRowsPerWave; ++r) {
+        float v = bf16_lo(wv[r].x) * h0.x;
+        v = fmaf(bf16_hi(wv[r].x), h0.y, v);
+        v = fmaf(bf16_lo(wv[r].y), h0.z, v);
+        v = fmaf(bf16_hi(wv[r].y), h0.w, v);
+        v = fmaf(bf16_lo(wv[r].z), h1.x, v);
+        v = fmaf(bf16_hi(wv[r].z), h1.y, v);
+        v = fmaf(bf16_lo(wv[r].w), h1.z, v);
+        v = fmaf(bf16_hi(wv[r].w), h1.w, v);
+        acc[r] = wave_sum_lane63(v);
+      }
+      if (lane == kWave - 1)
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r) ys[j * kTileRows + wave * kRowsPerWave + r] = acc[r];
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < n * kTileRows; q += kThreads) {
+      const int j = q / kTileRows;
+      store_coherent(y + (size_t)hrows[c0 + j] * H + r0 + (q - j * kTileRows), ys[q]);
     }
   }
 }
@@ -332,8 +353,10 @@ __device__ void combine_tile(const LayerArgs& a, int r0) {
 
 // ---------------------------------------------------------------- kernel
 
-__global__ __launch_bounds__(kThreads) void moe_decode_kernel(LayerArgs a, Plan P) {
-  __shared__ u32x4 xs[kXChunk * kVecH];                  // 32 KiB: x staging
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void moe_decode_kernel(LayerArgs a, Plan P) {
+  __shared__ u32x4 xs[kXChunk * kVecH];   // 32 KiB: x staging (gate/up) or h staging (down)
+  __shared__ float ys[kDownChunk * kTileRows];
   __shared__ int16_t s_tok[kDecodeMaxT], s_hrow[kDecodeMaxT];
   __shared__ int s_flag, s_val, s_cnt;
   uint32_t* hdr = a.ws.header;
@@ -358,8 +381,7 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(LayerArgs a, Plan 
       // Routed gate/up: active index ai, unit.
       const int ai = (item - P.g_routed) / kUnitsPerExpert;
       const int unit = (item - P.g_routed) - ai * kUnitsPerExpert;
-      block_wait(hdr + kHdrRoutingDone, 1u, err);
-      if (ai >= bcast_load(hdr + kHdrNActive, &s_val)) continue;
+      if (ai >= wait_routed(hdr, err, &s_val)) continue;
       if (threadIdx.x == 0) {
         const int e = load_coherent(a.ws.active + ai);
         s_val = e;
@@ -375,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(LayerArgs a, Plan 
       __syncthreads();
       const uint16_t* w13 = reinterpret_cast<const uint16_t*>(a.routed.w13) + (size_t)e * 2 * I * H;
       gateup_item(w13, unit * kPairsPerItem, cnt, TokenList{s_tok, s_hrow}, a.x, a.ws.h, xs);
-      block_signal(hdr + kHdrExpertDone + ai);
+      block_signal(hdr + kHdrExpertDone + ai * kLine);
     } else {
       // Down: (expert, 64-row tile); the shared expert's tiles come first.
       const int di = item - P.d_shared;
@@ -384,15 +406,14 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(LayerArgs a, Plan 
       const uint16_t* w2;
       int cnt;
       if (ei == 0) {
-        block_wait(hdr + kHdrSharedDone, (uint32_t)kUnitsPerExpert, err);
+        block_wait(hdr + kHdrSharedDone, (uint32_t)kUnitsPerExpert, err, &s_val);
         for (int q = threadIdx.x; q < T; q += kThreads) s_hrow[q] = (int16_t)(T * k + q);
         w2 = reinterpret_cast<const uint16_t*>(a.shared.w2);
         cnt = T;
       } else {
         const int ai = ei - 1;
-        block_wait(hdr + kHdrRoutingDone, 1u, err);
-        if (ai >= bcast_load(hdr + kHdrNActive, &s_val)) continue;
-        block_wait(hdr + kHdrExpertDone + ai, (uint32_t)kUnitsPerExpert, err);
+        if (ai >= wait_routed(hdr, err, &s_val)) continue;
+        block_wait(hdr + kHdrExpertDone + ai * kLine, (uint32_t)kUnitsPerExpert, err, &s_val);
         if (threadIdx.x == 0) {
           const int e = load_coherent(a.ws.active + ai);
           s_val = e;
@@ -406,13 +427,12 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(LayerArgs a, Plan 
         w2 = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)e * H * I;
       }
       __syncthreads();
-      down_rows(w2, tile * kTileRows, cnt, s_hrow, a.ws.h, a.ws.y);
+      down_rows(w2, tile * kTileRows, cnt, s_hrow, a.ws.h, a.ws.y, reinterpret_cast<float*>(xs), ys);
       // The last of the |U| + 1 down items of this tile combines it.  |U| is
       // final only once routing is done (the shared expert's items do not
       // otherwise wait for it).
-      block_wait(hdr + kHdrRoutingDone, 1u, err);
-      const int n_active = bcast_load(hdr + kHdrNActive, &s_val);
-      if (last_block_ticket(hdr + kHdrTileTicket + tile, (uint32_t)(n_active + 1), &s_flag))
+      const int n_active = wait_routed(hdr, err, &s_val);
+      if (last_block_ticket(hdr + kHdrTileTicket + tile * kLine, (uint32_t)(n_active + 1), &s_flag))
         combine_tile(a, tile * kTileRows);
     }
   }
@@ -423,11 +443,12 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(LayerArgs a, Plan 
   for (int i = threadIdx.x; i < n_active; i += kThreads) {
     const int e = load_coherent(a.ws.active + i);
     __hip_atomic_store(hdr + kHdrCounts + e, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(hdr + kHdrExpertDone + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(hdr + kHdrExpertDone + i * kLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
+  if (threadIdx.x < kRoutingReplicas)
+    __hip_atomic_store(hdr + kHdrRouted + threadIdx.x * kLine, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   if (threadIdx.x == 0) {
-    __hip_atomic_store(hdr + kHdrRoutingDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(hdr + kHdrNActive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(hdr + kHdrSharedDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -12,19 +12,23 @@ constexpr int kInter = 512;        // I
 constexpr int kMaxExperts = 256;   // E upper bound (four router scores per lane)
 constexpr int kMaxTopK = 8;
 constexpr int kDecodeMaxT = 64;    // largest T taken by the GEMV (decode) kernels
-constexpr int kHeaderWords = 1024;  // workspace header: uint32 counters (4 KiB)
-
-// Header words.  All are zero before a forward starts and zero after it ends.
-constexpr int kHdrTokensDone = 0;   // tokens whose selection is complete
-constexpr int kHdrRoutingDone = 1;  // 1 once every token is routed
-constexpr int kHdrNActive = 2;      // |U|
-constexpr int kHdrExit = 3;         // blocks that finished all their items
-constexpr int kHdrError = 4;        // sticky: a bounded wait timed out
-constexpr int kHdrSharedDone = 5;   // shared-expert gate/up items done
-constexpr int kHdrTokTicket = 64;   // [64]  router items done per token
-constexpr int kHdrCounts = 128;     // [256] slots routed to each expert
-constexpr int kHdrExpertDone = 384; // [256] gate/up items done per active index
-constexpr int kHdrTileTicket = 640; // [32]  down items done per 64-row output tile
+// Workspace header: uint32 counters, each hot one on its own 256-byte line
+// so that pollers of one word never queue behind atomics on another.  All
+// are zero before a forward starts and zero after it ends (except the
+// sticky error word).
+constexpr int kLine = 64;                       // words per 256-byte line
+constexpr int kRoutingReplicas = 16;
+constexpr int kHdrTokensDone = 0 * kLine;       // tokens whose selection is complete
+constexpr int kHdrExit = 1 * kLine;             // blocks that finished all their items
+constexpr int kHdrSharedDone = 2 * kLine;       // shared-expert gate/up items done
+constexpr int kHdrError = 3 * kLine;            // sticky: a bounded wait timed out
+constexpr int kHdrNActive = 4 * kLine;          // |U| (append counter)
+constexpr int kHdrRouted = 5 * kLine;           // [16 lines] |U| + 1 once routing is done
+constexpr int kHdrTokTicket = 21 * kLine;       // [64 lines] router items done per token
+constexpr int kHdrTileTicket = 85 * kLine;      // [32 lines] down items done per output tile
+constexpr int kHdrExpertDone = 117 * kLine;     // [256 lines] gate/up items done per active index
+constexpr int kHdrCounts = 373 * kLine;         // [256 words] slots routed to each expert
+constexpr int kHeaderWords = 377 * kLine;       // 94.25 KiB
 
 // Workspace regions, as device pointers.
 struct Workspace {
@@ -71,7 +75,7 @@ struct StageEvents {
   int n = 0;
   int used = 0;
   void mark(hipStream_t s) {
-    if (events && used < n) hipEventRecord(events[used++], s);
+    if (events && used < n) (void)hipEventRecord(events[used++], s);
   }
 };
 

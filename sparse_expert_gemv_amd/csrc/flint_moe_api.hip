@@ -26,6 +26,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kHeaderBytes = flint::kHeaderWords * sizeof(uint32_t);
+static_assert(kHeaderBytes == FLINT_MOE_WS_HEADER_BYTES, "header size in flint_moe.h");
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 

@@ -26,7 +26,7 @@ FLINT_ERR_HIP = 4
 FLINT_W_BF16 = 0
 FLINT_W_NVFP4 = 1
 
-HEADER_BYTES = 4096
+HEADER_BYTES = 96512  # FLINT_MOE_WS_HEADER_BYTES
 
 # Symbols the header declares; tests check the library exports each of them.
 ABI_SYMBOLS = (
