@@ -55,7 +55,7 @@ typedef struct flint_moe_ctx flint_moe_ctx; /* opaque, host memory */
 /* Bytes at the start of every workspace that hold the kernels' completion
  * counters.  They must be zero before a workspace is first used; every
  * completed forward leaves them zero again (except the error word). */
-#define FLINT_MOE_WS_HEADER_BYTES 96512
+#define FLINT_MOE_WS_HEADER_BYTES 95232
 
 typedef enum flint_status {
   FLINT_OK = 0,
@@ -113,27 +113,28 @@ typedef struct flint_moe_weights {
 
 /* Byte offsets of the regions of a workspace sized for T tokens.  Exposed so
  * that tests can read the intermediate results of one forward (a region is
- * valid once the forward that wrote it has completed).  Lists that the
- * kernels build with atomics (the union U and the per-expert slot lists) are
- * in no particular order; the layer output does not depend on that order. */
+ * valid once the forward that wrote it has completed). */
 typedef struct flint_moe_ws_layout {
   size_t total_bytes;
-  size_t header;    /* FLINT_MOE_WS_HEADER_BYTES of uint32 counters; zero before first use
-                       and after every completed forward, except the error word */
-  size_t error_word;/* uint32 inside the header: nonzero once a bounded wait of the
-                       fused decode kernel timed out (results of that forward are
-                       invalid); sticky until the caller clears it */
-  size_t logits;    /* fp32 [T][E]: z (router GEMV + bias) */
-  size_t topk_ids;  /* int32 [T][k]: selected experts in rank order */
-  size_t topk_w;    /* fp32 [T][k]: routing weights */
-  size_t n_active;  /* int32 inside the header: |U| while a forward runs (reset to 0 at its end) */
-  size_t active;    /* int32 [E]: U, first |U| entries */
-  size_t counts;    /* int32 [E] inside the header: slots per expert while a forward runs */
-  size_t lists;     /* int32 [E][T]: slot ids s = t*k + j routed to expert e */
-  size_t h;         /* fp32 [T*k + T][I]: h of slot s in row s; h of the shared expert
-                       for token t in row T*k + t */
-  size_t y;         /* fp32 [T*k + T][H]: unweighted down projection of each h row */
-  size_t extra;     /* path-private scratch (prefill-sized T only) */
+  size_t header;     /* FLINT_MOE_WS_HEADER_BYTES of uint32 counters; zero before first use
+                        and after every completed forward, except the error word */
+  size_t error_word; /* uint32 inside the header: nonzero once a bounded wait timed out
+                        (results of that forward are invalid); sticky until the caller
+                        clears it */
+  size_t logits;     /* fp32 [T][E]: z (router GEMV + bias) */
+  size_t topk_ids;   /* int32 [T][k]: selected experts in rank order */
+  size_t topk_w;     /* fp32 [T][k]: routing weights */
+  size_t route;      /* int32 routing table (the token -> expert bucketing):
+                          [0]                    |U|, the number of distinct selected experts
+                          [1, 1+E)               U, ascending (first |U| entries valid)
+                          [1+E, 2+2E)            off: slots of U[a] are slots[off[a], off[a+1]),
+                                                 off[|U|] = T*k
+                          [2+2E, 2+2E+T*k)       slots s = t*k + j grouped by U, ascending
+                                                 within a group */
+  size_t h;          /* fp32 [T*k + T][I]: h of slot s in row s; h of the shared expert
+                        for token t in row T*k + t */
+  size_t y;          /* fp32 [T*k + T][H]: unweighted down projection of each h row */
+  size_t extra;      /* path-private scratch (prefill-sized T only) */
 } flint_moe_ws_layout;
 
 /* Validate `cfg` and create a context.  Touches no GPU state.

@@ -13,14 +13,17 @@
 // down rows of early experts stream while later experts finish gate/up.
 // Hand-offs between blocks use completion counters in the workspace header
 // and coherent (write-through) stores/loads, never whole-cache flushes:
-//   - the last router item of token t picks its top-k and appends its slots
-//     to the per-expert lists (the first slot of an expert also appends the
-//     expert to the union U); the last token to finish raises routing-done;
-//   - gate/up item (a, .) waits for routing-done; 64 finished items of a
-//     complete expert a's h;
-//   - down item (a, tile) waits for expert a's h and writes y for its rows;
-//     the last of the |U| + 1 down items of a tile combines the tile:
-//     out = y_shared + sum_j w_j y_j in a fixed order, rounded once to bf16;
+//   - the last router item of token t picks its top-k; the last token to
+//     finish buckets every (token, rank) slot by expert into the routing
+//     table (U ascending, slots grouped by expert in ascending slot order)
+//     and raises the routed flag;
+//   - each block reads the routing table once into LDS;
+//   - gate/up item (a, .) needs the table; 64 finished items of active
+//     expert a complete its h;
+//   - down item (a, tile) issues its weight loads, then waits for expert a's
+//     h and writes y for its rows; the last of the |U| + 1 down items of a
+//     tile combines it: out = y_shared + sum_j w_j y_j in a fixed order,
+//     rounded once to bf16;
 //   - the last block to run out of items resets every counter to zero.
 // Every wait is bounded; a timeout sets an error word instead of hanging.
 //
@@ -53,6 +56,7 @@ constexpr uint32_t kSpinLimit = 1u << 18;  // ~0.3 s of polling
 static_assert(H % (8 * kWave) == 0, "H must be a multiple of 512");
 static_assert(I == 8 * kWave, "down GEMV maps one 16-byte vector of a w2 row per lane");
 static_assert(kTiles <= 32, "tile tickets");
+static_assert(kDecodeMaxT * kMaxTopK <= 32767 && kMaxExperts <= 32767, "int16 routing table");
 
 struct Plan {
   int G;            // blocks in the grid
@@ -105,10 +109,15 @@ __device__ __forceinline__ void block_signal(uint32_t* counter) {
 
 // ---------------------------------------------------------------- gate/up
 
-// Token list of one gate/up item, staged in LDS: x row and h row per entry.
+// Tokens of one gate/up or down item.  Routed: entry j is slot
+// s = slots[j] (token s / k, h row s).  Shared: entry j is token j, h row
+// base + j.
 struct TokenList {
-  const int16_t* tok;  // LDS
-  const int16_t* hrow; // LDS
+  const int16_t* slots;  // LDS, or nullptr for the shared expert
+  int k;
+  int base;
+  __device__ __forceinline__ int tok(int j) const { return slots ? slots[j] / k : j; }
+  __device__ __forceinline__ int hrow(int j) const { return slots ? slots[j] : base + j; }
 };
 
 // One block (4 waves) computes h = silu(gate) * up for the row pairs
@@ -138,7 +147,7 @@ __device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ w13, in
     for (int q = threadIdx.x; q < n * kVecH; q += kThreads) {
       const int j = q / kVecH;
       const int col = q - j * kVecH;
-      xs[q] = reinterpret_cast<const u32x4*>(x + (size_t)list.tok[c0 + j] * H)[col];
+      xs[q] = reinterpret_cast<const u32x4*>(x + (size_t)list.tok(c0 + j) * H)[col];
     }
     __syncthreads();
     for (int j = 0; j < n; ++j) {
@@ -152,7 +161,7 @@ __device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ w13, in
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = wave_sum_lane63(acc[r]);
       if (lane == kWave - 1) {
-        float* hr = h + (size_t)list.hrow[c0 + j] * I + p;
+        float* hr = h + (size_t)list.hrow(c0 + j) * I + p;
         store_coherent(hr, silu(acc[0]) * acc[2]);
         store_coherent(hr + 1, silu(acc[1]) * acc[3]);
       }
@@ -171,12 +180,11 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Top-k of token t by score, one wave, then the token's slots are appended
-// to the per-expert lists.  Ranks on the logit (the sigmoid is strictly
-// increasing), ties to the lower expert index: key = (logit, ~e).
+// Top-k of token t by score, one wave.  Ranks on the logit (the sigmoid is
+// strictly increasing), ties to the lower expert index: key = (logit, ~e).
 __device__ void route_token(const LayerArgs& a, int t) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int E = a.E, k = a.k, T = a.T;
+  const int E = a.E, k = a.k;
   uint64_t key[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -210,7 +218,6 @@ __device__ void route_token(const LayerArgs& a, int t) {
     s[j] = sigmoid(zsel[j]);
     if (j < k) sum += s[j];
   }
-  uint32_t* hdr = a.ws.header;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j < k && lane == j) {
@@ -220,19 +227,75 @@ __device__ void route_token(const LayerArgs& a, int t) {
       store_coherent(a.ws.wts + t * k + j, w);
       if (a.ids_out) a.ids_out[t * k + j] = e;
       if (a.wts_out) a.wts_out[t * k + j] = w;
-      const uint32_t c = __hip_atomic_fetch_add(hdr + kHdrCounts + e, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-      store_coherent(a.ws.lists + (size_t)e * T + c, t * k + j);
-      if (c == 0) {
-        const uint32_t pos = __hip_atomic_fetch_add(hdr + kHdrNActive, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        store_coherent(a.ws.active + pos, e);
-      }
     }
   }
 }
 
-__device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_flag) {
+// Bucket every (token, rank) slot by expert into the routing table, one
+// block of 256 threads.  U is ascending; the slots of one expert are in
+// ascending slot order: the rank of slot s among its expert's slots is the
+// number of set bits below s in that expert's occupancy mask.
+__device__ void build_route_table(const LayerArgs& a, void* smem) {
+  constexpr int kMaskWords = kDecodeMaxT * kMaxTopK / 32;  // 16
+  int* cnt = reinterpret_cast<int*>(smem);                   // [256]
+  int* aoff = cnt + kMaxExperts;                             // [256] offset of expert e
+  uint32_t* occ = reinterpret_cast<uint32_t*>(aoff + kMaxExperts);  // [256][16]
+  const int E = a.E;
+  const int nslots = a.T * a.k;
+  const int tid = threadIdx.x;
+  int32_t* route = a.ws.route;
+  int32_t* r_active = route + 1;
+  int32_t* r_off = route + 1 + E;
+  int32_t* r_slots = route + 2 + 2 * E;
+  for (int i = tid; i < kMaxExperts; i += kThreads) cnt[i] = 0;
+  for (int i = tid; i < kMaxExperts * kMaskWords; i += kThreads) occ[i] = 0;
+  __syncthreads();
+  for (int s = tid; s < nslots; s += kThreads) {
+    const int e = load_coherent(a.ws.ids + s);
+    atomicAdd(&cnt[e], 1);
+    atomicOr(&occ[e * kMaskWords + (s >> 5)], 1u << (s & 31));
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int lane = tid;
+    int c[4], sc = 0, sf = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      c[q] = e < E ? cnt[e] : 0;
+      sc += c[q];
+      sf += c[q] > 0;
+    }
+    const int ic = wave_incl_scan(sc);
+    const int iff = wave_incl_scan(sf);
+    int o = ic - sc, act = iff - sf;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      aoff[e] = o;
+      if (c[q] > 0) {
+        store_coherent(r_active + act, e);
+        store_coherent(r_off + act, o);
+        ++act;
+      }
+      o += c[q];
+    }
+    if (lane == kWave - 1) {
+      store_coherent(route, iff);
+      store_coherent(r_off + iff, ic);
+    }
+  }
+  __syncthreads();
+  for (int s = tid; s < nslots; s += kThreads) {
+    const int e = load_coherent(a.ws.ids + s);
+    const uint32_t* m = occ + e * kMaskWords;
+    int rank = __popc(m[s >> 5] & ((1u << (s & 31)) - 1u));
+    for (int w = 0; w < (s >> 5); ++w) rank += __popc(m[w]);
+    store_coherent(r_slots + aoff[e] + rank, s);
+  }
+}
+
+__device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_flag, void* smem) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int t = item / P.rg;
@@ -268,10 +331,14 @@ __device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_
   // The last router item of token t sees every logit of t.
   if (!last_block_ticket(hdr + kHdrTokTicket + t * kLine, P.rg, s_flag)) return;
   if (wave == 0) route_token(a, t);
-  // The last token to finish sees every token's slots and publishes |U| + 1.
+  // The last token to finish sees every token's selection: it builds the
+  // routing table, then publishes |U| + 1.
   if (!last_block_ticket(hdr + kHdrTokensDone, a.T, s_flag)) return;
+  build_route_table(a, smem);
+  drain_memory_ops();
+  __syncthreads();
   if (threadIdx.x < kRoutingReplicas) {
-    const uint32_t n = __hip_atomic_load(hdr + kHdrNActive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t n = (uint32_t)load_coherent(a.ws.route);
     __hip_atomic_store(hdr + kHdrRouted + threadIdx.x * kLine, n + 1u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -287,22 +354,27 @@ __device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_
 // stores, so no load waits behind this item's own write-through stores.
 constexpr int kDownChunk = 16;
 
-__device__ __forceinline__ void down_rows(const uint16_t* __restrict__ w2, int r0, int count,
-                                          const int16_t* hrows, const float* h, float* y,
-                                          float* hs, float* ys) {
+__device__ __forceinline__ void load_down_weights(u32x4 (&wv)[kRowsPerWave],
+                                                  const uint16_t* __restrict__ w2, int r0) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rw = r0 + wave * kRowsPerWave;
-  u32x4 wv[kRowsPerWave];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r)
     wv[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(rw + r) * I)[lane];
+}
+
+__device__ __forceinline__ void down_rows(u32x4 (&wv)[kRowsPerWave], int r0, int count,
+                                          const TokenList& list, const float* h, float* y,
+                                          float* hs, float* ys) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
   for (int c0 = 0; c0 < count; c0 += kDownChunk) {
     const int n = min(kDownChunk, count - c0);
     __syncthreads();
     for (int q = threadIdx.x; q < n * I; q += kThreads) {
       const int j = q / I;
-      hs[q] = load_coherent(h + (size_t)hrows[c0 + j] * I + (q - j * I));
+      hs[q] = load_coherent(h + (size_t)list.hrow(c0 + j) * I + (q - j * I));
     }
     __syncthreads();
     for (int j = 0; j < n; ++j) {
@@ -332,7 +404,7 @@ __device__ __forceinline__ void down_rows(const uint16_t* __restrict__ w2, int r
     __syncthreads();
     for (int q = threadIdx.x; q < n * kTileRows; q += kThreads) {
       const int j = q / kTileRows;
-      store_coherent(y + (size_t)hrows[c0 + j] * H + r0 + (q - j * kTileRows), ys[q]);
+      store_coherent(y + (size_t)list.hrow(c0 + j) * H + r0 + (q - j * kTileRows), ys[q]);
     }
   }
 }
@@ -353,105 +425,99 @@ __device__ void combine_tile(const LayerArgs& a, int r0) {
 
 // ---------------------------------------------------------------- kernel
 
+// The routing table, copied once per block into LDS.
+struct RouteLds {
+  int n;                              // |U|, or -1 before the block has read it
+  int16_t active[kMaxExperts];
+  int16_t off[kMaxExperts + 1];
+  int16_t slots[kDecodeMaxT * kMaxTopK];
+};
+
+__device__ __forceinline__ void ensure_routes(const LayerArgs& a, RouteLds& rt, uint32_t* err,
+                                              int* s_val) {
+  if (rt.n >= 0) return;  // block-uniform
+  const int n = wait_routed(a.ws.header, err, s_val);
+  const int E = a.E, ns = a.T * a.k;
+  const int32_t* route = a.ws.route;
+  for (int q = threadIdx.x; q < n; q += kThreads) rt.active[q] = (int16_t)load_coherent(route + 1 + q);
+  for (int q = threadIdx.x; q <= n; q += kThreads) rt.off[q] = (int16_t)load_coherent(route + 1 + E + q);
+  for (int q = threadIdx.x; q < ns; q += kThreads) rt.slots[q] = (int16_t)load_coherent(route + 2 + 2 * E + q);
+  if (threadIdx.x == 0) rt.n = n;
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void moe_decode_kernel(LayerArgs a, Plan P) {
-  __shared__ u32x4 xs[kXChunk * kVecH];   // 32 KiB: x staging (gate/up) or h staging (down)
+  __shared__ u32x4 xs[kXChunk * kVecH];   // 32 KiB: x staging (gate/up), h staging (down),
+                                          // bucketing tables (routing)
   __shared__ float ys[kDownChunk * kTileRows];
-  __shared__ int16_t s_tok[kDecodeMaxT], s_hrow[kDecodeMaxT];
-  __shared__ int s_flag, s_val, s_cnt;
+  __shared__ RouteLds rt;
+  __shared__ int s_flag, s_val;
   uint32_t* hdr = a.ws.header;
   uint32_t* err = hdr + kHdrError;
   const int T = a.T, k = a.k;
+  if (threadIdx.x == 0) rt.n = -1;
+  __syncthreads();
 
   for (int item = blockIdx.x; item < P.n_items; item += P.G) {
     if (item < P.n_router) {
-      router_item(a, P, item, &s_flag);
+      router_item(a, P, item, &s_flag, xs);
     } else if (item < P.g_routed) {
       // Shared expert gate/up: all T tokens, h rows T*k + t.
       const int unit = item - P.g_shared;
-      for (int q = threadIdx.x; q < T; q += kThreads) {
-        s_tok[q] = (int16_t)q;
-        s_hrow[q] = (int16_t)(T * k + q);
-      }
-      __syncthreads();
       gateup_item(reinterpret_cast<const uint16_t*>(a.shared.w13), unit * kPairsPerItem, T,
-                  TokenList{s_tok, s_hrow}, a.x, a.ws.h, xs);
+                  TokenList{nullptr, k, T * k}, a.x, a.ws.h, xs);
       block_signal(hdr + kHdrSharedDone);
     } else if (item < P.d_shared) {
       // Routed gate/up: active index ai, unit.
       const int ai = (item - P.g_routed) / kUnitsPerExpert;
       const int unit = (item - P.g_routed) - ai * kUnitsPerExpert;
-      if (ai >= wait_routed(hdr, err, &s_val)) continue;
-      if (threadIdx.x == 0) {
-        const int e = load_coherent(a.ws.active + ai);
-        s_val = e;
-        s_cnt = (int)__hip_atomic_load(hdr + kHdrCounts + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();
-      const int e = s_val, cnt = s_cnt;
-      for (int q = threadIdx.x; q < cnt; q += kThreads) {
-        const int slot = load_coherent(a.ws.lists + (size_t)e * T + q);
-        s_tok[q] = (int16_t)(slot / k);
-        s_hrow[q] = (int16_t)slot;
-      }
-      __syncthreads();
+      ensure_routes(a, rt, err, &s_val);
+      if (ai >= rt.n) continue;
+      const int e = rt.active[ai];
       const uint16_t* w13 = reinterpret_cast<const uint16_t*>(a.routed.w13) + (size_t)e * 2 * I * H;
-      gateup_item(w13, unit * kPairsPerItem, cnt, TokenList{s_tok, s_hrow}, a.x, a.ws.h, xs);
+      gateup_item(w13, unit * kPairsPerItem, rt.off[ai + 1] - rt.off[ai],
+                  TokenList{rt.slots + rt.off[ai], k, 0}, a.x, a.ws.h, xs);
       block_signal(hdr + kHdrExpertDone + ai * kLine);
     } else {
       // Down: (expert, 64-row tile); the shared expert's tiles come first.
       const int di = item - P.d_shared;
       const int ei = di / kTiles;          // 0: shared, 1 + ai: active index ai
       const int tile = di - ei * kTiles;
-      const uint16_t* w2;
-      int cnt;
+      ensure_routes(a, rt, err, &s_val);
+      const int ai = ei - 1;
+      if (ai >= rt.n) continue;
+      u32x4 wv[kRowsPerWave];
+      TokenList list{nullptr, k, T * k};
+      int cnt = T;
       if (ei == 0) {
+        load_down_weights(wv, reinterpret_cast<const uint16_t*>(a.shared.w2), tile * kTileRows);
         block_wait(hdr + kHdrSharedDone, (uint32_t)kUnitsPerExpert, err, &s_val);
-        for (int q = threadIdx.x; q < T; q += kThreads) s_hrow[q] = (int16_t)(T * k + q);
-        w2 = reinterpret_cast<const uint16_t*>(a.shared.w2);
-        cnt = T;
       } else {
-        const int ai = ei - 1;
-        if (ai >= wait_routed(hdr, err, &s_val)) continue;
+        const int e = rt.active[ai];
+        load_down_weights(wv, reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)e * H * I,
+                          tile * kTileRows);
+        list.slots = rt.slots + rt.off[ai];
+        cnt = rt.off[ai + 1] - rt.off[ai];
         block_wait(hdr + kHdrExpertDone + ai * kLine, (uint32_t)kUnitsPerExpert, err, &s_val);
-        if (threadIdx.x == 0) {
-          const int e = load_coherent(a.ws.active + ai);
-          s_val = e;
-          s_cnt = (int)__hip_atomic_load(hdr + kHdrCounts + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        const int e = s_val;
-        cnt = s_cnt;
-        for (int q = threadIdx.x; q < cnt; q += kThreads)
-          s_hrow[q] = (int16_t)load_coherent(a.ws.lists + (size_t)e * T + q);
-        w2 = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)e * H * I;
       }
-      __syncthreads();
-      down_rows(w2, tile * kTileRows, cnt, s_hrow, a.ws.h, a.ws.y, reinterpret_cast<float*>(xs), ys);
-      // The last of the |U| + 1 down items of this tile combines it.  |U| is
-      // final only once routing is done (the shared expert's items do not
-      // otherwise wait for it).
-      const int n_active = wait_routed(hdr, err, &s_val);
-      if (last_block_ticket(hdr + kHdrTileTicket + tile * kLine, (uint32_t)(n_active + 1), &s_flag))
+      down_rows(wv, tile * kTileRows, cnt, list, a.ws.h, a.ws.y, reinterpret_cast<float*>(xs), ys);
+      // The last of the |U| + 1 down items of this tile combines it.
+      if (last_block_ticket(hdr + kHdrTileTicket + tile * kLine, (uint32_t)(rt.n + 1), &s_flag))
         combine_tile(a, tile * kTileRows);
     }
   }
 
   // The last block to finish resets the per-forward counters.
   if (!last_block_ticket(hdr + kHdrExit, (uint32_t)P.G, &s_flag)) return;
-  const int n_active = (int)__hip_atomic_load(hdr + kHdrNActive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int i = threadIdx.x; i < n_active; i += kThreads) {
-    const int e = load_coherent(a.ws.active + i);
-    __hip_atomic_store(hdr + kHdrCounts + e, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int n_active = load_coherent(a.ws.route);
+  for (int i = threadIdx.x; i < n_active; i += kThreads)
     __hip_atomic_store(hdr + kHdrExpertDone + i * kLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
   if (threadIdx.x < kRoutingReplicas)
     __hip_atomic_store(hdr + kHdrRouted + threadIdx.x * kLine, 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x == 0) {
-    __hip_atomic_store(hdr + kHdrNActive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)
     __hip_atomic_store(hdr + kHdrSharedDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 }  // namespace

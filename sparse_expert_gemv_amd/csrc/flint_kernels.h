@@ -22,13 +22,21 @@ constexpr int kHdrTokensDone = 0 * kLine;       // tokens whose selection is com
 constexpr int kHdrExit = 1 * kLine;             // blocks that finished all their items
 constexpr int kHdrSharedDone = 2 * kLine;       // shared-expert gate/up items done
 constexpr int kHdrError = 3 * kLine;            // sticky: a bounded wait timed out
-constexpr int kHdrNActive = 4 * kLine;          // |U| (append counter)
-constexpr int kHdrRouted = 5 * kLine;           // [16 lines] |U| + 1 once routing is done
-constexpr int kHdrTokTicket = 21 * kLine;       // [64 lines] router items done per token
-constexpr int kHdrTileTicket = 85 * kLine;      // [32 lines] down items done per output tile
-constexpr int kHdrExpertDone = 117 * kLine;     // [256 lines] gate/up items done per active index
-constexpr int kHdrCounts = 373 * kLine;         // [256 words] slots routed to each expert
-constexpr int kHeaderWords = 377 * kLine;       // 94.25 KiB
+constexpr int kHdrRouted = 4 * kLine;           // [16 lines] |U| + 1 once routing is done
+constexpr int kHdrTokTicket = 20 * kLine;       // [64 lines] router items done per token
+constexpr int kHdrTileTicket = 84 * kLine;      // [32 lines] down items done per output tile
+constexpr int kHdrExpertDone = 116 * kLine;     // [256 lines] gate/up items done per active index
+constexpr int kHeaderWords = 372 * kLine;       // 93 KiB
+
+// Routing table (int32), written once per forward by the block that
+// finishes routing:
+//   [0]                      |U|
+//   [1, 1 + E)               U, ascending expert ids (first |U| valid)
+//   [1 + E, 2 + 2E)          offsets by active index: slots of U[a] are
+//                            slots[off[a], off[a + 1]), off[|U|] = T*k
+//   [2 + 2E, 2 + 2E + T*k)   slot ids s = t*k + j, grouped by active index,
+//                            ascending within a group
+__host__ __device__ constexpr int route_table_ints(int E, int T, int k) { return 2 + 2 * E + T * k; }
 
 // Workspace regions, as device pointers.
 struct Workspace {
@@ -36,8 +44,7 @@ struct Workspace {
   float* logits;      // [T][E]
   int32_t* ids;       // [T][k]
   float* wts;         // [T][k]
-  int32_t* active;    // [E]: the union U, first n_active entries, in completion order
-  int32_t* lists;     // [E][T]: slot ids routed to expert e, first counts[e] entries
+  int32_t* route;     // routing table (see above)
   float* h;           // [T*k + T][I]
   float* y;           // [T*k + T][H]: per-slot down projections (unweighted)
   void* extra;

@@ -37,13 +37,10 @@ void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L
   std::memset(L, 0, sizeof(*L));
   L->header = o;   o = align_up(o + kHeaderBytes);
   L->error_word = L->header + sizeof(uint32_t) * flint::kHdrError;
-  L->n_active = L->header + sizeof(uint32_t) * flint::kHdrNActive;
-  L->counts = L->header + sizeof(uint32_t) * flint::kHdrCounts;
   L->logits = o;   o = align_up(o + t * E * sizeof(float));
   L->topk_ids = o; o = align_up(o + t * k * sizeof(int32_t));
   L->topk_w = o;   o = align_up(o + t * k * sizeof(float));
-  L->active = o;   o = align_up(o + E * sizeof(int32_t));
-  L->lists = o;    o = align_up(o + E * t * sizeof(int32_t));
+  L->route = o;    o = align_up(o + (size_t)flint::route_table_ints((int)E, T, (int)k) * sizeof(int32_t));
   L->h = o;        o = align_up(o + (t * k + t) * I * sizeof(float));
   L->y = o;        o = align_up(o + (t * k + t) * H * sizeof(float));
   L->extra = o;
@@ -188,8 +185,7 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.ws.logits = reinterpret_cast<float*>(ws + L.logits);
   a.ws.ids = reinterpret_cast<int32_t*>(ws + L.topk_ids);
   a.ws.wts = reinterpret_cast<float*>(ws + L.topk_w);
-  a.ws.active = reinterpret_cast<int32_t*>(ws + L.active);
-  a.ws.lists = reinterpret_cast<int32_t*>(ws + L.lists);
+  a.ws.route = reinterpret_cast<int32_t*>(ws + L.route);
   a.ws.h = reinterpret_cast<float*>(ws + L.h);
   a.ws.y = reinterpret_cast<float*>(ws + L.y);
   a.ws.extra = ws + L.extra;

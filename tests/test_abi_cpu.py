@@ -65,11 +65,11 @@ def test_workspace_sizes_grow_with_T():
     sizes = [m.workspace_bytes(T) for T in (1, 2, 8, 64)]
     assert sizes == sorted(sizes) and sizes[0] > sg.flint_moe.HEADER_BYTES
     lay = m.workspace_layout(8)
-    offs = [lay[k] for k in ("header", "logits", "topk_ids", "topk_w", "active", "lists", "h",
-                             "y", "extra")]
+    offs = [lay[k] for k in ("header", "logits", "topk_ids", "topk_w", "route", "h", "y",
+                             "extra")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert lay["header"] <= lay["n_active"] < lay["counts"] < lay["logits"]
-    assert lay["error_word"] < lay["logits"]
+    assert lay["header"] < lay["error_word"] < lay["logits"]
+    assert lay["route"] + (2 + 2 * 256 + 8 * 6) * 4 <= lay["h"]
     assert lay["logits"] - lay["header"] >= sg.flint_moe.HEADER_BYTES
     hdr_decl = re.search(r"FLINT_MOE_WS_HEADER_BYTES\s+(\d+)",
                          open(os.path.join(ROOT, "include", "flint_moe.h")).read())

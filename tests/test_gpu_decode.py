@@ -90,15 +90,15 @@ def test_intermediates_t8(dev):
     logits = ws_region(r, "logits", T, np.float32, T * 256).reshape(T, 256)
     for t, rr in enumerate(res):
         np.testing.assert_allclose(logits[t], rr.logits, rtol=0, atol=2e-5)
-    # The counters are reset at the end of the forward; the lists and the
-    # union stay in place.  Rebuild the expected bucketing from the device ids.
+    # The routing table is the bucketing of the device's own ids: bit-exact.
     b = bucket(r["ids"], 256)
     nU = len(b["active"])
-    assert sorted(ws_region(r, "active", T, np.int32, nU).tolist()) == b["active"].tolist()
-    lists = ws_region(r, "lists", T, np.int32, 256 * T).reshape(256, T)
-    for e in b["active"]:
-        seg = b["slots"][b["offsets"][e]:b["offsets"][e + 1]]
-        assert sorted(lists[e][:len(seg)].tolist()) == seg.tolist()
+    route = ws_region(r, "route", T, np.int32, 2 + 2 * 256 + T * 6)
+    assert route[0] == nU
+    np.testing.assert_array_equal(route[1:1 + nU], b["active"])
+    off = route[1 + 256:1 + 256 + nU + 1]
+    np.testing.assert_array_equal(off, b["offsets"][b["active"].tolist() + [256]])
+    np.testing.assert_array_equal(route[2 + 512:2 + 512 + T * 6], b["slots"])
     hdr = ws_region(r, "header", T, np.uint32, dev["sg"].flint_moe.HEADER_BYTES // 4)
     assert not hdr.any(), "header not reset (or the error word is set)"
     h = ws_region(r, "h", T, np.float32, (T * 6 + T) * 512).reshape(T * 7, 512)
