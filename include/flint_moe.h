@@ -54,8 +54,8 @@ typedef struct flint_moe_ctx flint_moe_ctx; /* opaque, host memory */
 
 /* Bytes at the start of every workspace that hold the kernels' completion
  * counters.  They must be zero before a workspace is first used; every
- * completed forward leaves them zero again (except the error word). */
-#define FLINT_MOE_WS_HEADER_BYTES 95232
+ * completed forward leaves them zero again. */
+#define FLINT_MOE_WS_HEADER_BYTES 29696
 
 typedef enum flint_status {
   FLINT_OK = 0,
@@ -116,11 +116,8 @@ typedef struct flint_moe_weights {
  * valid once the forward that wrote it has completed). */
 typedef struct flint_moe_ws_layout {
   size_t total_bytes;
-  size_t header;     /* FLINT_MOE_WS_HEADER_BYTES of uint32 counters; zero before first use
-                        and after every completed forward, except the error word */
-  size_t error_word; /* uint32 inside the header: nonzero once a bounded wait timed out
-                        (results of that forward are invalid); sticky until the caller
-                        clears it */
+  size_t header;     /* FLINT_MOE_WS_HEADER_BYTES of uint32 completion counters; zero before
+                        first use and after every completed forward */
   size_t logits;     /* fp32 [T][E]: z (router GEMV + bias) */
   size_t topk_ids;   /* int32 [T][k]: selected experts in rank order */
   size_t topk_w;     /* fp32 [T][k]: routing weights */

@@ -1,31 +1,24 @@
-// Decode-sized (T <= 64) bf16 path of the Flint MoE layer on gfx950: the
-// whole layer in one launch.
+// Decode-sized (T <= 64) bf16 path of the Flint MoE layer on gfx950.
 //
-// The layer is cut into work items of ~64 KiB of weights each, in an order
-// where an item only ever waits for items before it:
-//   router    (token t, 16 router rows)   T * ceil(E/16) items
-//   shared    (8 gate/up row pairs of the shared expert, all T tokens)  64
-//   gate/up   (active expert a, 8 row pairs)   max|U| * 64
-//   down      (expert, 64 output rows): the shared expert first, then each
-//             active expert                   (1 + max|U|) * 32
-// Block b takes items b, b + G, b + 2G, ... (G = resident blocks), so the
-// phases overlap: the shared expert streams while tokens are routed, the
-// down rows of early experts stream while later experts finish gate/up.
-// Hand-offs between blocks use completion counters in the workspace header
-// and coherent (write-through) stores/loads, never whole-cache flushes:
-//   - the last router item of token t picks its top-k; the last token to
-//     finish buckets every (token, rank) slot by expert into the routing
-//     table (U ascending, slots grouped by expert in ascending slot order)
-//     and raises the routed flag;
-//   - each block reads the routing table once into LDS;
-//   - gate/up item (a, .) needs the table; 64 finished items of active
-//     expert a complete its h;
-//   - down item (a, tile) issues its weight loads, then waits for expert a's
-//     h and writes y for its rows; the last of the |U| + 1 down items of a
-//     tile combines it: out = y_shared + sum_j w_j y_j in a fixed order,
-//     rounded once to bf16;
-//   - the last block to run out of items resets every counter to zero.
-// Every wait is bounded; a timeout sets an error word instead of hanging.
+// Three launches on the caller's stream, each cut into blocks that move
+// ~64 KiB of weights:
+//   1. route   : router GEMV, 16 rows x one token per block.  The last block
+//                of a token picks its top-k by sigmoid score; the last token
+//                to finish buckets every (token, rank) slot by expert into
+//                the routing table (U ascending, slots grouped by expert in
+//                ascending slot order).  Extra blocks of the same launch run
+//                the shared expert's gate/up GEMV, which needs only x.
+//   2. gate/up : (active expert a, 8 gate/up row pairs) per block: the rows
+//                are streamed once for all of a's tokens; SiLU-and-mul in
+//                registers; h stays fp32.
+//   3. down    : (expert, 64 output rows) per block, the shared expert
+//                included: y = w2 rows . h for each of the expert's slots;
+//                the last of the |U| + 1 blocks of a row tile combines it:
+//                out = y_shared + sum_j w_j y_j in a fixed order, rounded once
+//                to bf16.
+// Hand-offs inside a launch use completion tickets in the workspace header
+// and coherent (write-through) stores/loads, never whole-cache flushes;
+// between launches the stream order is enough.
 //
 // What is computed follows "vLLM Day-0 Support for Recursive's Flint"
 // (section "Flint Model Architecture", bullet "MoE Structure"; section
@@ -50,62 +43,12 @@ constexpr int kUnitsPerExpert = I / kPairsPerItem;  // 64
 constexpr int kTileRows = 64;                 // down item: 64 output rows (16 per wave)
 constexpr int kRowsPerWave = kTileRows / 4;
 constexpr int kTiles = H / kTileRows;         // 32
-constexpr int kXChunk = 8;                    // tokens staged in LDS at a time
-constexpr uint32_t kSpinLimit = 1u << 18;  // ~0.3 s of polling
+constexpr int kXChunk = 4;                    // tokens staged in LDS at a time (16 KiB)
 
 static_assert(H % (8 * kWave) == 0, "H must be a multiple of 512");
 static_assert(I == 8 * kWave, "down GEMV maps one 16-byte vector of a w2 row per lane");
 static_assert(kTiles <= 32, "tile tickets");
 static_assert(kDecodeMaxT * kMaxTopK <= 32767 && kMaxExperts <= 32767, "int16 routing table");
-
-struct Plan {
-  int G;            // blocks in the grid
-  int rg;           // router items per token
-  int n_router;     // T * rg
-  int g_shared;     // first shared gate/up item
-  int g_routed;     // first routed gate/up item
-  int d_shared;     // first down item (shared expert)
-  int d_routed;     // first routed down item
-  int n_items;
-  int max_active;   // min(E, T*k)
-};
-
-// ---------------------------------------------------------------- waiting
-
-// Thread 0 polls `*p >= target` with a bounded number of sleeps; the value
-// it saw is returned to every thread.  A timeout raises the sticky error word.
-__device__ __forceinline__ uint32_t block_wait(const uint32_t* p, uint32_t target, uint32_t* err,
-                                               int* s_val) {
-  if (threadIdx.x == 0) {
-    uint32_t it = 0, v;
-    while ((v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < target) {
-      if (++it == kSpinLimit) {
-        __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(4);
-    }
-    *s_val = (int)v;
-  }
-  __syncthreads();
-  const uint32_t v = (uint32_t)*s_val;
-  __syncthreads();
-  return v;
-}
-
-// |U| once routing is done (each block polls one of the replicated flags).
-__device__ __forceinline__ int wait_routed(const uint32_t* hdr, uint32_t* err, int* s_val) {
-  const uint32_t* flag = hdr + kHdrRouted + (blockIdx.x % kRoutingReplicas) * kLine;
-  return (int)block_wait(flag, 1u, err, s_val) - 1;
-}
-
-// Every thread drains its stores, then thread 0 adds 1 to *counter.
-__device__ __forceinline__ void block_signal(uint32_t* counter) {
-  drain_memory_ops();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // ---------------------------------------------------------------- gate/up
 
@@ -162,8 +105,8 @@ __device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ w13, in
       for (int r = 0; r < 4; ++r) acc[r] = wave_sum_lane63(acc[r]);
       if (lane == kWave - 1) {
         float* hr = h + (size_t)list.hrow(c0 + j) * I + p;
-        store_coherent(hr, silu(acc[0]) * acc[2]);
-        store_coherent(hr + 1, silu(acc[1]) * acc[3]);
+        hr[0] = silu(acc[0]) * acc[2];
+        hr[1] = silu(acc[1]) * acc[3];
       }
     }
   }
@@ -295,11 +238,11 @@ __device__ void build_route_table(const LayerArgs& a, void* smem) {
   }
 }
 
-__device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_flag, void* smem) {
+__device__ void router_block(const LayerArgs& a, int rg, int item, int* s_flag, void* smem) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int t = item / P.rg;
-  const int g = item - t * P.rg;
+  const int t = item / rg;
+  const int g = item - t * rg;
   const int e0 = g * kRouterRowsPerItem + wave * 4;
 
   const u32x4* xr = reinterpret_cast<const u32x4*>(a.x + (size_t)t * H);
@@ -329,19 +272,12 @@ __device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_
   }
   uint32_t* hdr = a.ws.header;
   // The last router item of token t sees every logit of t.
-  if (!last_block_ticket(hdr + kHdrTokTicket + t * kLine, P.rg, s_flag)) return;
+  if (!last_block_ticket(hdr + kHdrTokTicket + t * kLine, rg, s_flag)) return;
   if (wave == 0) route_token(a, t);
   // The last token to finish sees every token's selection: it builds the
-  // routing table, then publishes |U| + 1.
+  // routing table (read by the next launches).
   if (!last_block_ticket(hdr + kHdrTokensDone, a.T, s_flag)) return;
   build_route_table(a, smem);
-  drain_memory_ops();
-  __syncthreads();
-  if (threadIdx.x < kRoutingReplicas) {
-    const uint32_t n = (uint32_t)load_coherent(a.ws.route);
-    __hip_atomic_store(hdr + kHdrRouted + threadIdx.x * kLine, n + 1u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 // ---------------------------------------------------------------- down
@@ -350,8 +286,8 @@ __device__ void router_item(const LayerArgs& a, const Plan& P, int item, int* s_
 // 16-byte vector per row per lane), for each of the expert's slots:
 // y[hrow][row] = w2[row] . h[hrow], summed over the 64 lanes in a fixed tree.
 // Slots go in chunks of 16: their h rows are staged in LDS with coalesced
-// coherent loads, the results collect in LDS and leave as one batch of
-// stores, so no load waits behind this item's own write-through stores.
+// loads, the results collect in LDS and leave as one batch of coherent
+// stores (the tile's combining block reads them in this launch).
 constexpr int kDownChunk = 16;
 
 __device__ __forceinline__ void load_down_weights(u32x4 (&wv)[kRowsPerWave],
@@ -374,7 +310,7 @@ __device__ __forceinline__ void down_rows(u32x4 (&wv)[kRowsPerWave], int r0, int
     __syncthreads();
     for (int q = threadIdx.x; q < n * I; q += kThreads) {
       const int j = q / I;
-      hs[q] = load_coherent(h + (size_t)list.hrow(c0 + j) * I + (q - j * I));
+      hs[q] = h[(size_t)list.hrow(c0 + j) * I + (q - j * I)];
     }
     __syncthreads();
     for (int j = 0; j < n; ++j) {
@@ -417,137 +353,114 @@ __device__ void combine_tile(const LayerArgs& a, int r0) {
     const int r = r0 + (q - t * kTileRows);
     float o = load_coherent(a.ws.y + (size_t)(T * k + t) * H + r);
     for (int j = 0; j < k; ++j)
-      o = fmaf(load_coherent(a.ws.wts + t * k + j),
-               load_coherent(a.ws.y + (size_t)(t * k + j) * H + r), o);
+      o = fmaf(a.ws.wts[t * k + j], load_coherent(a.ws.y + (size_t)(t * k + j) * H + r), o);
     a.out[(size_t)t * H + r] = f32_to_bf16_rne(o);
   }
 }
 
 // ---------------------------------------------------------------- kernel
 
-// The routing table, copied once per block into LDS.
-struct RouteLds {
-  int n;                              // |U|, or -1 before the block has read it
-  int16_t active[kMaxExperts];
-  int16_t off[kMaxExperts + 1];
-  int16_t slots[kDecodeMaxT * kMaxTopK];
-};
+// ---------------------------------------------------------------- kernels
 
-__device__ __forceinline__ void ensure_routes(const LayerArgs& a, RouteLds& rt, uint32_t* err,
-                                              int* s_val) {
-  if (rt.n >= 0) return;  // block-uniform
-  const int n = wait_routed(a.ws.header, err, s_val);
-  const int E = a.E, ns = a.T * a.k;
-  const int32_t* route = a.ws.route;
-  for (int q = threadIdx.x; q < n; q += kThreads) rt.active[q] = (int16_t)load_coherent(route + 1 + q);
-  for (int q = threadIdx.x; q <= n; q += kThreads) rt.off[q] = (int16_t)load_coherent(route + 1 + E + q);
-  for (int q = threadIdx.x; q < ns; q += kThreads) rt.slots[q] = (int16_t)load_coherent(route + 2 + 2 * E + q);
-  if (threadIdx.x == 0) rt.n = n;
-  __syncthreads();
+// LDS of the route kernel: x staging, or the bucketing tables (counts,
+// offsets and 16-word occupancy masks of 256 experts).
+constexpr int kRouteLdsVec = (2 * kMaxExperts * 4 + kMaxExperts * (kDecodeMaxT * kMaxTopK / 32) * 4) / 16;
+static_assert(kRouteLdsVec >= kXChunk * kVecH, "route LDS holds the x staging");
+
+__global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a, int rg, int n_router) {
+  __shared__ u32x4 xs[kRouteLdsVec];
+  __shared__ int s_flag;
+  if ((int)blockIdx.x < n_router) {
+    router_block(a, rg, blockIdx.x, &s_flag, xs);
+  } else {
+    // Shared expert gate/up: all T tokens, h rows T*k + t.
+    const int unit = blockIdx.x - n_router;
+    gateup_item(reinterpret_cast<const uint16_t*>(a.shared.w13), unit * kPairsPerItem, a.T,
+                TokenList{nullptr, a.k, a.T * a.k}, a.x, a.ws.h, xs);
+  }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
-void moe_decode_kernel(LayerArgs a, Plan P) {
-  __shared__ u32x4 xs[kXChunk * kVecH];   // 32 KiB: x staging (gate/up), h staging (down),
-                                          // bucketing tables (routing)
-  __shared__ float ys[kDownChunk * kTileRows];
-  __shared__ RouteLds rt;
-  __shared__ int s_flag, s_val;
-  uint32_t* hdr = a.ws.header;
-  uint32_t* err = hdr + kHdrError;
-  const int T = a.T, k = a.k;
-  if (threadIdx.x == 0) rt.n = -1;
-  __syncthreads();
-
-  for (int item = blockIdx.x; item < P.n_items; item += P.G) {
-    if (item < P.n_router) {
-      router_item(a, P, item, &s_flag, xs);
-    } else if (item < P.g_routed) {
-      // Shared expert gate/up: all T tokens, h rows T*k + t.
-      const int unit = item - P.g_shared;
-      gateup_item(reinterpret_cast<const uint16_t*>(a.shared.w13), unit * kPairsPerItem, T,
-                  TokenList{nullptr, k, T * k}, a.x, a.ws.h, xs);
-      block_signal(hdr + kHdrSharedDone);
-    } else if (item < P.d_shared) {
-      // Routed gate/up: active index ai, unit.
-      const int ai = (item - P.g_routed) / kUnitsPerExpert;
-      const int unit = (item - P.g_routed) - ai * kUnitsPerExpert;
-      ensure_routes(a, rt, err, &s_val);
-      if (ai >= rt.n) continue;
-      const int e = rt.active[ai];
-      const uint16_t* w13 = reinterpret_cast<const uint16_t*>(a.routed.w13) + (size_t)e * 2 * I * H;
-      gateup_item(w13, unit * kPairsPerItem, rt.off[ai + 1] - rt.off[ai],
-                  TokenList{rt.slots + rt.off[ai], k, 0}, a.x, a.ws.h, xs);
-      block_signal(hdr + kHdrExpertDone + ai * kLine);
-    } else {
-      // Down: (expert, 64-row tile); the shared expert's tiles come first.
-      const int di = item - P.d_shared;
-      const int ei = di / kTiles;          // 0: shared, 1 + ai: active index ai
-      const int tile = di - ei * kTiles;
-      ensure_routes(a, rt, err, &s_val);
-      const int ai = ei - 1;
-      if (ai >= rt.n) continue;
-      u32x4 wv[kRowsPerWave];
-      TokenList list{nullptr, k, T * k};
-      int cnt = T;
-      if (ei == 0) {
-        load_down_weights(wv, reinterpret_cast<const uint16_t*>(a.shared.w2), tile * kTileRows);
-        block_wait(hdr + kHdrSharedDone, (uint32_t)kUnitsPerExpert, err, &s_val);
-      } else {
-        const int e = rt.active[ai];
-        load_down_weights(wv, reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)e * H * I,
-                          tile * kTileRows);
-        list.slots = rt.slots + rt.off[ai];
-        cnt = rt.off[ai + 1] - rt.off[ai];
-        block_wait(hdr + kHdrExpertDone + ai * kLine, (uint32_t)kUnitsPerExpert, err, &s_val);
-      }
-      down_rows(wv, tile * kTileRows, cnt, list, a.ws.h, a.ws.y, reinterpret_cast<float*>(xs), ys);
-      // The last of the |U| + 1 down items of this tile combines it.
-      if (last_block_ticket(hdr + kHdrTileTicket + tile * kLine, (uint32_t)(rt.n + 1), &s_flag))
-        combine_tile(a, tile * kTileRows);
+// Slots of active expert ai (its count returned), copied from the routing
+// table into LDS; -1 if ai is not an active index.
+__device__ __forceinline__ int load_expert_slots(const LayerArgs& a, int ai, int16_t* s_slots,
+                                                 int* s_meta) {
+  const int32_t* route = a.ws.route;
+  const int E = a.E;
+  if (threadIdx.x == 0) {
+    const int n = route[0];
+    s_meta[0] = n;
+    if (ai < n) {
+      s_meta[1] = route[1 + ai];
+      s_meta[2] = route[1 + E + ai];
+      s_meta[3] = route[1 + E + ai + 1];
     }
   }
+  __syncthreads();
+  if (ai >= s_meta[0]) return -1;
+  const int off = s_meta[2], cnt = s_meta[3] - s_meta[2];
+  for (int q = threadIdx.x; q < cnt; q += kThreads) s_slots[q] = (int16_t)route[2 + 2 * E + off + q];
+  __syncthreads();
+  return cnt;
+}
 
-  // The last block to finish resets the per-forward counters.
-  if (!last_block_ticket(hdr + kHdrExit, (uint32_t)P.G, &s_flag)) return;
-  const int n_active = load_coherent(a.ws.route);
-  for (int i = threadIdx.x; i < n_active; i += kThreads)
-    __hip_atomic_store(hdr + kHdrExpertDone + i * kLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x < kRoutingReplicas)
-    __hip_atomic_store(hdr + kHdrRouted + threadIdx.x * kLine, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x == 0)
-    __hip_atomic_store(hdr + kHdrSharedDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__global__ __launch_bounds__(kThreads) void gateup_kernel(LayerArgs a) {
+  __shared__ u32x4 xs[kXChunk * kVecH];
+  __shared__ int16_t s_slots[kDecodeMaxT];
+  __shared__ int s_meta[4];
+  const int ai = blockIdx.x / kUnitsPerExpert;
+  const int unit = blockIdx.x - ai * kUnitsPerExpert;
+  const int cnt = load_expert_slots(a, ai, s_slots, s_meta);
+  if (cnt < 0) return;
+  const int e = s_meta[1];
+  const uint16_t* w13 = reinterpret_cast<const uint16_t*>(a.routed.w13) + (size_t)e * 2 * I * H;
+  gateup_item(w13, unit * kPairsPerItem, cnt, TokenList{s_slots, a.k, 0}, a.x, a.ws.h, xs);
+}
+
+__global__ __launch_bounds__(kThreads) void down_kernel(LayerArgs a) {
+  __shared__ float hs[kDownChunk * I];     // 32 KiB: h staging
+  __shared__ float ys[kDownChunk * kTileRows];
+  __shared__ int16_t s_slots[kDecodeMaxT];
+  __shared__ int s_meta[4];
+  __shared__ int s_flag;
+  const int ei = blockIdx.x / kTiles;      // 0: shared expert, 1 + ai: active index ai
+  const int tile = blockIdx.x - ei * kTiles;
+  const int T = a.T, k = a.k;
+  u32x4 wv[kRowsPerWave];
+  TokenList list{nullptr, k, T * k};
+  int cnt = T;
+  if (ei == 0) {
+    load_down_weights(wv, reinterpret_cast<const uint16_t*>(a.shared.w2), tile * kTileRows);
+    if (threadIdx.x == 0) s_meta[0] = a.ws.route[0];
+    __syncthreads();
+  } else {
+    cnt = load_expert_slots(a, ei - 1, s_slots, s_meta);
+    if (cnt < 0) return;
+    load_down_weights(wv, reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)s_meta[1] * H * I,
+                      tile * kTileRows);
+    list.slots = s_slots;
+  }
+  const int n_active = s_meta[0];
+  down_rows(wv, tile * kTileRows, cnt, list, a.ws.h, a.ws.y, hs, ys);
+  // The last of the |U| + 1 blocks of this row tile combines it.
+  if (last_block_ticket(a.ws.header + kHdrTileTicket + tile * kLine, (uint32_t)(n_active + 1), &s_flag))
+    combine_tile(a, tile * kTileRows);
 }
 
 }  // namespace
 
-int decode_grid_limit() {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_decode_kernel, kThreads, 0) !=
-      hipSuccess)
-    return 0;
-  return cus * min(per_cu, 4);
-}
-
-hipError_t launch_decode_bf16(const LayerArgs& a, int grid_limit, hipStream_t stream,
-                              StageEvents* ev) {
-  Plan P;
-  P.rg = (a.E + kRouterRowsPerItem - 1) / kRouterRowsPerItem;
-  P.n_router = a.T * P.rg;
-  P.max_active = min(a.E, a.T * a.k);
-  P.g_shared = P.n_router;
-  P.g_routed = P.g_shared + kUnitsPerExpert;
-  P.d_shared = P.g_routed + P.max_active * kUnitsPerExpert;
-  P.d_routed = P.d_shared + kTiles;
-  P.n_items = P.d_routed + P.max_active * kTiles;
-  P.G = min(P.n_items, grid_limit);
+hipError_t launch_decode_bf16(const LayerArgs& a, hipStream_t stream, StageEvents* ev) {
   StageEvents none;
   StageEvents& e = ev ? *ev : none;
+  const int rg = (a.E + kRouterRowsPerItem - 1) / kRouterRowsPerItem;
+  const int n_router = a.T * rg;
+  const int max_active = min(a.E, a.T * a.k);
   e.mark(stream);
-  hipLaunchKernelGGL(moe_decode_kernel, dim3(P.G), dim3(kThreads), 0, stream, a, P);
+  hipLaunchKernelGGL(route_kernel, dim3(n_router + kUnitsPerExpert), dim3(kThreads), 0, stream, a, rg,
+                     n_router);
+  e.mark(stream);
+  hipLaunchKernelGGL(gateup_kernel, dim3(max_active * kUnitsPerExpert), dim3(kThreads), 0, stream, a);
+  e.mark(stream);
+  hipLaunchKernelGGL(down_kernel, dim3((1 + max_active) * kTiles), dim3(kThreads), 0, stream, a);
   e.mark(stream);
   return hipGetLastError();
 }

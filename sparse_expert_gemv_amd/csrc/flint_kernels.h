@@ -12,21 +12,14 @@ constexpr int kInter = 512;        // I
 constexpr int kMaxExperts = 256;   // E upper bound (four router scores per lane)
 constexpr int kMaxTopK = 8;
 constexpr int kDecodeMaxT = 64;    // largest T taken by the GEMV (decode) kernels
-// Workspace header: uint32 counters, each hot one on its own 256-byte line
-// so that pollers of one word never queue behind atomics on another.  All
-// are zero before a forward starts and zero after it ends (except the
-// sticky error word).
+// Workspace header: uint32 completion counters, each on its own 256-byte
+// line so that tickets on one never queue behind atomics on another.  All
+// are zero before a forward starts and zero after it ends.
 constexpr int kLine = 64;                       // words per 256-byte line
-constexpr int kRoutingReplicas = 16;
 constexpr int kHdrTokensDone = 0 * kLine;       // tokens whose selection is complete
-constexpr int kHdrExit = 1 * kLine;             // blocks that finished all their items
-constexpr int kHdrSharedDone = 2 * kLine;       // shared-expert gate/up items done
-constexpr int kHdrError = 3 * kLine;            // sticky: a bounded wait timed out
-constexpr int kHdrRouted = 4 * kLine;           // [16 lines] |U| + 1 once routing is done
 constexpr int kHdrTokTicket = 20 * kLine;       // [64 lines] router items done per token
 constexpr int kHdrTileTicket = 84 * kLine;      // [32 lines] down items done per output tile
-constexpr int kHdrExpertDone = 116 * kLine;     // [256 lines] gate/up items done per active index
-constexpr int kHeaderWords = 372 * kLine;       // 93 KiB
+constexpr int kHeaderWords = 116 * kLine;       // 29 KiB
 
 // Routing table (int32), written once per forward by the block that
 // finishes routing:
@@ -86,10 +79,6 @@ struct StageEvents {
   }
 };
 
-// Blocks a decode launch may use on the current device (resident capacity).
-int decode_grid_limit();
-
-hipError_t launch_decode_bf16(const LayerArgs& a, int grid_limit, hipStream_t stream,
-                              StageEvents* ev);
+hipError_t launch_decode_bf16(const LayerArgs& a, hipStream_t stream, StageEvents* ev);
 
 }  // namespace flint

@@ -18,8 +18,6 @@
 struct flint_moe_ctx {
   flint_moe_config cfg;
   std::string last_error;
-  int grid_device = -1;  // device the cached decode grid limit belongs to
-  int grid_limit = 0;
 };
 
 namespace {
@@ -36,7 +34,6 @@ void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L
   size_t o = 0;
   std::memset(L, 0, sizeof(*L));
   L->header = o;   o = align_up(o + kHeaderBytes);
-  L->error_word = L->header + sizeof(uint32_t) * flint::kHdrError;
   L->logits = o;   o = align_up(o + t * E * sizeof(float));
   L->topk_ids = o; o = align_up(o + t * k * sizeof(int32_t));
   L->topk_w = o;   o = align_up(o + t * k * sizeof(float));
@@ -197,15 +194,7 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.nvfp4 = c.format == FLINT_W_NVFP4;
 
   (void)hipGetLastError();  // do not report an earlier, unrelated failure
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(ctx, FLINT_ERR_HIP, "hipGetDevice failed");
-  if (ctx->grid_device != dev) {
-    ctx->grid_limit = flint::decode_grid_limit();
-    ctx->grid_device = dev;
-  }
-  if (ctx->grid_limit <= 0) return fail(ctx, FLINT_ERR_HIP, "occupancy query failed");
-  const hipError_t err =
-      flint::launch_decode_bf16(a, ctx->grid_limit, static_cast<hipStream_t>(stream), ev);
+  const hipError_t err = flint::launch_decode_bf16(a, static_cast<hipStream_t>(stream), ev);
   if (err != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(err));
   return FLINT_OK;
 }

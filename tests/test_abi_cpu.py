@@ -68,7 +68,6 @@ def test_workspace_sizes_grow_with_T():
     offs = [lay[k] for k in ("header", "logits", "topk_ids", "topk_w", "route", "h", "y",
                              "extra")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert lay["header"] < lay["error_word"] < lay["logits"]
     assert lay["route"] + (2 + 2 * 256 + 8 * 6) * 4 <= lay["h"]
     assert lay["logits"] - lay["header"] >= sg.flint_moe.HEADER_BYTES
     hdr_decl = re.search(r"FLINT_MOE_WS_HEADER_BYTES\s+(\d+)",
