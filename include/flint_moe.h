@@ -55,7 +55,7 @@ typedef struct flint_moe_ctx flint_moe_ctx; /* opaque, host memory */
 /* Bytes at the start of every workspace that hold the kernels' completion
  * counters.  They must be zero before a workspace is first used; every
  * completed forward leaves them zero again. */
-#define FLINT_MOE_WS_HEADER_BYTES 29696
+#define FLINT_MOE_WS_HEADER_BYTES 21504
 
 typedef enum flint_status {
   FLINT_OK = 0,
@@ -130,7 +130,6 @@ typedef struct flint_moe_ws_layout {
                                                  within a group */
   size_t h;          /* fp32 [T*k + T][I]: h of slot s in row s; h of the shared expert
                         for token t in row T*k + t */
-  size_t y;          /* fp32 [T*k + T][H]: unweighted down projection of each h row */
   size_t extra;      /* path-private scratch (prefill-sized T only) */
 } flint_moe_ws_layout;
 

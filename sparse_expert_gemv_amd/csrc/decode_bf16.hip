@@ -11,11 +11,11 @@
 //   2. gate/up : (active expert a, 8 gate/up row pairs) per block: the rows
 //                are streamed once for all of a's tokens; SiLU-and-mul in
 //                registers; h stays fp32.
-//   3. down    : (expert, 64 output rows) per block, the shared expert
-//                included: y = w2 rows . h for each of the expert's slots;
-//                the last of the |U| + 1 blocks of a row tile combines it:
-//                out = y_shared + sum_j w_j y_j in a fixed order, rounded once
-//                to bf16.
+//   3. down    : 8 output rows of every token per block, over the |U| active
+//                experts and the shared expert, each expert's w2 rows read
+//                once; the partial dot products meet in LDS and combine as
+//                out = shared + sum_j w_j * routed_j in a fixed order,
+//                rounded once to bf16.
 // Hand-offs inside a launch use completion tickets in the workspace header
 // and coherent (write-through) stores/loads, never whole-cache flushes;
 // between launches the stream order is enough.
@@ -40,14 +40,10 @@ constexpr int kVecPerLaneH = kVecH / kWave;   // 4
 constexpr int kRouterRowsPerItem = 16;        // 4 waves x 4 rows
 constexpr int kPairsPerItem = 8;              // gate/up item: 8 (gate, up) row pairs
 constexpr int kUnitsPerExpert = I / kPairsPerItem;  // 64
-constexpr int kTileRows = 64;                 // down item: 64 output rows (16 per wave)
-constexpr int kRowsPerWave = kTileRows / 4;
-constexpr int kTiles = H / kTileRows;         // 32
 constexpr int kXChunk = 4;                    // tokens staged in LDS at a time (16 KiB)
 
 static_assert(H % (8 * kWave) == 0, "H must be a multiple of 512");
 static_assert(I == 8 * kWave, "down GEMV maps one 16-byte vector of a w2 row per lane");
-static_assert(kTiles <= 32, "tile tickets");
 static_assert(kDecodeMaxT * kMaxTopK <= 32767 && kMaxExperts <= 32767, "int16 routing table");
 
 // ---------------------------------------------------------------- gate/up
@@ -65,25 +61,31 @@ struct TokenList {
 
 // One block (4 waves) computes h = silu(gate) * up for the row pairs
 // [p0, p0 + 8) of one expert, for `count` tokens.  Wave w owns pairs
-// p0 + 2w and p0 + 2w + 1: four 4 KiB rows held in registers while the
-// tokens' x vectors stream through LDS.
-__device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ w13, int p0, int count,
-                                            const TokenList& list, const uint16_t* __restrict__ x,
-                                            float* h, u32x4* xs) {
+// p0 + 2w and p0 + 2w + 1: four 4 KiB rows held in registers (loaded first,
+// so they are in flight while the token list is fetched) while the tokens'
+// x vectors stream through LDS.
+typedef u32x4 GateUpRows[4][kVecPerLaneH];
+
+__device__ __forceinline__ void load_gateup_weights(GateUpRows& wv, const uint16_t* __restrict__ w13,
+                                                    int p0) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int p = p0 + 2 * wave;
+  const int p = p0 + 2 * (threadIdx.x / kWave);
   const u32x4* rows[4] = {
       reinterpret_cast<const u32x4*>(w13 + (size_t)p * H),
       reinterpret_cast<const u32x4*>(w13 + (size_t)(p + 1) * H),
       reinterpret_cast<const u32x4*>(w13 + (size_t)(I + p) * H),
       reinterpret_cast<const u32x4*>(w13 + (size_t)(I + p + 1) * H)};
-  u32x4 wv[4][kVecPerLaneH];
 #pragma unroll
   for (int i = 0; i < kVecPerLaneH; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) wv[r][i] = rows[r][lane + i * kWave];
+}
 
+__device__ __forceinline__ void gateup_compute(GateUpRows& wv, int p0, int count,
+                                               const TokenList& list, const uint16_t* __restrict__ x,
+                                               float* h, u32x4* xs) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int p = p0 + 2 * (threadIdx.x / kWave);
   for (int c0 = 0; c0 < count; c0 += kXChunk) {
     const int n = min(kXChunk, count - c0);
     __syncthreads();
@@ -280,86 +282,6 @@ __device__ void router_block(const LayerArgs& a, int rg, int item, int* s_flag, 
   build_route_table(a, smem);
 }
 
-// ---------------------------------------------------------------- down
-
-// Down item: rows [r0, r0 + 64) of one expert's w2 (wave w: 16 rows, one
-// 16-byte vector per row per lane), for each of the expert's slots:
-// y[hrow][row] = w2[row] . h[hrow], summed over the 64 lanes in a fixed tree.
-// Slots go in chunks of 16: their h rows are staged in LDS with coalesced
-// loads, the results collect in LDS and leave as one batch of coherent
-// stores (the tile's combining block reads them in this launch).
-constexpr int kDownChunk = 16;
-
-__device__ __forceinline__ void load_down_weights(u32x4 (&wv)[kRowsPerWave],
-                                                  const uint16_t* __restrict__ w2, int r0) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int rw = r0 + wave * kRowsPerWave;
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r)
-    wv[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(rw + r) * I)[lane];
-}
-
-__device__ __forceinline__ void down_rows(u32x4 (&wv)[kRowsPerWave], int r0, int count,
-                                          const TokenList& list, const float* h, float* y,
-                                          float* hs, float* ys) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  for (int c0 = 0; c0 < count; c0 += kDownChunk) {
-    const int n = min(kDownChunk, count - c0);
-    __syncthreads();
-    for (int q = threadIdx.x; q < n * I; q += kThreads) {
-      const int j = q / I;
-      hs[q] = h[(size_t)list.hrow(c0 + j) * I + (q - j * I)];
-    }
-    __syncthreads();
-    for (int j = 0; j < n; ++j) {
-      // Keep the weights packed across slots: widening all 16 rows to fp32
-      // once would cost 128 registers.
-#pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r) asm volatile("" : "+v"(wv[r]));
-      const f32x4 h0 = *reinterpret_cast<const f32x4*>(hs + j * I + lane * 8);
-      const f32x4 h1 = *reinterpret_cast<const f32x4*>(hs + j * I + lane * 8 + 4);
-      float acc[kRowsPerWave];
-#pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r) {
-        float v = bf16_lo(wv[r].x) * h0.x;
-        v = fmaf(bf16_hi(wv[r].x), h0.y, v);
-        v = fmaf(bf16_lo(wv[r].y), h0.z, v);
-        v = fmaf(bf16_hi(wv[r].y), h0.w, v);
-        v = fmaf(bf16_lo(wv[r].z), h1.x, v);
-        v = fmaf(bf16_hi(wv[r].z), h1.y, v);
-        v = fmaf(bf16_lo(wv[r].w), h1.z, v);
-        v = fmaf(bf16_hi(wv[r].w), h1.w, v);
-        acc[r] = wave_sum_lane63(v);
-      }
-      if (lane == kWave - 1)
-#pragma unroll
-        for (int r = 0; r < kRowsPerWave; ++r) ys[j * kTileRows + wave * kRowsPerWave + r] = acc[r];
-    }
-    __syncthreads();
-    for (int q = threadIdx.x; q < n * kTileRows; q += kThreads) {
-      const int j = q / kTileRows;
-      store_coherent(y + (size_t)list.hrow(c0 + j) * H + r0 + (q - j * kTileRows), ys[q]);
-    }
-  }
-}
-
-// out rows [r0, r0 + 64) of every token: shared + sum_j w_j * y_j, fixed order.
-__device__ void combine_tile(const LayerArgs& a, int r0) {
-  const int T = a.T, k = a.k;
-  for (int q = threadIdx.x; q < T * kTileRows; q += kThreads) {
-    const int t = q / kTileRows;
-    const int r = r0 + (q - t * kTileRows);
-    float o = load_coherent(a.ws.y + (size_t)(T * k + t) * H + r);
-    for (int j = 0; j < k; ++j)
-      o = fmaf(a.ws.wts[t * k + j], load_coherent(a.ws.y + (size_t)(t * k + j) * H + r), o);
-    a.out[(size_t)t * H + r] = f32_to_bf16_rne(o);
-  }
-}
-
-// ---------------------------------------------------------------- kernel
-
 // ---------------------------------------------------------------- kernels
 
 // LDS of the route kernel: x staging, or the bucketing tables (counts,
@@ -375,75 +297,153 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a, int rg, in
   } else {
     // Shared expert gate/up: all T tokens, h rows T*k + t.
     const int unit = blockIdx.x - n_router;
-    gateup_item(reinterpret_cast<const uint16_t*>(a.shared.w13), unit * kPairsPerItem, a.T,
-                TokenList{nullptr, a.k, a.T * a.k}, a.x, a.ws.h, xs);
+    GateUpRows wv;
+    load_gateup_weights(wv, reinterpret_cast<const uint16_t*>(a.shared.w13), unit * kPairsPerItem);
+    gateup_compute(wv, unit * kPairsPerItem, a.T, TokenList{nullptr, a.k, a.T * a.k}, a.x, a.ws.h, xs);
   }
 }
 
-// Slots of active expert ai (its count returned), copied from the routing
-// table into LDS; -1 if ai is not an active index.
-__device__ __forceinline__ int load_expert_slots(const LayerArgs& a, int ai, int16_t* s_slots,
-                                                 int* s_meta) {
-  const int32_t* route = a.ws.route;
-  const int E = a.E;
-  if (threadIdx.x == 0) {
-    const int n = route[0];
-    s_meta[0] = n;
-    if (ai < n) {
-      s_meta[1] = route[1 + ai];
-      s_meta[2] = route[1 + E + ai];
-      s_meta[3] = route[1 + E + ai + 1];
-    }
-  }
-  __syncthreads();
-  if (ai >= s_meta[0]) return -1;
-  const int off = s_meta[2], cnt = s_meta[3] - s_meta[2];
-  for (int q = threadIdx.x; q < cnt; q += kThreads) s_slots[q] = (int16_t)route[2 + 2 * E + off + q];
-  __syncthreads();
-  return cnt;
-}
-
-__global__ __launch_bounds__(kThreads) void gateup_kernel(LayerArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
+void gateup_kernel(LayerArgs a) {
   __shared__ u32x4 xs[kXChunk * kVecH];
   __shared__ int16_t s_slots[kDecodeMaxT];
   __shared__ int s_meta[4];
   const int ai = blockIdx.x / kUnitsPerExpert;
   const int unit = blockIdx.x - ai * kUnitsPerExpert;
-  const int cnt = load_expert_slots(a, ai, s_slots, s_meta);
-  if (cnt < 0) return;
-  const int e = s_meta[1];
-  const uint16_t* w13 = reinterpret_cast<const uint16_t*>(a.routed.w13) + (size_t)e * 2 * I * H;
-  gateup_item(w13, unit * kPairsPerItem, cnt, TokenList{s_slots, a.k, 0}, a.x, a.ws.h, xs);
+  const int32_t* route = a.ws.route;
+  const int E = a.E;
+  // |U|, U[ai] and its slot range in one round trip (all in bounds: ai < E).
+  if (threadIdx.x == 0) {
+    s_meta[0] = route[0];
+    s_meta[1] = route[1 + ai];
+    s_meta[2] = route[1 + E + ai];
+    s_meta[3] = route[1 + E + ai + 1];
+  }
+  __syncthreads();
+  if (ai >= s_meta[0]) return;
+  const int e = s_meta[1], off = s_meta[2], cnt = s_meta[3] - s_meta[2];
+  GateUpRows wv;
+  load_gateup_weights(wv, reinterpret_cast<const uint16_t*>(a.routed.w13) + (size_t)e * 2 * I * H,
+                      unit * kPairsPerItem);
+  for (int q = threadIdx.x; q < cnt; q += kThreads) s_slots[q] = (int16_t)route[2 + 2 * E + off + q];
+  __syncthreads();
+  gateup_compute(wv, unit * kPairsPerItem, cnt, TokenList{s_slots, a.k, 0}, a.x, a.ws.h, xs);
 }
 
-__global__ __launch_bounds__(kThreads) void down_kernel(LayerArgs a) {
-  __shared__ float hs[kDownChunk * I];     // 32 KiB: h staging
-  __shared__ float ys[kDownChunk * kTileRows];
-  __shared__ int16_t s_slots[kDecodeMaxT];
-  __shared__ int s_meta[4];
-  __shared__ int s_flag;
-  const int ei = blockIdx.x / kTiles;      // 0: shared expert, 1 + ai: active index ai
-  const int tile = blockIdx.x - ei * kTiles;
-  const int T = a.T, k = a.k;
-  u32x4 wv[kRowsPerWave];
-  TokenList list{nullptr, k, T * k};
-  int cnt = T;
-  if (ei == 0) {
-    load_down_weights(wv, reinterpret_cast<const uint16_t*>(a.shared.w2), tile * kTileRows);
-    if (threadIdx.x == 0) s_meta[0] = a.ws.route[0];
-    __syncthreads();
+// Down + combine.  Block b owns output rows [8b, 8b + 8) of every token and
+// walks the |U| active experts and then the shared expert; wave w takes
+// items w, w + 8, ... and keeps the next item's rows in flight while it
+// reduces the current one.  Per (h row, output row) the 64-lane partial dot
+// products are summed in a fixed tree and parked in LDS; the block then
+// combines out = shared + sum_j w_j * routed_j in a fixed order.
+constexpr int kDownRowsPerBlock = 8;
+constexpr int kDownThreads = 512;
+constexpr int kDownWaves = kDownThreads / kWave;
+
+struct DownItem {
+  const uint16_t* w2;
+  int off, cnt;     // routed: slots[off, off + cnt); shared: cnt = T, off < 0
+};
+
+__device__ __forceinline__ DownItem down_item(const LayerArgs& a, int item, int n,
+                                              const int16_t* s_active, const int16_t* s_off) {
+  DownItem d;
+  if (item < n) {
+    d.w2 = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)s_active[item] * H * I;
+    d.off = s_off[item];
+    d.cnt = s_off[item + 1] - s_off[item];
   } else {
-    cnt = load_expert_slots(a, ei - 1, s_slots, s_meta);
-    if (cnt < 0) return;
-    load_down_weights(wv, reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)s_meta[1] * H * I,
-                      tile * kTileRows);
-    list.slots = s_slots;
+    d.w2 = reinterpret_cast<const uint16_t*>(a.shared.w2);
+    d.off = -1;
+    d.cnt = a.T;
   }
-  const int n_active = s_meta[0];
-  down_rows(wv, tile * kTileRows, cnt, list, a.ws.h, a.ws.y, hs, ys);
-  // The last of the |U| + 1 blocks of this row tile combines it.
-  if (last_block_ticket(a.ws.header + kHdrTileTicket + tile * kLine, (uint32_t)(n_active + 1), &s_flag))
-    combine_tile(a, tile * kTileRows);
+  return d;
+}
+
+__device__ __forceinline__ void load_w2_rows(u32x4 (&wv)[kDownRowsPerBlock], const uint16_t* w2, int r0) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int r = 0; r < kDownRowsPerBlock; ++r)
+    wv[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I)[lane];
+}
+
+__device__ __forceinline__ void down_item_rows(const LayerArgs& a, const DownItem& d,
+                                               u32x4 (&wv)[kDownRowsPerBlock],
+                                               const int16_t* s_slots, float* part) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int T = a.T, k = a.k;
+  for (int j = 0; j < d.cnt; ++j) {
+    const int hrow = d.off >= 0 ? s_slots[d.off + j] : T * k + j;
+    const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)hrow * I) + lane * 2;
+    const f32x4 h0 = hp[0], h1 = hp[1];
+    float acc[kDownRowsPerBlock];
+#pragma unroll
+    for (int r = 0; r < kDownRowsPerBlock; ++r) {
+      float v = bf16_lo(wv[r].x) * h0.x;
+      v = fmaf(bf16_hi(wv[r].x), h0.y, v);
+      v = fmaf(bf16_lo(wv[r].y), h0.z, v);
+      v = fmaf(bf16_hi(wv[r].y), h0.w, v);
+      v = fmaf(bf16_lo(wv[r].z), h1.x, v);
+      v = fmaf(bf16_hi(wv[r].z), h1.y, v);
+      v = fmaf(bf16_lo(wv[r].w), h1.z, v);
+      v = fmaf(bf16_hi(wv[r].w), h1.w, v);
+      acc[r] = wave_sum_lane63(v);
+    }
+    if (lane == kWave - 1)
+#pragma unroll
+      for (int r = 0; r < kDownRowsPerBlock; ++r) part[hrow * kDownRowsPerBlock + r] = acc[r];
+  }
+}
+
+__global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
+  __shared__ int16_t s_active[kMaxExperts];
+  __shared__ int16_t s_off[kMaxExperts + 1];
+  __shared__ int16_t s_slots[kDecodeMaxT * kMaxTopK];
+  __shared__ float part[(kMaxTopK + 1) * kDecodeMaxT * kDownRowsPerBlock];
+  const int wave = threadIdx.x / kWave;
+  const int r0 = blockIdx.x * kDownRowsPerBlock;
+  const int T = a.T, k = a.k, E = a.E;
+  const int32_t* route = a.ws.route;
+  // The routing table in one round trip (whole arrays, no dependence on |U|).
+  for (int q = threadIdx.x; q < E; q += kDownThreads) s_active[q] = (int16_t)route[1 + q];
+  for (int q = threadIdx.x; q <= E; q += kDownThreads) s_off[q] = (int16_t)route[1 + E + q];
+  for (int q = threadIdx.x; q < T * k; q += kDownThreads) s_slots[q] = (int16_t)route[2 + 2 * E + q];
+  const int n = route[0];
+  __syncthreads();
+
+  // Items 0..n-1: active experts; item n: the shared expert.
+  u32x4 wa[kDownRowsPerBlock], wb[kDownRowsPerBlock];
+  int item = wave;
+  DownItem da{}, db{};
+  if (item <= n) {
+    da = down_item(a, item, n, s_active, s_off);
+    load_w2_rows(wa, da.w2, r0);
+  }
+  while (item <= n) {
+    const int nx = item + kDownWaves;
+    if (nx <= n) {
+      db = down_item(a, nx, n, s_active, s_off);
+      load_w2_rows(wb, db.w2, r0);
+    }
+    down_item_rows(a, da, wa, s_slots, part);
+    if (nx > n) break;
+    const int nx2 = nx + kDownWaves;
+    if (nx2 <= n) {
+      da = down_item(a, nx2, n, s_active, s_off);
+      load_w2_rows(wa, da.w2, r0);
+    }
+    down_item_rows(a, db, wb, s_slots, part);
+    item = nx2;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < T * kDownRowsPerBlock; q += kDownThreads) {
+    const int t = q / kDownRowsPerBlock;
+    const int r = q - t * kDownRowsPerBlock;
+    float o = part[(T * k + t) * kDownRowsPerBlock + r];
+    for (int j = 0; j < k; ++j)
+      o = fmaf(a.ws.wts[t * k + j], part[(t * k + j) * kDownRowsPerBlock + r], o);
+    a.out[(size_t)t * H + r0 + r] = f32_to_bf16_rne(o);
+  }
 }
 
 }  // namespace
@@ -460,7 +460,7 @@ hipError_t launch_decode_bf16(const LayerArgs& a, hipStream_t stream, StageEvent
   e.mark(stream);
   hipLaunchKernelGGL(gateup_kernel, dim3(max_active * kUnitsPerExpert), dim3(kThreads), 0, stream, a);
   e.mark(stream);
-  hipLaunchKernelGGL(down_kernel, dim3((1 + max_active) * kTiles), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(down_kernel, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), 0, stream, a);
   e.mark(stream);
   return hipGetLastError();
 }

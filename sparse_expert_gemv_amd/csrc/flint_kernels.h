@@ -18,8 +18,7 @@ constexpr int kDecodeMaxT = 64;    // largest T taken by the GEMV (decode) kerne
 constexpr int kLine = 64;                       // words per 256-byte line
 constexpr int kHdrTokensDone = 0 * kLine;       // tokens whose selection is complete
 constexpr int kHdrTokTicket = 20 * kLine;       // [64 lines] router items done per token
-constexpr int kHdrTileTicket = 84 * kLine;      // [32 lines] down items done per output tile
-constexpr int kHeaderWords = 116 * kLine;       // 29 KiB
+constexpr int kHeaderWords = 84 * kLine;        // 21 KiB
 
 // Routing table (int32), written once per forward by the block that
 // finishes routing:
@@ -39,7 +38,6 @@ struct Workspace {
   float* wts;         // [T][k]
   int32_t* route;     // routing table (see above)
   float* h;           // [T*k + T][I]
-  float* y;           // [T*k + T][H]: per-slot down projections (unweighted)
   void* extra;
 };
 

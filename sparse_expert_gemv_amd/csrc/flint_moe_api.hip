@@ -39,7 +39,6 @@ void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L
   L->topk_w = o;   o = align_up(o + t * k * sizeof(float));
   L->route = o;    o = align_up(o + (size_t)flint::route_table_ints((int)E, T, (int)k) * sizeof(int32_t));
   L->h = o;        o = align_up(o + (t * k + t) * I * sizeof(float));
-  L->y = o;        o = align_up(o + (t * k + t) * H * sizeof(float));
   L->extra = o;
   L->total_bytes = o;
 }
@@ -184,7 +183,6 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.ws.wts = reinterpret_cast<float*>(ws + L.topk_w);
   a.ws.route = reinterpret_cast<int32_t*>(ws + L.route);
   a.ws.h = reinterpret_cast<float*>(ws + L.h);
-  a.ws.y = reinterpret_cast<float*>(ws + L.y);
   a.ws.extra = ws + L.extra;
   a.T = T;
   a.E = c.n_experts;

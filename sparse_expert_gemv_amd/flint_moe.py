@@ -26,7 +26,7 @@ FLINT_ERR_HIP = 4
 FLINT_W_BF16 = 0
 FLINT_W_NVFP4 = 1
 
-HEADER_BYTES = 29696  # FLINT_MOE_WS_HEADER_BYTES
+HEADER_BYTES = 21504  # FLINT_MOE_WS_HEADER_BYTES
 
 # Symbols the header declares; tests check the library exports each of them.
 ABI_SYMBOLS = (
@@ -62,7 +62,7 @@ class Weights(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("total_bytes", "header", "logits", "topk_ids", "topk_w",
-                 "route", "h", "y", "extra")]
+                 "route", "h", "extra")]
 
 
 class FlintError(RuntimeError):

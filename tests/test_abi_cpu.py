@@ -65,15 +65,14 @@ def test_workspace_sizes_grow_with_T():
     sizes = [m.workspace_bytes(T) for T in (1, 2, 8, 64)]
     assert sizes == sorted(sizes) and sizes[0] > sg.flint_moe.HEADER_BYTES
     lay = m.workspace_layout(8)
-    offs = [lay[k] for k in ("header", "logits", "topk_ids", "topk_w", "route", "h", "y",
-                             "extra")]
+    offs = [lay[k] for k in ("header", "logits", "topk_ids", "topk_w", "route", "h", "extra")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay["route"] + (2 + 2 * 256 + 8 * 6) * 4 <= lay["h"]
     assert lay["logits"] - lay["header"] >= sg.flint_moe.HEADER_BYTES
     hdr_decl = re.search(r"FLINT_MOE_WS_HEADER_BYTES\s+(\d+)",
                          open(os.path.join(ROOT, "include", "flint_moe.h")).read())
     assert int(hdr_decl.group(1)) == sg.flint_moe.HEADER_BYTES
-    assert lay["y"] + (8 * 6 + 8) * 2048 * 4 <= lay["total_bytes"]
+    assert lay["h"] + (8 * 6 + 8) * 512 * 4 <= lay["total_bytes"]
 
 
 def _fake_weights(base=1 << 20):
