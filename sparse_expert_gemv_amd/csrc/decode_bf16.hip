@@ -343,50 +343,68 @@ constexpr int kDownWaves = kDownThreads / kWave;
 struct DownItem {
   const uint16_t* w2;
   int off, cnt;     // routed: slots[off, off + cnt); shared: cnt = T, off < 0
+  int hrow0;        // h row of the first slot
 };
 
 __device__ __forceinline__ DownItem down_item(const LayerArgs& a, int item, int n,
-                                              const int16_t* s_active, const int16_t* s_off) {
+                                              const int16_t* s_active, const int16_t* s_off,
+                                              const int16_t* s_slots) {
   DownItem d;
   if (item < n) {
     d.w2 = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)s_active[item] * H * I;
     d.off = s_off[item];
     d.cnt = s_off[item + 1] - s_off[item];
+    d.hrow0 = s_slots[d.off];
   } else {
     d.w2 = reinterpret_cast<const uint16_t*>(a.shared.w2);
     d.off = -1;
     d.cnt = a.T;
+    d.hrow0 = a.T * a.k;
   }
   return d;
 }
 
-__device__ __forceinline__ void load_w2_rows(u32x4 (&wv)[kDownRowsPerBlock], const uint16_t* w2, int r0) {
+// An item's rows and its first slot's h, issued together ahead of use.
+struct DownPrefetch {
+  u32x4 w[kDownRowsPerBlock];
+  f32x4 h0, h1;
+};
+
+__device__ __forceinline__ void prefetch_item(DownPrefetch& p, const LayerArgs& a, const DownItem& d,
+                                              int r0) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int r = 0; r < kDownRowsPerBlock; ++r)
-    wv[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I)[lane];
+    p.w[r] = reinterpret_cast<const u32x4*>(d.w2 + (size_t)(r0 + r) * I)[lane];
+  const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)d.hrow0 * I) + lane * 2;
+  p.h0 = hp[0];
+  p.h1 = hp[1];
 }
 
 __device__ __forceinline__ void down_item_rows(const LayerArgs& a, const DownItem& d,
-                                               u32x4 (&wv)[kDownRowsPerBlock],
-                                               const int16_t* s_slots, float* part) {
+                                               DownPrefetch& p, const int16_t* s_slots, float* part) {
   const int lane = threadIdx.x & (kWave - 1);
   const int T = a.T, k = a.k;
+  f32x4 h0 = p.h0, h1 = p.h1;
   for (int j = 0; j < d.cnt; ++j) {
     const int hrow = d.off >= 0 ? s_slots[d.off + j] : T * k + j;
-    const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)hrow * I) + lane * 2;
-    const f32x4 h0 = hp[0], h1 = hp[1];
+    if (j > 0) {
+      const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)hrow * I) + lane * 2;
+      h0 = hp[0];
+      h1 = hp[1];
+    }
     float acc[kDownRowsPerBlock];
 #pragma unroll
     for (int r = 0; r < kDownRowsPerBlock; ++r) {
-      float v = bf16_lo(wv[r].x) * h0.x;
-      v = fmaf(bf16_hi(wv[r].x), h0.y, v);
-      v = fmaf(bf16_lo(wv[r].y), h0.z, v);
-      v = fmaf(bf16_hi(wv[r].y), h0.w, v);
-      v = fmaf(bf16_lo(wv[r].z), h1.x, v);
-      v = fmaf(bf16_hi(wv[r].z), h1.y, v);
-      v = fmaf(bf16_lo(wv[r].w), h1.z, v);
-      v = fmaf(bf16_hi(wv[r].w), h1.w, v);
+      const u32x4 w = p.w[r];
+      float v = bf16_lo(w.x) * h0.x;
+      v = fmaf(bf16_hi(w.x), h0.y, v);
+      v = fmaf(bf16_lo(w.y), h0.z, v);
+      v = fmaf(bf16_hi(w.y), h0.w, v);
+      v = fmaf(bf16_lo(w.z), h1.x, v);
+      v = fmaf(bf16_hi(w.z), h1.y, v);
+      v = fmaf(bf16_lo(w.w), h1.z, v);
+      v = fmaf(bf16_hi(w.w), h1.w, v);
       acc[r] = wave_sum_lane63(v);
     }
     if (lane == kWave - 1)
@@ -412,27 +430,27 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   __syncthreads();
 
   // Items 0..n-1: active experts; item n: the shared expert.
-  u32x4 wa[kDownRowsPerBlock], wb[kDownRowsPerBlock];
-  int item = wave;
+  DownPrefetch pa, pb;
   DownItem da{}, db{};
+  int item = wave;
   if (item <= n) {
-    da = down_item(a, item, n, s_active, s_off);
-    load_w2_rows(wa, da.w2, r0);
+    da = down_item(a, item, n, s_active, s_off, s_slots);
+    prefetch_item(pa, a, da, r0);
   }
   while (item <= n) {
     const int nx = item + kDownWaves;
     if (nx <= n) {
-      db = down_item(a, nx, n, s_active, s_off);
-      load_w2_rows(wb, db.w2, r0);
+      db = down_item(a, nx, n, s_active, s_off, s_slots);
+      prefetch_item(pb, a, db, r0);
     }
-    down_item_rows(a, da, wa, s_slots, part);
+    down_item_rows(a, da, pa, s_slots, part);
     if (nx > n) break;
     const int nx2 = nx + kDownWaves;
     if (nx2 <= n) {
-      da = down_item(a, nx2, n, s_active, s_off);
-      load_w2_rows(wa, da.w2, r0);
+      da = down_item(a, nx2, n, s_active, s_off, s_slots);
+      prefetch_item(pa, a, da, r0);
     }
-    down_item_rows(a, db, wb, s_slots, part);
+    down_item_rows(a, db, pb, s_slots, part);
     item = nx2;
   }
   __syncthreads();
