@@ -26,14 +26,19 @@ import time
 METRIC = "µs per MoE layer forward at T=1/8/32 + achieved HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
 H, E, K_TOP, I = 2048, 256, 6, 512
-EXPERT_W13_BYTES = 2 * I * H * 2           # 4,194,304
-EXPERT_W2_BYTES = H * I * 2                # 2,097,152
 ROUTER_BYTES = E * H * 2                   # 1,048,576
+# Algorithmic bytes of one expert's gate/up and down weights.
+EXPERT_BYTES = {
+    "bf16": (2 * I * H * 2, H * I * 2),                               # 4,194,304 + 2,097,152
+    "nvfp4": (2 * I * H // 2 + 2 * I * H // 16 + 4, H * I // 2 + H * I // 16 + 4),  # 1,179,652 + 589,828
+}
 
 WORKLOADS = {
-    "decode_t1": dict(T=1, bias=False),
-    "decode_t8": dict(T=8, bias=False),
-    "decode_t32_skewed": dict(T=32, bias=True),
+    "decode_t1": dict(T=1, bias=False, fmt="bf16"),
+    "decode_t8": dict(T=8, bias=False, fmt="bf16"),
+    "decode_t32_skewed": dict(T=32, bias=True, fmt="bf16"),
+    "decode_nvfp4_t1": dict(T=1, bias=False, fmt="nvfp4"),
+    "decode_nvfp4_t8": dict(T=8, bias=False, fmt="nvfp4"),
 }
 
 
@@ -96,26 +101,33 @@ def main():
 
     import sparse_expert_gemv_amd as sg
     from synth import SyntheticLayer, make_x
-    from synth.device import upload_bf16
+    from synth.device import nvfp4_layer, upload_bf16, upload_nvfp4
 
     wl = WORKLOADS[args.workload]
-    T, bias = wl["T"], wl["bias"]
+    T, bias, fmt = wl["T"], wl["bias"], wl["fmt"]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
     log(f"workload {args.workload}: generating seeded layer {args.seed}")
     syn = SyntheticLayer(args.seed)
     syn.routed_banks()
-    base = upload_bf16(syn, dev, with_bias=bias)
+    if fmt == "bf16":
+        base = upload_bf16(syn, dev, with_bias=bias)
+        bank = lambda t, n: (sg.DeviceBank(t["w13"], t["w2"]) if n == "routed"
+                             else sg.DeviceBank(t["sh_w13"], t["sh_w2"]))
+    else:
+        base = upload_nvfp4(syn, nvfp4_layer(syn), dev, with_bias=bias)
+        bank = lambda t, n: sg.DeviceBank(t[f"{n}_w13_q"], t[f"{n}_w2_q"], t[f"{n}_w13_s"],
+                                          t[f"{n}_w2_s"], t[f"{n}_w13_g"], t[f"{n}_w2_g"])
     copies = []
     for c in range(args.copies):
         t = base if c == 0 else {k: (None if v is None else v.clone()) for k, v in base.items()}
-        copies.append(sg.DeviceWeights(t["router_w"], t["router_b"], sg.DeviceBank(t["w13"], t["w2"]),
-                                       sg.DeviceBank(t["sh_w13"], t["sh_w2"])))
+        copies.append(sg.DeviceWeights(t["router_w"], t["router_b"], bank(t, "routed"),
+                                       bank(t, "shared")))
     torch.cuda.synchronize()
     log(f"{args.copies} layer copies resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
 
-    moe = sg.FlintMoE(max_tokens=max(T, 1))
+    moe = sg.FlintMoE(max_tokens=max(T, 1), fmt=sg.FLINT_W_BF16 if fmt == "bf16" else sg.FLINT_W_NVFP4)
     x_bits = make_x(T, seed=args.seed, x_seed=0)
     x = sg.bf16_tensor(x_bits, dev)
     out = torch.empty_like(x)
@@ -189,9 +201,10 @@ def main():
     us_step = ms_total * 1e3 / args.steps
     log(f"graph: {us_step:.2f} us/step over {args.steps} steps")
 
-    layer_bytes = ROUTER_BYTES + (n_active + 1) * (EXPERT_W13_BYTES + EXPERT_W2_BYTES) + 2 * T * H * 2
-    # Dominant kernel: the routed gate/up GEMV, |U| experts x 4 MiB of w13.
-    dom_bytes = n_active * EXPERT_W13_BYTES
+    w13_bytes, w2_bytes = EXPERT_BYTES[fmt]
+    layer_bytes = ROUTER_BYTES + (n_active + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 2
+    # Dominant kernel: the routed gate/up GEMV, |U| experts' gate/up weights.
+    dom_bytes = n_active * w13_bytes
     dom_us = float(kern_us[1])
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
 
@@ -214,7 +227,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if fmt == "bf16" else "nvfp4 weights (e2m1 + e4m3 scales), bf16 activations",
         "data": "synthetic",
         "config": {"workload": f"flint_moe_{args.workload}", "T": T, "hidden": H,
                    "n_experts": E, "top_k": K_TOP, "inter": I, "shared_experts": 1,

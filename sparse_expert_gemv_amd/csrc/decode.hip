@@ -1,4 +1,5 @@
-// Decode-sized (T <= 64) bf16 path of the Flint MoE layer on gfx950.
+// Decode-sized (T <= 64) path of the Flint MoE layer on gfx950, for bf16 and
+// NVFP4 (W4A16) expert weights.
 //
 // Three launches on the caller's stream, each cut into blocks that move
 // ~64 KiB of weights:
@@ -59,29 +60,86 @@ struct TokenList {
   __device__ __forceinline__ int hrow(int j) const { return slots ? slots[j] : base + j; }
 };
 
+// Gate/up rows of one wave: gate p, p+1 and up p, p+1 (p = p0 + 2 * wave);
+// lane l holds columns [8l + 512i, 8l + 512i + 8) of each row, i = 0..3.
+template <bool kFp4>
+struct GateUpRows;
+
+// bf16: 16 bytes per row per i.
+template <>
+struct GateUpRows<false> {
+  u32x4 w[4][kVecPerLaneH];
+  float g;  // tensor scale (1 for bf16)
+  __device__ __forceinline__ void load(const Bank& bank, int e, int p0) {
+    const uint16_t* w13 = reinterpret_cast<const uint16_t*>(bank.w13) + (size_t)e * 2 * I * H;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int p = p0 + 2 * (threadIdx.x / kWave);
+    const int row[4] = {p, p + 1, I + p, I + p + 1};
+#pragma unroll
+    for (int i = 0; i < kVecPerLaneH; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        w[r][i] = reinterpret_cast<const u32x4*>(w13 + (size_t)row[r] * H)[lane + i * kWave];
+    g = 1.0f;
+  }
+  __device__ __forceinline__ float dot(int r, int i, const u32x4& xv, float acc) const {
+    return dot8_bf16(w[r][i], xv, acc);
+  }
+  __device__ __forceinline__ void pin() {}
+};
+
+// NVFP4: 8 E2M1 codes (one 32-bit word) and their E4M3 block scale per row
+// per i; the codes convert exactly to bf16 and meet x in bf16 dot products,
+// the block scale multiplies each 8-element partial sum, the tensor scale
+// the row total.
+template <>
+struct GateUpRows<true> {
+  uint32_t q[4][kVecPerLaneH];
+  uint32_t sc[4][kVecPerLaneH];  // E4M3 byte
+  float g;
+  __device__ __forceinline__ void load(const Bank& bank, int e, int p0) {
+    const uint8_t* w13 = bank.w13 + (size_t)e * 2 * I * (H / 2);
+    const uint8_t* s13 = bank.w13_scale + (size_t)e * 2 * I * (H / 16);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int p = p0 + 2 * (threadIdx.x / kWave);
+    const int row[4] = {p, p + 1, I + p, I + p + 1};
+#pragma unroll
+    for (int i = 0; i < kVecPerLaneH; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        q[r][i] = reinterpret_cast<const uint32_t*>(w13 + (size_t)row[r] * (H / 2))[lane + i * kWave];
+        sc[r][i] = s13[(size_t)row[r] * (H / 16) + (lane * 8 + i * 512) / 16];
+      }
+    g = bank.w13_gscale[e];
+  }
+  __device__ __forceinline__ float dot(int r, int i, const u32x4& xv, float acc) const {
+    const uint32_t c = q[r][i];
+    float p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 0),
+                                              __builtin_bit_cast(bf16x2_t, xv.x), 0.f, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 1),
+                                        __builtin_bit_cast(bf16x2_t, xv.y), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 2),
+                                        __builtin_bit_cast(bf16x2_t, xv.z), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 3),
+                                        __builtin_bit_cast(bf16x2_t, xv.w), p, false);
+    return fmaf(p, __builtin_amdgcn_cvt_f32_fp8((int)sc[r][i], 0), acc);
+  }
+  // Keep the codes packed across tokens: widening every word once, outside
+  // the token loop, would need four times the registers.
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < kVecPerLaneH; ++i) asm volatile("" : "+v"(q[r][i]), "+v"(sc[r][i]));
+  }
+};
+
 // One block (4 waves) computes h = silu(gate) * up for the row pairs
-// [p0, p0 + 8) of one expert, for `count` tokens.  Wave w owns pairs
-// p0 + 2w and p0 + 2w + 1: four 4 KiB rows held in registers (loaded first,
-// so they are in flight while the token list is fetched) while the tokens'
+// [p0, p0 + 8) of one expert, for `count` tokens, with the wave's rows
+// already loaded (in flight while the token list was fetched); the tokens'
 // x vectors stream through LDS.
-typedef u32x4 GateUpRows[4][kVecPerLaneH];
-
-__device__ __forceinline__ void load_gateup_weights(GateUpRows& wv, const uint16_t* __restrict__ w13,
-                                                    int p0) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int p = p0 + 2 * (threadIdx.x / kWave);
-  const u32x4* rows[4] = {
-      reinterpret_cast<const u32x4*>(w13 + (size_t)p * H),
-      reinterpret_cast<const u32x4*>(w13 + (size_t)(p + 1) * H),
-      reinterpret_cast<const u32x4*>(w13 + (size_t)(I + p) * H),
-      reinterpret_cast<const u32x4*>(w13 + (size_t)(I + p + 1) * H)};
-#pragma unroll
-  for (int i = 0; i < kVecPerLaneH; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wv[r][i] = rows[r][lane + i * kWave];
-}
-
-__device__ __forceinline__ void gateup_compute(GateUpRows& wv, int p0, int count,
+template <bool kFp4>
+__device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int count,
                                                const TokenList& list, const uint16_t* __restrict__ x,
                                                float* h, u32x4* xs) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -96,15 +154,16 @@ __device__ __forceinline__ void gateup_compute(GateUpRows& wv, int p0, int count
     }
     __syncthreads();
     for (int j = 0; j < n; ++j) {
+      wv.pin();
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < kVecPerLaneH; ++i) {
         const u32x4 xv = xs[j * kVecH + lane + i * kWave];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = dot8_bf16(wv[r][i], xv, acc[r]);
+        for (int r = 0; r < 4; ++r) acc[r] = wv.dot(r, i, xv, acc[r]);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = wave_sum_lane63(acc[r]);
+      for (int r = 0; r < 4; ++r) acc[r] = wave_sum_lane63(acc[r]) * wv.g;
       if (lane == kWave - 1) {
         float* hr = h + (size_t)list.hrow(c0 + j) * I + p;
         hr[0] = silu(acc[0]) * acc[2];
@@ -289,6 +348,7 @@ __device__ void router_block(const LayerArgs& a, int rg, int item, int* s_flag, 
 constexpr int kRouteLdsVec = (2 * kMaxExperts * 4 + kMaxExperts * (kDecodeMaxT * kMaxTopK / 32) * 4) / 16;
 static_assert(kRouteLdsVec >= kXChunk * kVecH, "route LDS holds the x staging");
 
+template <bool kFp4>
 __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a, int rg, int n_router) {
   __shared__ u32x4 xs[kRouteLdsVec];
   __shared__ int s_flag;
@@ -297,12 +357,13 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a, int rg, in
   } else {
     // Shared expert gate/up: all T tokens, h rows T*k + t.
     const int unit = blockIdx.x - n_router;
-    GateUpRows wv;
-    load_gateup_weights(wv, reinterpret_cast<const uint16_t*>(a.shared.w13), unit * kPairsPerItem);
+    GateUpRows<kFp4> wv;
+    wv.load(a.shared, 0, unit * kPairsPerItem);
     gateup_compute(wv, unit * kPairsPerItem, a.T, TokenList{nullptr, a.k, a.T * a.k}, a.x, a.ws.h, xs);
   }
 }
 
+template <bool kFp4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void gateup_kernel(LayerArgs a) {
   __shared__ u32x4 xs[kXChunk * kVecH];
@@ -322,9 +383,8 @@ void gateup_kernel(LayerArgs a) {
   __syncthreads();
   if (ai >= s_meta[0]) return;
   const int e = s_meta[1], off = s_meta[2], cnt = s_meta[3] - s_meta[2];
-  GateUpRows wv;
-  load_gateup_weights(wv, reinterpret_cast<const uint16_t*>(a.routed.w13) + (size_t)e * 2 * I * H,
-                      unit * kPairsPerItem);
+  GateUpRows<kFp4> wv;
+  wv.load(a.routed, e, unit * kPairsPerItem);
   for (int q = threadIdx.x; q < cnt; q += kThreads) s_slots[q] = (int16_t)route[2 + 2 * E + off + q];
   __syncthreads();
   gateup_compute(wv, unit * kPairsPerItem, cnt, TokenList{s_slots, a.k, 0}, a.x, a.ws.h, xs);
@@ -332,16 +392,18 @@ void gateup_kernel(LayerArgs a) {
 
 // Down + combine.  Block b owns output rows [8b, 8b + 8) of every token and
 // walks the |U| active experts and then the shared expert; wave w takes
-// items w, w + 8, ... and keeps the next item's rows in flight while it
-// reduces the current one.  Per (h row, output row) the 64-lane partial dot
-// products are summed in a fixed tree and parked in LDS; the block then
+// items w, w + 8, ... and keeps the next item's rows (and its first slot's
+// h) in flight while it reduces the current one.  Lane l holds columns
+// [8l, 8l + 8) of each row.  Per (h row, output row) the 64-lane partial
+// dot products are summed in a fixed tree and parked in LDS; the block then
 // combines out = shared + sum_j w_j * routed_j in a fixed order.
 constexpr int kDownRowsPerBlock = 8;
 constexpr int kDownThreads = 512;
 constexpr int kDownWaves = kDownThreads / kWave;
 
 struct DownItem {
-  const uint16_t* w2;
+  int e;            // expert index in its bank
+  bool shared;
   int off, cnt;     // routed: slots[off, off + cnt); shared: cnt = T, off < 0
   int hrow0;        // h row of the first slot
 };
@@ -350,13 +412,14 @@ __device__ __forceinline__ DownItem down_item(const LayerArgs& a, int item, int 
                                               const int16_t* s_active, const int16_t* s_off,
                                               const int16_t* s_slots) {
   DownItem d;
-  if (item < n) {
-    d.w2 = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)s_active[item] * H * I;
+  d.shared = item >= n;
+  if (!d.shared) {
+    d.e = s_active[item];
     d.off = s_off[item];
     d.cnt = s_off[item + 1] - s_off[item];
     d.hrow0 = s_slots[d.off];
   } else {
-    d.w2 = reinterpret_cast<const uint16_t*>(a.shared.w2);
+    d.e = 0;
     d.off = -1;
     d.cnt = a.T;
     d.hrow0 = a.T * a.k;
@@ -364,25 +427,92 @@ __device__ __forceinline__ DownItem down_item(const LayerArgs& a, int item, int 
   return d;
 }
 
-// An item's rows and its first slot's h, issued together ahead of use.
-struct DownPrefetch {
+// The 8 rows of one item in a lane, plus the item's first slot's h.
+template <bool kFp4>
+struct DownRows;
+
+template <>
+struct DownRows<false> {
   u32x4 w[kDownRowsPerBlock];
   f32x4 h0, h1;
+  __device__ __forceinline__ void load(const LayerArgs& a, const DownItem& d, int r0) {
+    const Bank& bank = d.shared ? a.shared : a.routed;
+    const uint16_t* w2 = reinterpret_cast<const uint16_t*>(bank.w2) + (size_t)d.e * H * I;
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int r = 0; r < kDownRowsPerBlock; ++r)
+      w[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I)[lane];
+  }
+  __device__ __forceinline__ float scale() const { return 1.0f; }
+  // Lane partial of row r: its 8 columns of w2 . h.
+  __device__ __forceinline__ float partial(int r, const f32x4& a0, const f32x4& a1) const {
+    const u32x4 v = w[r];
+    float s = bf16_lo(v.x) * a0.x;
+    s = fmaf(bf16_hi(v.x), a0.y, s);
+    s = fmaf(bf16_lo(v.y), a0.z, s);
+    s = fmaf(bf16_hi(v.y), a0.w, s);
+    s = fmaf(bf16_lo(v.z), a1.x, s);
+    s = fmaf(bf16_hi(v.z), a1.y, s);
+    s = fmaf(bf16_lo(v.w), a1.z, s);
+    s = fmaf(bf16_hi(v.w), a1.w, s);
+    return s;
+  }
 };
 
-__device__ __forceinline__ void prefetch_item(DownPrefetch& p, const LayerArgs& a, const DownItem& d,
-                                              int r0) {
-  const int lane = threadIdx.x & (kWave - 1);
+// NVFP4: the lane's 8 columns are one 32-bit word of E2M1 codes, all in one
+// 16-element block (one E4M3 scale); codes widen exactly to fp32 so h keeps
+// full precision.
+template <>
+struct DownRows<true> {
+  uint32_t q[kDownRowsPerBlock];
+  uint32_t sc[kDownRowsPerBlock];
+  float g;
+  f32x4 h0, h1;
+  __device__ __forceinline__ void load(const LayerArgs& a, const DownItem& d, int r0) {
+    const Bank& bank = d.shared ? a.shared : a.routed;
+    const uint8_t* w2 = bank.w2 + (size_t)d.e * H * (I / 2);
+    const uint8_t* s2 = bank.w2_scale + (size_t)d.e * H * (I / 16);
+    const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-  for (int r = 0; r < kDownRowsPerBlock; ++r)
-    p.w[r] = reinterpret_cast<const u32x4*>(d.w2 + (size_t)(r0 + r) * I)[lane];
+    for (int r = 0; r < kDownRowsPerBlock; ++r) {
+      q[r] = reinterpret_cast<const uint32_t*>(w2 + (size_t)(r0 + r) * (I / 2))[lane];
+      sc[r] = s2[(size_t)(r0 + r) * (I / 16) + lane / 2];
+    }
+    g = bank.w2_gscale[d.e];
+  }
+  __device__ __forceinline__ float scale() const { return g; }
+  __device__ __forceinline__ float partial(int r, const f32x4& a0, const f32x4& a1) const {
+    const uint32_t c = q[r];
+    const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+    const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+    const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+    float s = p0.x * a0.x;
+    s = fmaf(p0.y, a0.y, s);
+    s = fmaf(p1.x, a0.z, s);
+    s = fmaf(p1.y, a0.w, s);
+    s = fmaf(p2.x, a1.x, s);
+    s = fmaf(p2.y, a1.y, s);
+    s = fmaf(p3.x, a1.z, s);
+    s = fmaf(p3.y, a1.w, s);
+    return s * __builtin_amdgcn_cvt_f32_fp8((int)sc[r], 0);
+  }
+};
+
+template <bool kFp4>
+__device__ __forceinline__ void prefetch_item(DownRows<kFp4>& p, const LayerArgs& a,
+                                              const DownItem& d, int r0) {
+  const int lane = threadIdx.x & (kWave - 1);
+  p.load(a, d, r0);
   const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)d.hrow0 * I) + lane * 2;
   p.h0 = hp[0];
   p.h1 = hp[1];
 }
 
+template <bool kFp4>
 __device__ __forceinline__ void down_item_rows(const LayerArgs& a, const DownItem& d,
-                                               DownPrefetch& p, const int16_t* s_slots, float* part) {
+                                               const DownRows<kFp4>& p, const int16_t* s_slots,
+                                               float* part) {
   const int lane = threadIdx.x & (kWave - 1);
   const int T = a.T, k = a.k;
   f32x4 h0 = p.h0, h1 = p.h1;
@@ -395,24 +525,14 @@ __device__ __forceinline__ void down_item_rows(const LayerArgs& a, const DownIte
     }
     float acc[kDownRowsPerBlock];
 #pragma unroll
-    for (int r = 0; r < kDownRowsPerBlock; ++r) {
-      const u32x4 w = p.w[r];
-      float v = bf16_lo(w.x) * h0.x;
-      v = fmaf(bf16_hi(w.x), h0.y, v);
-      v = fmaf(bf16_lo(w.y), h0.z, v);
-      v = fmaf(bf16_hi(w.y), h0.w, v);
-      v = fmaf(bf16_lo(w.z), h1.x, v);
-      v = fmaf(bf16_hi(w.z), h1.y, v);
-      v = fmaf(bf16_lo(w.w), h1.z, v);
-      v = fmaf(bf16_hi(w.w), h1.w, v);
-      acc[r] = wave_sum_lane63(v);
-    }
+    for (int r = 0; r < kDownRowsPerBlock; ++r) acc[r] = wave_sum_lane63(p.partial(r, h0, h1));
     if (lane == kWave - 1)
 #pragma unroll
-      for (int r = 0; r < kDownRowsPerBlock; ++r) part[hrow * kDownRowsPerBlock + r] = acc[r];
+      for (int r = 0; r < kDownRowsPerBlock; ++r) part[hrow * kDownRowsPerBlock + r] = acc[r] * p.scale();
   }
 }
 
+template <bool kFp4>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   __shared__ int16_t s_active[kMaxExperts];
   __shared__ int16_t s_off[kMaxExperts + 1];
@@ -430,7 +550,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   __syncthreads();
 
   // Items 0..n-1: active experts; item n: the shared expert.
-  DownPrefetch pa, pb;
+  DownRows<kFp4> pa, pb;
   DownItem da{}, db{};
   int item = wave;
   if (item <= n) {
@@ -466,21 +586,27 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const LayerArgs& a, hipStream_t stream, StageEvents* ev) {
+template <bool kFp4>
+static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, StageEvents* ev) {
   StageEvents none;
   StageEvents& e = ev ? *ev : none;
   const int rg = (a.E + kRouterRowsPerItem - 1) / kRouterRowsPerItem;
   const int n_router = a.T * rg;
   const int max_active = min(a.E, a.T * a.k);
   e.mark(stream);
-  hipLaunchKernelGGL(route_kernel, dim3(n_router + kUnitsPerExpert), dim3(kThreads), 0, stream, a, rg,
-                     n_router);
+  hipLaunchKernelGGL(route_kernel<kFp4>, dim3(n_router + kUnitsPerExpert), dim3(kThreads), 0, stream,
+                     a, rg, n_router);
   e.mark(stream);
-  hipLaunchKernelGGL(gateup_kernel, dim3(max_active * kUnitsPerExpert), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(gateup_kernel<kFp4>, dim3(max_active * kUnitsPerExpert), dim3(kThreads), 0, stream,
+                     a);
   e.mark(stream);
-  hipLaunchKernelGGL(down_kernel, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), 0, stream, a);
+  hipLaunchKernelGGL(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), 0, stream, a);
   e.mark(stream);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, StageEvents* ev) {
+  return a.nvfp4 ? launch_decode_impl<true>(a, stream, ev) : launch_decode_impl<false>(a, stream, ev);
 }
 
 }  // namespace flint

@@ -11,6 +11,7 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // a.lo*b.lo + a.hi*b.hi + c for two packed bf16 pairs, fp32 accumulate
 // (v_dot2c_f32_bf16).

@@ -77,6 +77,7 @@ struct StageEvents {
   }
 };
 
-hipError_t launch_decode_bf16(const LayerArgs& a, hipStream_t stream, StageEvents* ev);
+// The decode path (T <= kDecodeMaxT) for bf16 or NVFP4 expert weights.
+hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, StageEvents* ev);
 
 }  // namespace flint

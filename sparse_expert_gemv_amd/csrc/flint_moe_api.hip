@@ -82,10 +82,6 @@ flint_status check_config(const flint_moe_config& c, std::string* why) {
     *why = buf;
     return FLINT_ERR_UNSUPPORTED;
   }
-  if (c.format == FLINT_W_NVFP4) {
-    *why = "NVFP4 weights are not supported by this build";
-    return FLINT_ERR_UNSUPPORTED;
-  }
   return FLINT_OK;
 }
 
@@ -144,6 +140,15 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   const void* p16[] = {w->router_w, w->routed.w13, w->routed.w2, w->shared.w13, w->shared.w2, x, out};
   for (const void* p : p16)
     if (!aligned(p, 16)) return fail(ctx, FLINT_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (c.format == FLINT_W_NVFP4) {
+    const flint_expert_bank* banks[2] = {&w->routed, &w->shared};
+    for (const flint_expert_bank* b : banks) {
+      if (!b->w13_scale || !b->w2_scale || !b->w13_gscale || !b->w2_gscale)
+        return fail(ctx, FLINT_ERR_INVALID_ARG, "NVFP4 weights need block and tensor scales");
+      if (!aligned(b->w13_gscale, 4) || !aligned(b->w2_gscale, 4))
+        return fail(ctx, FLINT_ERR_INVALID_ARG, "tensor scales must be 4-byte aligned");
+    }
+  }
   if (w->router_b && !aligned(w->router_b, 4))
     return fail(ctx, FLINT_ERR_INVALID_ARG, "router_b must be 4-byte aligned");
   if ((topk_ids && !aligned(topk_ids, 4)) || (topk_w && !aligned(topk_w, 4)))
@@ -192,7 +197,7 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.nvfp4 = c.format == FLINT_W_NVFP4;
 
   (void)hipGetLastError();  // do not report an earlier, unrelated failure
-  const hipError_t err = flint::launch_decode_bf16(a, static_cast<hipStream_t>(stream), ev);
+  const hipError_t err = flint::launch_decode(a, static_cast<hipStream_t>(stream), ev);
   if (err != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(err));
   return FLINT_OK;
 }

@@ -30,22 +30,29 @@ def upload_bf16(syn: SyntheticLayer, device="cuda", with_bias: bool = False) -> 
     }
 
 
-def nvfp4_layer(syn: SyntheticLayer) -> dict:
+def nvfp4_layer(syn: SyntheticLayer, threads: int = 8) -> dict:
     """NVFP4 encoding of every routed expert and the shared expert (host arrays).
 
-    Keys: for bank in (routed, shared): packed/scale/gscale of w13 and w2,
-    stacked on a leading expert axis."""
+    Keys: for bank in (routed, shared): w13_q / w13_s / w13_g and w2_q / w2_s /
+    w2_g (packed codes, E4M3 block scales, fp32 tensor scale), stacked on a
+    leading expert axis."""
+    from concurrent.futures import ThreadPoolExecutor
     E = syn.shape.n_experts
     out = {}
     for name, ids in (("routed", list(range(E))), ("shared", [-1])):
-        parts = {k: [] for k in ("w13_q", "w13_s", "w13_g", "w2_q", "w2_s", "w2_g")}
-        for e in ids:
+        def enc(e):
             a, b = syn.expert(e)
-            qa, qb = quantize_nvfp4(a), quantize_nvfp4(b)
-            parts["w13_q"].append(qa.packed); parts["w13_s"].append(qa.scales); parts["w13_g"].append(qa.gscale)
-            parts["w2_q"].append(qb.packed); parts["w2_s"].append(qb.scales); parts["w2_g"].append(qb.gscale)
-        out[name] = {k: (np.stack(v) if k[-1] != "g" else np.array(v, dtype=np.float32))
-                     for k, v in parts.items()}
+            return quantize_nvfp4(a), quantize_nvfp4(b)
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            encs = list(ex.map(enc, ids))
+        out[name] = {
+            "w13_q": np.stack([qa.packed for qa, _ in encs]),
+            "w13_s": np.stack([qa.scales for qa, _ in encs]),
+            "w13_g": np.array([qa.gscale for qa, _ in encs], dtype=np.float32),
+            "w2_q": np.stack([qb.packed for _, qb in encs]),
+            "w2_s": np.stack([qb.scales for _, qb in encs]),
+            "w2_g": np.array([qb.gscale for _, qb in encs], dtype=np.float32),
+        }
     return out
 
 

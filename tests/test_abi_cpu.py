@@ -46,6 +46,7 @@ def test_status_strings():
     (dict(max_tokens=0), sg.FLINT_ERR_INVALID_ARG),
     (dict(routed_scale=float("nan")), sg.FLINT_ERR_INVALID_ARG),
     (dict(fmt=7), sg.FLINT_ERR_INVALID_ARG),
+    (dict(fmt=sg.FLINT_W_NVFP4, inter=1024), sg.FLINT_ERR_UNSUPPORTED),
 ])
 def test_init_rejects(kw, status):
     with pytest.raises(sg.FlintError) as e:
@@ -99,6 +100,10 @@ def test_forward_host_validation_without_gpu():
     bad.routed.w2 = None
     assert f(w=bad) == sg.FLINT_ERR_INVALID_ARG
     assert m.forward_raw(W, None, 0, None, None, None, None, 0, None) == sg.FLINT_OK
+    m4 = sg.FlintMoE(max_tokens=8, fmt=sg.FLINT_W_NVFP4)
+    need4 = m4.workspace_bytes(4)
+    assert m4.forward_raw(W, x, 4, out, None, None, ws, need4, None) == sg.FLINT_ERR_INVALID_ARG
+    assert "scales" in m4.last_error()
     lib = sg.load_library()
     assert lib.flint_moe_forward(None, None, None, 1, None, None, None, None, 0, None) == \
         sg.FLINT_ERR_INVALID_ARG

@@ -1,0 +1,100 @@
+"""GPU parity of the NVFP4 (W4A16) decode path against the fp64 oracle.
+
+Weights: the seeded bf16 layer encoded as E2M1 codes + E4M3 block scales
+(one per 16 K-elements) + an fp32 tensor scale.  The oracle evaluates the
+layer on the decoded weights (exact in fp64); the router, x and out stay
+bf16.  Tolerance: max |err| <= 5e-2 * RMS(oracle output).
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import OracleLayer, moe_forward  # noqa: E402
+from oracle.grading import TOL_NVFP4, grade  # noqa: E402
+from synth import SyntheticLayer, make_x  # noqa: E402
+from synth.device import nvfp4_layer, upload_nvfp4  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+SEED = 0
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev4():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_expert_gemv_amd as sg
+    say("generating and encoding the NVFP4 layer")
+    syn = SyntheticLayer(SEED)
+    syn.routed_banks()
+    q = nvfp4_layer(syn)
+    t = upload_nvfp4(syn, q, "cuda", with_bias=True)
+
+    def bank(name):
+        return sg.DeviceBank(t[f"{name}_w13_q"], t[f"{name}_w2_q"], t[f"{name}_w13_s"],
+                             t[f"{name}_w2_s"], t[f"{name}_w13_g"], t[f"{name}_w2_g"])
+
+    W = sg.DeviceWeights(t["router_w"], None, bank("routed"), bank("shared"))
+    Wb = sg.DeviceWeights(t["router_w"], t["router_b"], bank("routed"), bank("shared"))
+
+    def raw(e):
+        b, i = ("shared", 0) if e < 0 else ("routed", e)
+        d = q[b]
+        return ((d["w13_q"][i], d["w13_s"][i], d["w13_g"][i]),
+                (d["w2_q"][i], d["w2_s"][i], d["w2_g"][i]))
+
+    L = OracleLayer(2048, 256, 6, 512, syn.router_w(), None, raw, fmt="nvfp4")
+    Lb = OracleLayer(2048, 256, 6, 512, syn.router_w(), syn.router_bias(), raw, fmt="nvfp4")
+    L16 = OracleLayer(2048, 256, 6, 512, syn.router_w(), None, syn.expert)
+    return dict(sg=sg, W=W, Wb=Wb, L=L, Lb=Lb, L16=L16, t=t)
+
+
+def run4(dev4, xb, bias=False):
+    sg = dev4["sg"]
+    T = xb.shape[0]
+    moe = sg.FlintMoE(max_tokens=64, fmt=sg.FLINT_W_NVFP4)
+    x = sg.bf16_tensor(xb, "cuda")
+    out = torch.empty_like(x)
+    ids = torch.full((T, 6), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((T, 6), dtype=torch.float32, device="cuda")
+    moe.forward(dev4["Wb"] if bias else dev4["W"], x, out, ids, w)
+    torch.cuda.synchronize()
+    return sg.bf16_bits(out), ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,bias,x_seed", [(1, False, 0), (8, False, 0), (3, True, 1),
+                                           (13, False, 2), (64, True, 3)])
+def test_nvfp4_decode_matches_oracle(dev4, T, bias, x_seed):
+    say(f"nvfp4 parity T={T} bias={bias} x_seed={x_seed}")
+    xb = make_x(T, seed=SEED, x_seed=x_seed)
+    out, ids, w = run4(dev4, xb, bias)
+    res = moe_forward(dev4["Lb"] if bias else dev4["L"], xb)
+    g = grade(out, ids, res, tol=TOL_NVFP4)
+    print(g)
+    assert g.ok, str(g)
+    for t, r in enumerate(res):
+        if t not in g.excluded:
+            assert ids[t].tolist() == r.ids.tolist()
+            np.testing.assert_allclose(w[t], r.weights, rtol=2e-6, atol=1e-7)
+    if not bias:
+        ref16 = moe_forward(dev4["L16"], xb)
+        g16 = grade(out, ids, ref16, tol=1.0)
+        print(f"against the bf16 layer (reported, not graded): ratio={g16.ratio:.3f}")
+
+
+def test_nvfp4_rejects_missing_scales(dev4):
+    sg = dev4["sg"]
+    moe = sg.FlintMoE(max_tokens=8, fmt=sg.FLINT_W_NVFP4)
+    W = dev4["W"].struct()
+    W.routed.w13_scale = None
+    x = torch.zeros((1, 2048), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(x)
+    ws = moe.new_workspace(1, "cuda")
+    st = moe.forward_raw(W, x.data_ptr(), 1, out.data_ptr(), None, None, ws.data_ptr(),
+                         ws.numel(), None)
+    assert st == sg.FLINT_ERR_INVALID_ARG
