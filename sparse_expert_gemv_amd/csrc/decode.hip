@@ -113,15 +113,14 @@ struct GateUpRows<true> {
     g = bank.w13_gscale[e];
   }
   __device__ __forceinline__ float dot(int r, int i, const u32x4& xv, float acc) const {
+    // x words go through dot2_bf16's scalar parameters: bit-casting a vector
+    // element in place (bit_cast<bf16x2>(xv.y)) is miscompiled to element 0
+    // by the ROCm 7.2 clang used here.
     const uint32_t c = q[r][i];
-    float p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 0),
-                                              __builtin_bit_cast(bf16x2_t, xv.x), 0.f, false);
-    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 1),
-                                        __builtin_bit_cast(bf16x2_t, xv.y), p, false);
-    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 2),
-                                        __builtin_bit_cast(bf16x2_t, xv.z), p, false);
-    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 3),
-                                        __builtin_bit_cast(bf16x2_t, xv.w), p, false);
+    float p = dot2_bf16(fp4x2_to_bf16x2<0>(c), xv.x, 0.f);
+    p = dot2_bf16(fp4x2_to_bf16x2<1>(c), xv.y, p);
+    p = dot2_bf16(fp4x2_to_bf16x2<2>(c), xv.z, p);
+    p = dot2_bf16(fp4x2_to_bf16x2<3>(c), xv.w, p);
     return fmaf(p, __builtin_amdgcn_cvt_f32_fp8((int)sc[r][i], 0), acc);
   }
   // Keep the codes packed across tokens: widening every word once, outside

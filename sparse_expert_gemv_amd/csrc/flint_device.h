@@ -29,6 +29,13 @@ __device__ __forceinline__ float dot8_bf16(const u32x4& a, const u32x4& b, float
   return c;
 }
 
+// Byte kByte of c holds two E2M1 codes (low nibble first); returns them as a
+// packed bf16 pair (exact: every E2M1 value is a bf16 value).
+template <int kByte>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t c) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, kByte));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 

@@ -98,3 +98,29 @@ def test_nvfp4_rejects_missing_scales(dev4):
     st = moe.forward_raw(W, x.data_ptr(), 1, out.data_ptr(), None, None, ws.data_ptr(),
                          ws.numel(), None)
     assert st == sg.FLINT_ERR_INVALID_ARG
+
+
+def test_nvfp4_intermediate_h(dev4):
+    """h of every slot after the gate/up GEMV against the oracle's h."""
+    sg = dev4["sg"]
+    T = 2
+    say("nvfp4 intermediates T=2")
+    xb = make_x(T, seed=SEED, x_seed=5)
+    moe = sg.FlintMoE(max_tokens=64, fmt=sg.FLINT_W_NVFP4)
+    x = sg.bf16_tensor(xb, "cuda")
+    out = torch.empty_like(x)
+    ids = torch.full((T, 6), -1, dtype=torch.int32, device="cuda")
+    ws = moe.new_workspace(T, "cuda")
+    moe.forward(dev4["W"], x, out, ids, None, ws)
+    torch.cuda.synchronize()
+    lay = moe.workspace_layout(T)
+    h = ws[lay["h"]:lay["h"] + (T * 7) * 512 * 4].cpu().numpy().view(np.float32).reshape(T * 7, 512)
+    res = moe_forward(dev4["L"], xb)
+    for t, r in enumerate(res):
+        sc = np.max(np.abs(r.h_shared))
+        np.testing.assert_allclose(h[T * 6 + t], r.h_shared, rtol=0, atol=1e-4 * sc,
+                                   err_msg=f"shared h of token {t}")
+        for j in range(6):
+            sc = np.max(np.abs(r.h_routed[j]))
+            np.testing.assert_allclose(h[t * 6 + j], r.h_routed[j], rtol=0, atol=1e-4 * sc,
+                                       err_msg=f"routed h of token {t} rank {j}")
