@@ -39,7 +39,9 @@ WORKLOADS = {
     "decode_t32_skewed": dict(T=32, bias=True, fmt="bf16"),
     "decode_nvfp4_t1": dict(T=1, bias=False, fmt="nvfp4"),
     "decode_nvfp4_t8": dict(T=8, bias=False, fmt="nvfp4"),
+    "prefill_t8192": dict(T=8192, bias=False, fmt="bf16"),
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def log(msg):
@@ -52,7 +54,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_t8", choices=sorted(WORKLOADS))
-    p.add_argument("--copies", type=int, default=32, help="device copies of the layer")
+    p.add_argument("--copies", type=int, default=0,
+                   help="device copies of the layer (0: 32 for decode, 8 for prefill)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
                    help="CPU time budget of the oracle baseline (0 disables it)")
@@ -105,6 +108,8 @@ def main():
 
     wl = WORKLOADS[args.workload]
     T, bias, fmt = wl["T"], wl["bias"], wl["fmt"]
+    if args.copies <= 0:
+        args.copies = 8 if T > 64 else 32
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
@@ -172,7 +177,12 @@ def main():
     kern_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nk)]
                         for i in range(args.steps)])
     kern_us = kern_ms.mean(axis=0) * 1e3
-    names = ["route", "gateup", "down"][:nk] if nk == 3 else [f"kernel{i}" for i in range(nk)]
+    if nk == 3:
+        names = ["route", "gateup", "down"]
+    elif nk == 6:
+        names = ["router", "scan", "scatter", "gateup", "down", "shared_down_combine"]
+    else:
+        names = [f"kernel{i}" for i in range(nk)]
     log("eager per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_us)))
 
     # Timed region: one graph replay of exactly K steps.
@@ -203,10 +213,23 @@ def main():
 
     w13_bytes, w2_bytes = EXPERT_BYTES[fmt]
     layer_bytes = ROUTER_BYTES + (n_active + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 2
-    # Dominant kernel: the routed gate/up GEMV, |U| experts' gate/up weights.
-    dom_bytes = n_active * w13_bytes
-    dom_us = float(kern_us[1])
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    if T <= 64:
+        # Dominant kernel: the routed gate/up GEMV, |U| experts' gate/up weights.
+        dom_name, dom_bytes, dom_us = names[1], n_active * w13_bytes, float(kern_us[1])
+        achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+        roof = {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None, "algorithmic_bytes_per_launch": dom_bytes,
+                "avg_launch_us": round(dom_us, 3)}
+    else:
+        # Dominant kernel: the grouped gate/up GEMM, 2 * (T * 7) * 1024 * 2048 flops.
+        dom_name, dom_us = names[3], float(kern_us[3])
+        flops = 2.0 * T * (K_TOP + 1) * (2 * I) * H
+        achieved = flops / (dom_us * 1e-6) / 1e12
+        roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": flops, "avg_launch_us": round(dom_us, 3)}
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * 2**20
@@ -237,13 +260,10 @@ def main():
         "layer_algorithmic_bytes": layer_bytes,
         "layer_GBps": round(layer_bytes / (us_step * 1e-6) / 1e9, 1),
         "layer_hbm_frac": round(layer_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "layer_algorithmic_flops": 2.0 * T * E * H + 2.0 * T * (K_TOP + 1) * 3 * I * H,
         "kernels_us_eager": {n: round(float(v), 3) for n, v in zip(names, kern_us)},
         "eager_wall_us_per_step": round(eager_wall * 1e6, 2),
-        "roofline": {"kernel": names[0], "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": dom_bytes,
-                     "avg_launch_us": round(dom_us, 3)},
+        "roofline": roof,
     }
     if rank == 0 and args.cpu_baseline_seconds > 0:
         log("timing the oracle on the host")

@@ -12,6 +12,7 @@ constexpr int kInter = 512;        // I
 constexpr int kMaxExperts = 256;   // E upper bound (four router scores per lane)
 constexpr int kMaxTopK = 8;
 constexpr int kDecodeMaxT = 64;    // largest T taken by the GEMV (decode) kernels
+constexpr int kPrefillTile = 64;   // rows per grouped-GEMM tile (prefill-sized T)
 // Workspace header: uint32 completion counters, each on its own 256-byte
 // line so that tickets on one never queue behind atomics on another.  All
 // are zero before a forward starts and zero after it ends.
@@ -30,6 +31,16 @@ constexpr int kHeaderWords = 84 * kLine;        // 21 KiB
 //                            ascending within a group
 __host__ __device__ constexpr int route_table_ints(int E, int T, int k) { return 2 + 2 * E + T * k; }
 
+// Regions used only by the prefill-sized path.
+struct PrefillWs {
+  int32_t* counts;    // [nb][E]: slots per (64-token block, expert)
+  int32_t* base;      // [nb][E]: first sorted position of each (block, expert)
+  int32_t* tiles;     // [0] = routed tiles; then (expert, start, count) per tile
+  int32_t* pos;       // [T*k]: sorted position of slot s
+  _Float16* h16;      // [T*k + T][I]: h in sorted slot order, then the shared expert's
+  float* y32;         // [T*k][H]: unweighted down projection per sorted slot
+};
+
 // Workspace regions, as device pointers.
 struct Workspace {
   uint32_t* header;   // kHeaderWords counters (see above)
@@ -37,7 +48,8 @@ struct Workspace {
   int32_t* ids;       // [T][k]
   float* wts;         // [T][k]
   int32_t* route;     // routing table (see above)
-  float* h;           // [T*k + T][I]
+  float* h;           // [T*k + T][I] (decode-sized T)
+  PrefillWs pre;      // prefill-sized T
   void* extra;
 };
 
@@ -79,5 +91,9 @@ struct StageEvents {
 
 // The decode path (T <= kDecodeMaxT) for bf16 or NVFP4 expert weights.
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, StageEvents* ev);
+
+// The prefill path (T > kDecodeMaxT), bf16 expert weights.
+hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, StageEvents* ev);
+int prefill_tiles_max(int T, int E, int k);
 
 }  // namespace flint

@@ -28,6 +28,31 @@ static_assert(kHeaderBytes == FLINT_MOE_WS_HEADER_BYTES, "header size in flint_m
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Prefill regions inside the "extra" area; fills `p` relative to `base` when given.
+size_t prefill_extra_bytes(const flint_moe_config& c, int32_t T, flint::PrefillWs* p,
+                           uint8_t* base = nullptr) {
+  const size_t t = (size_t)T, E = (size_t)c.n_experts, k = (size_t)c.top_k, I = (size_t)c.inter,
+               H = (size_t)c.hidden;
+  const size_t nb = (t + flint::kPrefillTile - 1) / flint::kPrefillTile;
+  const size_t tiles = (size_t)flint::prefill_tiles_max(T, c.n_experts, c.top_k);
+  size_t o = 0;
+  const size_t counts = o; o = align_up(o + nb * E * sizeof(int32_t));
+  const size_t basep = o;  o = align_up(o + nb * E * sizeof(int32_t));
+  const size_t tl = o;     o = align_up(o + (1 + 3 * tiles) * sizeof(int32_t));
+  const size_t pos = o;    o = align_up(o + t * k * sizeof(int32_t));
+  const size_t h16 = o;    o = align_up(o + (t * k + t) * I * sizeof(uint16_t));
+  const size_t y32 = o;    o = align_up(o + t * k * H * sizeof(float));
+  if (p) {
+    p->counts = reinterpret_cast<int32_t*>(base + counts);
+    p->base = reinterpret_cast<int32_t*>(base + basep);
+    p->tiles = reinterpret_cast<int32_t*>(base + tl);
+    p->pos = reinterpret_cast<int32_t*>(base + pos);
+    p->h16 = reinterpret_cast<_Float16*>(base + h16);
+    p->y32 = reinterpret_cast<float*>(base + y32);
+  }
+  return o;
+}
+
 void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L) {
   const size_t t = (size_t)T, E = (size_t)c.n_experts, k = (size_t)c.top_k, I = (size_t)c.inter,
                H = (size_t)c.hidden;
@@ -38,8 +63,10 @@ void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L
   L->topk_ids = o; o = align_up(o + t * k * sizeof(int32_t));
   L->topk_w = o;   o = align_up(o + t * k * sizeof(float));
   L->route = o;    o = align_up(o + (size_t)flint::route_table_ints((int)E, T, (int)k) * sizeof(int32_t));
-  L->h = o;        o = align_up(o + (t * k + t) * I * sizeof(float));
+  const bool prefill = T > flint::kDecodeMaxT;
+  L->h = o;        o = align_up(o + (prefill ? 0 : (t * k + t) * I * sizeof(float)));
   L->extra = o;
+  if (prefill) o = L->extra + prefill_extra_bytes(c, T, nullptr);
   L->total_bytes = o;
 }
 
@@ -167,8 +194,9 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
                   L.total_bytes, T);
     return fail(ctx, FLINT_ERR_WORKSPACE, buf);
   }
-  if (T > flint::kDecodeMaxT)
-    return fail(ctx, FLINT_ERR_UNSUPPORTED, "T above the decode path's limit needs the prefill path");
+  const bool prefill = T > flint::kDecodeMaxT;
+  if (prefill && c.format != FLINT_W_BF16)
+    return fail(ctx, FLINT_ERR_UNSUPPORTED, "NVFP4 weights are supported for T <= 64 only");
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   flint::LayerArgs a{};
@@ -189,6 +217,7 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.ws.route = reinterpret_cast<int32_t*>(ws + L.route);
   a.ws.h = reinterpret_cast<float*>(ws + L.h);
   a.ws.extra = ws + L.extra;
+  if (prefill) prefill_extra_bytes(c, T, &a.ws.pre, ws + L.extra);
   a.T = T;
   a.E = c.n_experts;
   a.k = c.top_k;
@@ -197,7 +226,8 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.nvfp4 = c.format == FLINT_W_NVFP4;
 
   (void)hipGetLastError();  // do not report an earlier, unrelated failure
-  const hipError_t err = flint::launch_decode(a, static_cast<hipStream_t>(stream), ev);
+  const hipError_t err = prefill ? flint::launch_prefill(a, static_cast<hipStream_t>(stream), ev)
+                                 : flint::launch_decode(a, static_cast<hipStream_t>(stream), ev);
   if (err != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(err));
   return FLINT_OK;
 }

@@ -11,3 +11,30 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(scope="session")
+def flint_bf16():
+    """The seeded full-size bf16 layer on cuda:0, with its oracle (GPU tests only)."""
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_expert_gemv_amd as sg
+    from oracle import OracleLayer
+    from synth import SyntheticLayer
+    from synth.device import upload_bf16
+    print("[gpu-case] generating seeded layer 0", flush=True)
+    syn = SyntheticLayer(0)
+    syn.routed_banks()
+    t = upload_bf16(syn, "cuda", with_bias=True)
+    bank = sg.DeviceBank(t["w13"], t["w2"])
+    shared = sg.DeviceBank(t["sh_w13"], t["sh_w2"])
+    return dict(
+        sg=sg, syn=syn, t=t,
+        W=sg.DeviceWeights(t["router_w"], None, bank, shared),
+        Wb=sg.DeviceWeights(t["router_w"], t["router_b"], bank, shared),
+        L=OracleLayer(2048, 256, 6, 512, syn.router_w(), None, syn.expert),
+        Lb=OracleLayer(2048, 256, 6, 512, syn.router_w(), syn.router_bias(), syn.expert))

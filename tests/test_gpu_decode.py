@@ -9,10 +9,9 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from oracle import OracleLayer, bf16_to_f64, bucket, moe_forward  # noqa: E402
+from oracle import bucket, moe_forward  # noqa: E402
 from oracle.grading import TOL_BF16, grade  # noqa: E402
-from synth import SyntheticLayer, make_x  # noqa: E402
-from synth.device import upload_bf16  # noqa: E402
+from synth import make_x  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -24,21 +23,8 @@ def say(msg):
 
 
 @pytest.fixture(scope="module")
-def dev():
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import sparse_expert_gemv_amd as sg
-    say("generating seeded layer")
-    syn = SyntheticLayer(SEED)
-    syn.routed_banks()
-    t = upload_bf16(syn, "cuda", with_bias=True)
-    bank = sg.DeviceBank(t["w13"], t["w2"])
-    shared = sg.DeviceBank(t["sh_w13"], t["sh_w2"])
-    W = sg.DeviceWeights(t["router_w"], None, bank, shared)
-    Wb = sg.DeviceWeights(t["router_w"], t["router_b"], bank, shared)
-    L = OracleLayer(2048, 256, 6, 512, syn.router_w(), None, syn.expert)
-    Lb = OracleLayer(2048, 256, 6, 512, syn.router_w(), syn.router_bias(), syn.expert)
-    return dict(sg=sg, syn=syn, t=t, W=W, Wb=Wb, L=L, Lb=Lb)
+def dev(flint_bf16):
+    return flint_bf16
 
 
 def run(dev, x_bits, bias=False, renormalize=True, routed_scale=1.0, moe=None, ws=None):
