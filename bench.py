@@ -12,14 +12,23 @@ synchronisation and HIP events on the replay stream.  Per-kernel durations
 come from a separate eager pass of K steps that records HIP events between
 the kernels (flint_moe_forward_timed).
 
+Per-kernel durations for the roofline come from a second graph of the same
+K steps captured with HIP event nodes between the kernels.  The roofline's
+"traffic" (HBM bytes per launch of the dominant kernel) is read from the
+counter table in profiles/hbm_traffic.md when its row was measured on the
+kernel sources as they are now (SHA-256 of the path's .hip file and the two
+shared headers); otherwise it is null.
+
 Prints ONE JSON line.  Default workload: decode T=8 (bf16).
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -42,6 +51,36 @@ WORKLOADS = {
     "prefill_t8192": dict(T=8192, bias=False, fmt="bf16"),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "sparse_expert_gemv_amd", "csrc")
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def kernel_sources_sha(path_file: str) -> str:
+    """SHA-256 (first 16 hex digits) over a path's kernel source and the shared headers."""
+    h = hashlib.sha256()
+    for f in (path_file, "flint_device.h", "flint_kernels.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str, sha: str):
+    """HBM bytes per launch from the counter table, or None if absent or stale.
+
+    Table rows: | workload | kernel | sources sha | FETCH KiB | WRITE KiB | bytes |"""
+    try:
+        with open(TRAFFIC_TABLE) as fh:
+            for line in fh:
+                cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                if len(cells) >= 6 and cells[0] == workload and cells[1] == kernel:
+                    if cells[2] == sha and re.fullmatch(r"\d+", cells[5]):
+                        return int(cells[5])
+    except OSError:
+        pass
+    return None
 
 
 def log(msg):
@@ -177,6 +216,30 @@ def main():
     kern_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nk)]
                         for i in range(args.steps)])
     kern_us = kern_ms.mean(axis=0) * 1e3
+    # Per-kernel durations inside a graph: the same K steps captured with
+    # external event nodes between the kernels, replayed once untimed and
+    # once timed; kernel j of step i lasts evg[i][j] -> evg[i][j + 1].
+    evg = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    for row in evg:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    gk = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gk):
+        cap = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(args.steps):
+            st, _ = moe.forward_timed_raw(structs[i % len(structs)], ptrs[0], T, ptrs[1], ptrs[2],
+                                          ptrs[3], ptrs[4], ws_bytes, cap,
+                                          [e.cuda_event for e in evg[i]])
+            if st != sg.FLINT_OK:
+                raise sg.FlintError(st, moe.last_error())
+    gk.replay()
+    torch.cuda.synchronize()
+    gk.replay()
+    torch.cuda.synchronize()
+    kern_g_us = np.array([[evg[i][j].elapsed_time(evg[i][j + 1]) for j in range(nk)]
+                          for i in range(args.steps)]).mean(axis=0) * 1e3
+    del gk
     if nk == 3:
         names = ["route", "gateup", "down"]
     elif nk == 6:
@@ -184,6 +247,7 @@ def main():
     else:
         names = [f"kernel{i}" for i in range(nk)]
     log("eager per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_us)))
+    log("graph per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_g_us)))
 
     # Timed region: one graph replay of exactly K steps.
     g = torch.cuda.CUDAGraph()
@@ -211,24 +275,27 @@ def main():
     us_step = ms_total * 1e3 / args.steps
     log(f"graph: {us_step:.2f} us/step over {args.steps} steps")
 
+    sha = kernel_sources_sha("decode.hip" if T <= 64 else "prefill.hip")
     w13_bytes, w2_bytes = EXPERT_BYTES[fmt]
     layer_bytes = ROUTER_BYTES + (n_active + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 2
     if T <= 64:
         # Dominant kernel: the routed gate/up GEMV, |U| experts' gate/up weights.
-        dom_name, dom_bytes, dom_us = names[1], n_active * w13_bytes, float(kern_us[1])
+        dom_name, dom_bytes, dom_us = names[1], n_active * w13_bytes, float(kern_g_us[1])
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roof = {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": None, "algorithmic_bytes_per_launch": dom_bytes,
+                "traffic": measured_traffic(args.workload, dom_name, sha),
+                "algorithmic_bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_us, 3)}
     else:
         # Dominant kernel: the grouped gate/up GEMM, 2 * (T * 7) * 1024 * 2048 flops.
-        dom_name, dom_us = names[3], float(kern_us[3])
+        dom_name, dom_us = names[3], float(kern_g_us[3])
         flops = 2.0 * T * (K_TOP + 1) * (2 * I) * H
         achieved = flops / (dom_us * 1e-6) / 1e12
         roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(args.workload, dom_name, sha),
                 "algorithmic_flops_per_launch": flops, "avg_launch_us": round(dom_us, 3)}
 
     if args.calibrate_copy_mib:
@@ -261,6 +328,7 @@ def main():
         "layer_GBps": round(layer_bytes / (us_step * 1e-6) / 1e9, 1),
         "layer_hbm_frac": round(layer_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "layer_algorithmic_flops": 2.0 * T * E * H + 2.0 * T * (K_TOP + 1) * 3 * I * H,
+        "kernels_us_graph": {n: round(float(v), 3) for n, v in zip(names, kern_g_us)},
         "kernels_us_eager": {n: round(float(v), 3) for n, v in zip(names, kern_us)},
         "eager_wall_us_per_step": round(eager_wall * 1e6, 2),
         "roofline": roof,

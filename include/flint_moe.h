@@ -167,7 +167,9 @@ flint_status flint_moe_forward(flint_moe_ctx* ctx, const flint_moe_weights* w,
  * i is recorded on `stream` before kernel i of the chosen path and event
  * n_kernels after the last one, so (event i, event i+1) brackets kernel i.
  * *n_kernels receives the number of kernels the path launched.  Requires
- * n_events >= 8.  Same arguments, validation and results as
+ * n_events >= 8.  While `stream` is being captured into a graph the events
+ * are recorded as external event nodes, so each replay of the graph
+ * timestamps them.  Same arguments, validation and results as
  * flint_moe_forward otherwise. */
 flint_status flint_moe_forward_timed(flint_moe_ctx* ctx, const flint_moe_weights* w,
                                      const uint16_t* x, int32_t T, uint16_t* out,

@@ -84,8 +84,14 @@ struct StageEvents {
   hipEvent_t* events = nullptr;
   int n = 0;
   int used = 0;
+  // Inside stream capture the event becomes an external record node, so a
+  // replayed graph still timestamps the boundaries between the kernels.
   void mark(hipStream_t s) {
-    if (events && used < n) (void)hipEventRecord(events[used++], s);
+    if (!events || used >= n) return;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    (void)hipStreamIsCapturing(s, &st);
+    (void)hipEventRecordWithFlags(events[used++], s,
+                                  st == hipStreamCaptureStatusActive ? hipEventRecordExternal : 0);
   }
 };
 
