@@ -9,11 +9,11 @@ To measure HBM rather than the 256 MB Infinity Cache, the layer is cloned
 into several device copies and step i runs on copy i mod copies.  The K
 timed steps are captured in one HIP graph and replayed once, bracketed by
 synchronisation and HIP events on the replay stream.  Per-kernel durations
-come from a separate eager pass of K steps that records HIP events between
-the kernels (flint_moe_forward_timed).
+come from a separate eager pass of K steps in which each kernel is launched
+with a start and a stop event that take its own execution timestamps
+(flint_moe_forward_timed).
 
-Per-kernel durations for the roofline come from a second graph of the same
-K steps captured with HIP event nodes between the kernels.  The roofline's
+The roofline's
 "traffic" (HBM bytes per launch of the dominant kernel) is read from the
 counter table in profiles/hbm_traffic.md when its row was measured on the
 kernel sources as they are now (SHA-256 of the path's .hip file and the two
@@ -196,8 +196,9 @@ def main():
     n_active = int(np.unique(ids.cpu().numpy()).size)
     log(f"warmup done: |U| = {n_active}")
 
-    # Per-kernel durations: K eager steps with HIP events between the kernels.
-    n_ev = 8
+    # Per-kernel durations: K eager steps; each kernel's own start and end
+    # timestamps land in a pair of HIP events.
+    n_ev = 16
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
@@ -213,41 +214,16 @@ def main():
             raise sg.FlintError(st, moe.last_error())
     torch.cuda.synchronize()
     eager_wall = (time.perf_counter() - t0) / args.steps
-    kern_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nk)]
+    kern_ms = np.array([[evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for j in range(nk)]
                         for i in range(args.steps)])
     kern_us = kern_ms.mean(axis=0) * 1e3
-    # Per-kernel durations inside a graph: the same K steps captured with
-    # external event nodes between the kernels, replayed once untimed and
-    # once timed; kernel j of step i lasts evg[i][j] -> evg[i][j + 1].
-    evg = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    for row in evg:
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    gk = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gk):
-        cap = torch.cuda.current_stream(dev).cuda_stream
-        for i in range(args.steps):
-            st, _ = moe.forward_timed_raw(structs[i % len(structs)], ptrs[0], T, ptrs[1], ptrs[2],
-                                          ptrs[3], ptrs[4], ws_bytes, cap,
-                                          [e.cuda_event for e in evg[i]])
-            if st != sg.FLINT_OK:
-                raise sg.FlintError(st, moe.last_error())
-    gk.replay()
-    torch.cuda.synchronize()
-    gk.replay()
-    torch.cuda.synchronize()
-    kern_g_us = np.array([[evg[i][j].elapsed_time(evg[i][j + 1]) for j in range(nk)]
-                          for i in range(args.steps)]).mean(axis=0) * 1e3
-    del gk
     if nk == 3:
         names = ["route", "gateup", "down"]
     elif nk == 6:
         names = ["router", "scan", "scatter", "gateup", "down", "shared_down_combine"]
     else:
         names = [f"kernel{i}" for i in range(nk)]
-    log("eager per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_us)))
-    log("graph per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_g_us)))
+    log("per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_us)))
 
     # Timed region: one graph replay of exactly K steps.
     g = torch.cuda.CUDAGraph()
@@ -280,7 +256,7 @@ def main():
     layer_bytes = ROUTER_BYTES + (n_active + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 2
     if T <= 64:
         # Dominant kernel: the routed gate/up GEMV, |U| experts' gate/up weights.
-        dom_name, dom_bytes, dom_us = names[1], n_active * w13_bytes, float(kern_g_us[1])
+        dom_name, dom_bytes, dom_us = names[1], n_active * w13_bytes, float(kern_us[1])
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roof = {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -289,7 +265,7 @@ def main():
                 "avg_launch_us": round(dom_us, 3)}
     else:
         # Dominant kernel: the grouped gate/up GEMM, 2 * (T * 7) * 1024 * 2048 flops.
-        dom_name, dom_us = names[3], float(kern_g_us[3])
+        dom_name, dom_us = names[3], float(kern_us[3])
         flops = 2.0 * T * (K_TOP + 1) * (2 * I) * H
         achieved = flops / (dom_us * 1e-6) / 1e12
         roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
@@ -328,8 +304,9 @@ def main():
         "layer_GBps": round(layer_bytes / (us_step * 1e-6) / 1e9, 1),
         "layer_hbm_frac": round(layer_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "layer_algorithmic_flops": 2.0 * T * E * H + 2.0 * T * (K_TOP + 1) * 3 * I * H,
-        "kernels_us_graph": {n: round(float(v), 3) for n, v in zip(names, kern_g_us)},
-        "kernels_us_eager": {n: round(float(v), 3) for n, v in zip(names, kern_us)},
+        "kernels_us": {n: round(float(v), 3) for n, v in zip(names, kern_us)},
+        "kernel_timing": "start/stop timestamps of each kernel's execution (hipExtLaunchKernelGGL "
+                         "events), averaged over K eager steps",
         "eager_wall_us_per_step": round(eager_wall * 1e6, 2),
         "roofline": roof,
     }

@@ -163,14 +163,13 @@ flint_status flint_moe_forward(flint_moe_ctx* ctx, const flint_moe_weights* w,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* flint_moe_forward with per-kernel timing, for measurement.  `events` holds
- * n_events hipEvent_t handles (passed as void*) created by the caller; event
- * i is recorded on `stream` before kernel i of the chosen path and event
- * n_kernels after the last one, so (event i, event i+1) brackets kernel i.
- * *n_kernels receives the number of kernels the path launched.  Requires
- * n_events >= 8.  While `stream` is being captured into a graph the events
- * are recorded as external event nodes, so each replay of the graph
- * timestamps them.  Same arguments, validation and results as
- * flint_moe_forward otherwise. */
+ * n_events hipEvent_t handles (passed as void*, created by the caller with
+ * timing enabled).  Kernel i of the chosen path is launched with events
+ * 2i and 2i+1 as its start and stop events (hipExtLaunchKernelGGL), so they
+ * take the start and end timestamps of that kernel's own execution.
+ * *n_kernels receives the number of kernels the path launched (at most 8).
+ * Requires n_events >= 16.  Not for use under stream capture.  Same
+ * arguments, validation and results as flint_moe_forward otherwise. */
 flint_status flint_moe_forward_timed(flint_moe_ctx* ctx, const flint_moe_weights* w,
                                      const uint16_t* x, int32_t T, uint16_t* out,
                                      int32_t* topk_ids, float* topk_w, void* workspace,

@@ -586,26 +586,19 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
 }  // namespace
 
 template <bool kFp4>
-static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, StageEvents* ev) {
-  StageEvents none;
-  StageEvents& e = ev ? *ev : none;
+static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
   const int rg = (a.E + kRouterRowsPerItem - 1) / kRouterRowsPerItem;
   const int n_router = a.T * rg;
   const int max_active = min(a.E, a.T * a.k);
-  e.mark(stream);
-  hipLaunchKernelGGL(route_kernel<kFp4>, dim3(n_router + kUnitsPerExpert), dim3(kThreads), 0, stream,
-                     a, rg, n_router);
-  e.mark(stream);
-  hipLaunchKernelGGL(gateup_kernel<kFp4>, dim3(max_active * kUnitsPerExpert), dim3(kThreads), 0, stream,
-                     a);
-  e.mark(stream);
-  hipLaunchKernelGGL(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), 0, stream, a);
-  e.mark(stream);
+  launch(route_kernel<kFp4>, dim3(n_router + kUnitsPerExpert), dim3(kThreads), stream, a, rg, n_router);
+  launch(gateup_kernel<kFp4>, dim3(max_active * kUnitsPerExpert), dim3(kThreads), stream, a);
+  launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, StageEvents* ev) {
-  return a.nvfp4 ? launch_decode_impl<true>(a, stream, ev) : launch_decode_impl<false>(a, stream, ev);
+hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
+  return a.nvfp4 ? launch_decode_impl<true>(a, stream, launch)
+                 : launch_decode_impl<false>(a, stream, launch);
 }
 
 }  // namespace flint

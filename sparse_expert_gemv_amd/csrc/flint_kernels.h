@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -78,28 +79,29 @@ struct LayerArgs {
   int nvfp4;
 };
 
-// Optional per-kernel timing: records events[used++] on the stream before each
-// kernel and once after the last (see flint_moe_forward_timed).
-struct StageEvents {
+// Launches the path's kernels.  With timing events, kernel i is launched with
+// hipExtLaunchKernelGGL so that events[2i] and events[2i+1] take the start and
+// end timestamps of that kernel's own execution (see flint_moe_forward_timed).
+struct Launcher {
   hipEvent_t* events = nullptr;
   int n = 0;
-  int used = 0;
-  // Inside stream capture the event becomes an external record node, so a
-  // replayed graph still timestamps the boundaries between the kernels.
-  void mark(hipStream_t s) {
-    if (!events || used >= n) return;
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    (void)hipStreamIsCapturing(s, &st);
-    (void)hipEventRecordWithFlags(events[used++], s,
-                                  st == hipStreamCaptureStatusActive ? hipEventRecordExternal : 0);
+  int used = 0;   // kernels launched so far
+  template <typename F, typename... Args>
+  void operator()(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+    if (events && 2 * used + 1 < n)
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, s, events[2 * used], events[2 * used + 1], 0,
+                            args...);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+    ++used;
   }
 };
 
 // The decode path (T <= kDecodeMaxT) for bf16 or NVFP4 expert weights.
-hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, StageEvents* ev);
+hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, Launcher& launch);
 
 // The prefill path (T > kDecodeMaxT), bf16 expert weights.
-hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, StageEvents* ev);
+hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& launch);
 int prefill_tiles_max(int T, int E, int k);
 
 }  // namespace flint

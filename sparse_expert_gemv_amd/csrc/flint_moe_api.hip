@@ -150,7 +150,7 @@ namespace {
 flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const uint16_t* x,
                           int32_t T, uint16_t* out, int32_t* topk_ids, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* stream,
-                          flint::StageEvents* ev) {
+                          flint::Launcher& launch) {
   if (!ctx) return FLINT_ERR_INVALID_ARG;
   ctx->last_error.clear();
   const flint_moe_config& c = ctx->cfg;
@@ -226,8 +226,8 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.nvfp4 = c.format == FLINT_W_NVFP4;
 
   (void)hipGetLastError();  // do not report an earlier, unrelated failure
-  const hipError_t err = prefill ? flint::launch_prefill(a, static_cast<hipStream_t>(stream), ev)
-                                 : flint::launch_decode(a, static_cast<hipStream_t>(stream), ev);
+  const hipError_t err = prefill ? flint::launch_prefill(a, static_cast<hipStream_t>(stream), launch)
+                                 : flint::launch_decode(a, static_cast<hipStream_t>(stream), launch);
   if (err != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(err));
   return FLINT_OK;
 }
@@ -238,8 +238,9 @@ FLINT_API flint_status flint_moe_forward(flint_moe_ctx* ctx, const flint_moe_wei
                                          const uint16_t* x, int32_t T, uint16_t* out,
                                          int32_t* topk_ids, float* topk_w, void* workspace,
                                          size_t workspace_bytes, void* stream) {
+  flint::Launcher launch;
   return forward_impl(ctx, w, x, T, out, topk_ids, topk_w, workspace, workspace_bytes, stream,
-                      nullptr);
+                      launch);
 }
 
 FLINT_API flint_status flint_moe_forward_timed(flint_moe_ctx* ctx, const flint_moe_weights* w,
@@ -249,16 +250,16 @@ FLINT_API flint_status flint_moe_forward_timed(flint_moe_ctx* ctx, const flint_m
                                                void* const* events, int32_t n_events,
                                                int32_t* n_kernels) {
   if (!ctx) return FLINT_ERR_INVALID_ARG;
-  if (!events || n_events < 8 || !n_kernels)
-    return fail(ctx, FLINT_ERR_INVALID_ARG, "events (>= 8) and n_kernels are required");
+  if (!events || n_events < 16 || !n_kernels)
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "events (>= 16) and n_kernels are required");
   for (int i = 0; i < n_events; ++i)
     if (!events[i]) return fail(ctx, FLINT_ERR_INVALID_ARG, "NULL event handle");
-  flint::StageEvents ev;
-  ev.events = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
-  ev.n = n_events;
+  flint::Launcher launch;
+  launch.events = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  launch.n = n_events;
   const flint_status s = forward_impl(ctx, w, x, T, out, topk_ids, topk_w, workspace,
-                                      workspace_bytes, stream, &ev);
-  *n_kernels = ev.used > 0 ? ev.used - 1 : 0;
+                                      workspace_bytes, stream, launch);
+  *n_kernels = launch.used;
   return s;
 }
 

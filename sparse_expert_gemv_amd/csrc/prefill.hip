@@ -465,30 +465,19 @@ int prefill_tiles_max(int T, int E, int k) {
   return (T * k + kMT - 1) / kMT + E;  // sum over experts of ceil(count / 64)
 }
 
-hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, StageEvents* ev) {
-  StageEvents none;
-  StageEvents& e = ev ? *ev : none;
+hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
   const int nb = (a.T + kMT - 1) / kMT;
   const int n_routed_max = prefill_tiles_max(a.T, a.E, a.k);
   const int n_shared = nb;
-  e.mark(stream);
-  hipLaunchKernelGGL(prefill_router_kernel, dim3(nb), dim3(kThreads), 0, stream, a);
-  e.mark(stream);
-  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(kThreads), 0, stream, a, nb);
-  e.mark(stream);
-  hipLaunchKernelGGL(prefill_scatter_kernel, dim3(nb), dim3(kThreads), 0, stream, a);
-  e.mark(stream);
+  launch(prefill_router_kernel, dim3(nb), dim3(kThreads), stream, a);
+  launch(prefill_scan_kernel, dim3(1), dim3(kThreads), stream, a, nb);
+  launch(prefill_scatter_kernel, dim3(nb), dim3(kThreads), stream, a);
   const int n_gu = (n_shared + n_routed_max) * 4;
-  hipLaunchKernelGGL(prefill_gateup_kernel, dim3(round8(n_gu)), dim3(kThreads), 0, stream, a, n_shared,
-                     n_gu);
-  e.mark(stream);
+  launch(prefill_gateup_kernel, dim3(round8(n_gu)), dim3(kThreads), stream, a, n_shared, n_gu);
   const int n_dn = n_routed_max * 8;
-  hipLaunchKernelGGL(prefill_down_kernel, dim3(round8(n_dn)), dim3(kThreads), 0, stream, a, n_dn);
-  e.mark(stream);
+  launch(prefill_down_kernel, dim3(round8(n_dn)), dim3(kThreads), stream, a, n_dn);
   const int n_sc = n_shared * 8;
-  hipLaunchKernelGGL(prefill_shared_combine_kernel, dim3(round8(n_sc)), dim3(kThreads), 0, stream, a,
-                     n_sc);
-  e.mark(stream);
+  launch(prefill_shared_combine_kernel, dim3(round8(n_sc)), dim3(kThreads), stream, a, n_sc);
   return hipGetLastError();
 }
 
