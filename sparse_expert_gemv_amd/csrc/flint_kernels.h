@@ -13,7 +13,8 @@ constexpr int kInter = 512;        // I
 constexpr int kMaxExperts = 256;   // E upper bound (four router scores per lane)
 constexpr int kMaxTopK = 8;
 constexpr int kDecodeMaxT = 64;    // largest T taken by the GEMV (decode) kernels
-constexpr int kPrefillTile = 64;   // rows per grouped-GEMM tile (prefill-sized T)
+constexpr int kPrefillTile = 64;   // tokens per router / scatter block (prefill-sized T)
+constexpr int kGroupTile = 128;    // slots per grouped-GEMM M-tile (prefill-sized T)
 // Workspace header: uint32 completion counters, each on its own 256-byte
 // line so that tickets on one never queue behind atomics on another.  All
 // are zero before a forward starts and zero after it ends.
@@ -36,10 +37,10 @@ __host__ __device__ constexpr int route_table_ints(int E, int T, int k) { return
 struct PrefillWs {
   int32_t* counts;    // [nb][E]: slots per (64-token block, expert)
   int32_t* base;      // [nb][E]: first sorted position of each (block, expert)
-  int32_t* tiles;     // [0] = routed tiles; then (expert, start, count) per tile
+  int32_t* tiles;     // [0] = routed tiles; then (expert, start, count) per 128-slot tile
   int32_t* pos;       // [T*k]: sorted position of slot s
   _Float16* h16;      // [T*k + T][I]: h in sorted slot order, then the shared expert's
-  float* y32;         // [T*k][H]: unweighted down projection per sorted slot
+  _Float16* y16;      // [T*k][H]: unweighted down projection per sorted slot
 };
 
 // Workspace regions, as device pointers.

@@ -8,7 +8,7 @@
 //                accumulate, + bias), top-k per token by sigmoid score, the
 //                routing weights, and the block's per-expert slot counts.
 //   2. scan    : one block turns the counts into expert offsets, the routing
-//                table (U ascending) and the grouped-GEMM tile list (64 slots
+//                table (U ascending) and the grouped-GEMM tile list (128 slots
 //                per tile, no padding stored).
 //   3. scatter : stable counting sort of the (token, rank) slots by expert,
 //                ascending slot order within an expert; the inverse
@@ -18,15 +18,22 @@
 //                mul in registers, h stored as fp16 in sorted slot order (the
 //                shared expert's tiles cover tokens in order).
 //   5. down    : grouped GEMM per (routed expert tile, 256 output columns):
-//                h (fp16) times w2 (bf16 widened to fp16 in registers, exact
-//                for |w| >= 2^-14) into fp32 y per slot.
-//   6. shared down + combine : the shared expert's down GEMM per (64 tokens,
+//                h (fp16) times w2 (bf16 converted to fp16 on its way into
+//                LDS, exact for |w| >= 2^-14) into fp16 y per slot.
+//   6. shared down + combine : the shared expert's down GEMM per (128 tokens,
 //                256 columns) whose epilogue adds sum_j w_j * y_j in rank order
 //                and rounds once to bf16.
-// Numerics: fp32 accumulation everywhere; h is fp16 (11-bit significand) and
-// y is fp32, so the only roundings of the decode path's fp32 arithmetic that
-// this path adds are those of h to fp16 and of tiny w2 values to fp16
-// subnormals.
+// All GEMMs share one block-level scheme: 256 threads (4 waves); A and B
+// tiles move from global memory straight into LDS (LDS-direct loads, no
+// register staging) 32 K-elements at a time through a three-stage ring, so
+// two stages' loads are in flight while the third feeds the matrix cores;
+// 64-byte LDS rows with their 16-byte chunks XOR-swizzled by row, so that
+// the fragment reads of 16 consecutive rows hit distinct banks; each wave
+// owns a 64x128 (or 64x64) tile of 32x32x16 MFMAs.
+// Numerics: fp32 accumulation everywhere; h and y are stored as fp16 (11-bit
+// significand), so the roundings this path adds to the decode path's fp32
+// arithmetic are those of h and y to fp16 and of tiny w2 values to fp16
+// subnormals.  h and y must stay within fp16's range (|v| < 65504).
 //
 // What is computed follows "vLLM Day-0 Support for Recursive's Flint"
 // (section "Flint Model Architecture", bullet "MoE Structure"; section
@@ -45,7 +52,8 @@ namespace {
 constexpr int H = kHidden;
 constexpr int I = kInter;
 constexpr int kThreads = 256;
-constexpr int kMT = kPrefillTile;   // rows (slots or tokens) per M-tile
+constexpr int kMT = kPrefillTile;   // tokens per router / scatter block
+constexpr int kGM = kGroupTile;     // slots per grouped-GEMM M-tile
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -73,58 +81,154 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& v) {
   r.w = pack_f16x2(bf16_lo(v.w), bf16_hi(v.w));
   return r;
 }
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// A wave's 64x64 tile: two 32-row tiles (rt) x two 32-column tiles (ct).
-// MFMA 32x32x16 lane layout: lane l feeds row/column l % 32 with K elements
-// [(l / 32) * 8, +8) of each 16-wide K step; accumulator element r of lane l
-// is row (r / 4) * 8 + (l / 32) * 4 + r % 4, column l % 32.
-struct Tile64 {
-  f32x16 acc[2][2];
-  __device__ __forceinline__ void zero() {
+// Accumulator element r of lane l in a 32x32 MFMA tile: row (r / 4) * 8 +
+// (l / 32) * 4 + r % 4, column l % 32.  A and B operands: lane l supplies row
+// (column) l % 32 with K elements [(l / 32) * 8, +8) of each 16-wide K step.
+__device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
+
+// Waits until at most n vector-memory operations of this wave are
+// outstanding (the LDS-direct loads below count as vector-memory operations
+// until their data has landed in LDS).
+template <int n>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
+}
+// Workgroup barrier that is also a compiler barrier for memory operations.
+// Unlike __syncthreads it does not wait for this wave's outstanding loads,
+// so loads of later pipeline stages stay in flight across it; the caller
+// waits for exactly the stage it needs first (wait_vmem).
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Block GEMM C[BM x BN] = A[BM x K] B[BN x K]^T with both operands K-
+// contiguous in global memory, fed through an S-stage LDS ring of 32-wide K
+// chunks.  Global -> LDS moves are LDS-direct loads (global_load_lds, 16
+// bytes per lane): one instruction of a wave fills 16 consecutive 64-byte
+// LDS rows, lane i writing 16-byte chunk i % 4 of row i / 4.  Within a row
+// the four 16-byte K chunks are XOR-swizzled by swz(row), which spreads the
+// MFMA fragment reads of consecutive rows over all LDS banks; each lane
+// therefore fetches the K chunk that belongs at its physical slot.  Thread
+// (wave w, lane i) fetches A rows (w * NA + j) * 16 + i / 4 and B rows
+// (w * NB + j) * 16 + i / 4; the caller hands over one global pointer per
+// such row, already advanced by chunk_elems(row) elements (fetch_row_a/b and
+// chunk_elems give the mapping).  Waves form a WM x WN grid; each owns a
+// (BM / WM) x (BN / WN) tile of 32x32x16 MFMAs.  kF16: A is fp16 and B (bf16
+// in memory) is converted to fp16 in registers before the MFMA; otherwise
+// both are bf16.
+template <int BM, int BN, int WM, int WN, bool kF16, int S>
+struct BlockGemm {
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int RT = TM / 32, CT = TN / 32;
+  static constexpr int NA = BM / 64, NB = BN / 64;   // LDS-direct loads per thread per stage
+  static constexpr int NL = NA + NB;
+  static constexpr int kKC = 32;                     // K elements per stage
+  static constexpr int kRow = kKC * 2;               // LDS bytes per row
+  static constexpr int kStage = (BM + BN) * kRow;
+  static constexpr int kLds = S * kStage;
+  static_assert(WM * WN == kThreads / 64, "one wave per tile");
+  static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % 64 == 0 && BN % 64 == 0, "tile shape");
+  static_assert(S >= 2 && (S - 2) * NL < 64, "pipeline depth");
+
+  f32x16 acc[RT][CT];
+
+  __device__ static __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+  __device__ static __forceinline__ int fetch_row_a(int j) {
+    return ((threadIdx.x >> 6) * NA + j) * 16 + ((threadIdx.x & 63) >> 2);
+  }
+  __device__ static __forceinline__ int fetch_row_b(int j) {
+    return ((threadIdx.x >> 6) * NB + j) * 16 + ((threadIdx.x & 63) >> 2);
+  }
+  __device__ static __forceinline__ int chunk_elems(int row) { return ((threadIdx.x & 3) ^ swz(row)) * 8; }
+
+  // rt_n: 32-row sub-tiles of this wave that hold data (the rest are skipped).
+  // Returns after a barrier, with the LDS free for reuse.
+  __device__ __forceinline__ void run(uint8_t* lds, const uint16_t* const (&ag)[NA],
+                                      const uint16_t* const (&bg)[NB], int K, int rt_n_in) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rt_n = __builtin_amdgcn_readfirstlane(rt_n_in);   // wave-uniform
+    const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < CT; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int nk = K / kKC;
+    auto issue = [&](int kc) {
+      uint8_t* st = lds + (kc % S) * kStage;
+      const int k0 = kc * kKC;
+#pragma unroll
+      for (int j = 0; j < NA; ++j)
+        __builtin_amdgcn_global_load_lds(ag[j] + k0, (lds_ptr_t)(st + (wave * NA + j) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        __builtin_amdgcn_global_load_lds(bg[j] + k0, (lds_ptr_t)(st + BM * kRow + (wave * NB + j) * 1024),
+                                         16, 0, 0);
+    };
+    // Fragment reads: rows wm*TM + rt*32 + lane%32 (A) and BM + wn*TN +
+    // ct*32 + lane%32 (B) all have swz == swz(lane % 32).
+    int koff[kKC / 16];
+#pragma unroll
+    for (int ks = 0; ks < kKC / 16; ++ks) koff[ks] = (((ks * 2 + (lane >> 5)) ^ swz(lane & 31)) * 16);
+    const int a_rd = (wm * TM + (lane & 31)) * kRow;
+    const int b_rd = (BM + wn * TN + (lane & 31)) * kRow;
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk) issue(s);
+    for (int kc = 0; kc < nk; ++kc) {
+      if (kc + S - 2 < nk) wait_vmem<(S - 2) * NL>();
+      else wait_vmem<0>();
+      stage_barrier();   // stage kc is in LDS for every wave; stage kc-1 is free
+      if (kc + S - 1 < nk) issue(kc + S - 1);
+      const uint8_t* st = lds + (kc % S) * kStage;
+      // All fragments of the stage first, then its MFMAs.
+      constexpr int KS = kKC / 16;
+      u32x4 af[KS][RT], bfr[KS][CT];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+          af[ks][i] = *reinterpret_cast<const u32x4*>(st + a_rd + i * 32 * kRow + koff[ks]);
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+          bfr[ks][j] = *reinterpret_cast<const u32x4*>(st + b_rd + j * 32 * kRow + koff[ks]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (kF16) {
+#pragma unroll
+          for (int j = 0; j < CT; ++j) bfr[ks][j] = bf16x8_to_f16x8(bfr[ks][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+          if (i >= rt_n) continue;
+#pragma unroll
+          for (int j = 0; j < CT; ++j) {
+            if constexpr (kF16) acc[i][j] = mfma_f16(af[ks][i], bfr[ks][j], acc[i][j]);
+            else acc[i][j] = mfma_bf16(af[ks][i], bfr[ks][j], acc[i][j]);
+          }
+        }
+      }
+    }
+    __syncthreads();
   }
 };
 
-__device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
-
-// C += A B^T over K: a[rt] and b[ct] point at the lane's A row / B row; both
-// K-contiguous.  kF16: operands are fp16 (B widened from bf16 on the fly).
-template <int K, bool kF16>
-__device__ __forceinline__ void mma_k(Tile64& t, const uint16_t* const (&a)[2],
-                                      const uint16_t* const (&b)[2]) {
-  const int ko = ((threadIdx.x & 63) >> 5) * 8;
-#pragma unroll 4
-  for (int k = 0; k < K; k += 16) {
-    const u32x4 a0 = ld16(a[0] + k + ko), a1 = ld16(a[1] + k + ko);
-    u32x4 b0 = ld16(b[0] + k + ko), b1 = ld16(b[1] + k + ko);
-    if constexpr (kF16) {
-      b0 = bf16x8_to_f16x8(b0);
-      b1 = bf16x8_to_f16x8(b1);
-      t.acc[0][0] = mfma_f16(a0, b0, t.acc[0][0]);
-      t.acc[0][1] = mfma_f16(a0, b1, t.acc[0][1]);
-      t.acc[1][0] = mfma_f16(a1, b0, t.acc[1][0]);
-      t.acc[1][1] = mfma_f16(a1, b1, t.acc[1][1]);
-    } else {
-      t.acc[0][0] = mfma_bf16(a0, b0, t.acc[0][0]);
-      t.acc[0][1] = mfma_bf16(a0, b1, t.acc[0][1]);
-      t.acc[1][0] = mfma_bf16(a1, b0, t.acc[1][0]);
-      t.acc[1][1] = mfma_bf16(a1, b1, t.acc[1][1]);
-    }
-  }
-}
-
 // Block -> work item, XCD-aware: the hardware deals blocks to the 8 XCDs
 // round-robin; item w is given to XCD w / ceil(n/8) so that consecutive items
-// (the M-tiles of one expert at one column range, which read the same weight
-// rows) share an XCD's L2.  The grid is n rounded up to a multiple of 8, so
-// every item below n has exactly one block; blocks past n return.
+// (the M-tiles and column blocks of one expert, which read the same weight
+// and activation rows) share an XCD's L2.  The grid is n rounded up to a
+// multiple of 8, so every item below n has exactly one block; blocks past n
+// return.
 __device__ __forceinline__ int xcd_item(int n) {
   const int per = (n + 7) / 8;
   const int b = blockIdx.x;
@@ -132,6 +236,7 @@ __device__ __forceinline__ int xcd_item(int n) {
 }
 
 constexpr int round8(int n) { return (n + 7) / 8 * 8; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------- 1. router
 
@@ -143,38 +248,47 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+using RouterGemm = BlockGemm<kMT, kMaxExperts, 1, 4, false, 3>;
+constexpr int kZRow = kMaxExperts + 1;   // logits row stride in LDS (floats)
+
 __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
-  __shared__ float zs[kMT][kMaxExperts + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[cmax(RouterGemm::kLds, kMT * kZRow * 4)];
   __shared__ int hist[kMaxExperts];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k;
   const int t0 = blockIdx.x * kMT;
-  for (int i = threadIdx.x; i < kMaxExperts; i += kThreads) hist[i] = 0;
+  for (int i = tid; i < kMaxExperts; i += kThreads) hist[i] = 0;
 
-  // logits[t0 .. t0+64) x [64 wave, +64): rows clamped to T-1, experts to E-1.
-  const uint16_t* ap[2];
-  const uint16_t* bp[2];
+  // logits[t0 .. t0+64) x [0, 256): token rows clamped to T-1, experts to E-1.
+  const uint16_t* ag[RouterGemm::NA];
+  const uint16_t* bg[RouterGemm::NB];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) ap[rt] = a.x + (size_t)min(t0 + rt * 32 + (lane & 31), T - 1) * H;
+  for (int i = 0; i < RouterGemm::NA; ++i) {
+    const int r = RouterGemm::fetch_row_a(i);
+    ag[i] = a.x + (size_t)min(t0 + r, T - 1) * H + RouterGemm::chunk_elems(r);
+  }
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-    bp[ct] = a.router_w + (size_t)min(wave * 64 + ct * 32 + (lane & 31), E - 1) * H;
-  Tile64 tile;
-  tile.zero();
-  mma_k<H, false>(tile, ap, bp);
+  for (int i = 0; i < RouterGemm::NB; ++i) {
+    const int r = RouterGemm::fetch_row_b(i);
+    bg[i] = a.router_w + (size_t)min(r, E - 1) * H + RouterGemm::chunk_elems(r);
+  }
+  RouterGemm g;
+  g.run(lds, ag, bg, H, RouterGemm::RT);   // LDS is free afterwards
+
+  float* zs = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RouterGemm::RT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int e = wave * 64 + ct * 32 + (lane & 31);
+    for (int ct = 0; ct < RouterGemm::CT; ++ct) {
+      const int e = wave * RouterGemm::TN + ct * 32 + (lane & 31);
       const float b = (a.router_b && e < E) ? a.router_b[e] : 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) zs[rt * 32 + acc_row(r, lane)][e] = tile.acc[rt][ct][r] + b;
+      for (int r = 0; r < 16; ++r) zs[(rt * 32 + acc_row(r, lane)) * kZRow + e] = g.acc[rt][ct][r] + b;
     }
   __syncthreads();
-  for (int q = threadIdx.x; q < kMT * E; q += kThreads) {
+  for (int q = tid; q < kMT * E; q += kThreads) {
     const int i = q / E, e = q - i * E;
-    if (t0 + i < T) a.ws.logits[(size_t)(t0 + i) * E + e] = zs[i][e];
+    if (t0 + i < T) a.ws.logits[(size_t)(t0 + i) * E + e] = zs[i * kZRow + e];
   }
 
   // Top-k per token, one wave per token: ties to the lower expert index.
@@ -184,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      key[q] = e < E ? (((uint64_t)ord_f32(zs[i][e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0;
+      key[q] = e < E ? (((uint64_t)ord_f32(zs[i * kZRow + e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e))
+                     : 0;
     }
     float zsel[kMaxTopK];
     int isel[kMaxTopK];
@@ -221,63 +336,94 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) a.ws.pre.counts[(size_t)blockIdx.x * E + e] = hist[e];
+  for (int e = tid; e < E; e += kThreads) a.ws.pre.counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
 // ---------------------------------------------------------------- 2. scan
 
-// Exclusive prefix sum over 256 values held one per thread (256 threads).
-__device__ __forceinline__ int block_excl_scan256(int v, int* s_wave) {
+constexpr int kScanThreads = 1024;             // 4 threads per expert
+constexpr int kScanParts = kScanThreads / kMaxExperts;
+constexpr int kScanBatch = 16;                 // counts loaded per round trip
+
+// Exclusive prefix sum of v over threads [0, 256) (one value per expert).
+// Every thread of the block calls it; threads >= 256 pass 0 and get 0.
+__device__ __forceinline__ int expert_excl_scan(int v, int* s_wave) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int incl = wave_incl_scan(v);
-  if (lane == 63) s_wave[wave] = incl;
+  if (lane == 63 && wave < 4) s_wave[wave] = incl;
   __syncthreads();
   int base = 0;
-  for (int w = 0; w < wave; ++w) base += s_wave[w];
+  for (int w = 0; w < wave && w < 4; ++w) base += s_wave[w];
   __syncthreads();
-  return base + incl - v;
+  return threadIdx.x < kMaxExperts ? base + incl - v : 0;
 }
 
-__global__ __launch_bounds__(kThreads) void prefill_scan_kernel(LayerArgs a, int nb) {
+__global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(LayerArgs a, int nb) {
   __shared__ int s_wave[4];
   __shared__ int s_tot[2];
-  const int e = threadIdx.x;  // one thread per expert (E <= 256)
+  __shared__ int s_part[kScanParts][kMaxExperts];
+  __shared__ int s_off[kMaxExperts];
+  const int e = threadIdx.x % kMaxExperts, part = threadIdx.x / kMaxExperts;
+  const bool lead = part == 0;
   const int E = a.E, T = a.T, k = a.k;
   const PrefillWs& p = a.ws.pre;
-  int cnt = 0;
+  // Part `part` owns blocks [b0, b1); counts are loaded kScanBatch at a time
+  // so that each thread has one round trip to memory in flight per batch.
+  const int per = (nb + kScanParts - 1) / kScanParts;
+  const int b0 = min(nb, part * per), b1 = min(nb, b0 + per);
+  int psum = 0;
   if (e < E)
-    for (int b = 0; b < nb; ++b) cnt += p.counts[(size_t)b * E + e];
-  const int off = block_excl_scan256(cnt, s_wave);
+    for (int b = b0; b < b1; b += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int q = 0; q < kScanBatch; ++q) c[q] = b + q < b1 ? p.counts[(size_t)(b + q) * E + e] : 0;
+#pragma unroll
+      for (int q = 0; q < kScanBatch; ++q) psum += c[q];
+    }
+  s_part[part][e] = psum;
+  __syncthreads();
+  int cnt = 0;
+  if (lead && e < E)
+    for (int q = 0; q < kScanParts; ++q) cnt += s_part[q][e];
+  const int off = expert_excl_scan(cnt, s_wave);
   const int active = cnt > 0;
-  const int aidx = block_excl_scan256(active, s_wave);
-  const int ntile = (cnt + kMT - 1) / kMT;
-  const int tile0 = block_excl_scan256(ntile, s_wave);
-  if (e == kThreads - 1) {
+  const int aidx = expert_excl_scan(active, s_wave);
+  const int ntile = (cnt + kGM - 1) / kGM;
+  const int tile0 = expert_excl_scan(ntile, s_wave);
+  if (threadIdx.x == kMaxExperts - 1) {
     s_tot[0] = aidx + active;
     s_tot[1] = tile0 + ntile;
   }
+  if (lead) s_off[e] = off;
+  __syncthreads();
   // Per (block, expert) base = expert offset + counts of earlier blocks.
   if (e < E) {
-    int run = off;
-    for (int b = 0; b < nb; ++b) {
-      const int c = p.counts[(size_t)b * E + e];
-      p.base[(size_t)b * E + e] = run;
-      run += c;
+    int run = s_off[e];
+    for (int q = 0; q < part; ++q) run += s_part[q][e];
+    for (int b = b0; b < b1; b += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int q = 0; q < kScanBatch; ++q) c[q] = b + q < b1 ? p.counts[(size_t)(b + q) * E + e] : 0;
+#pragma unroll
+      for (int q = 0; q < kScanBatch; ++q)
+        if (b + q < b1) {
+          p.base[(size_t)(b + q) * E + e] = run;
+          run += c[q];
+        }
     }
   }
-  __syncthreads();
   int32_t* route = a.ws.route;
-  if (active) {
+  if (lead && active) {
     route[1 + aidx] = e;
     route[1 + E + aidx] = off;
     for (int q = 0; q < ntile; ++q) {
       int32_t* tl = p.tiles + 1 + 3 * (tile0 + q);
       tl[0] = e;
-      tl[1] = off + q * kMT;
-      tl[2] = min(kMT, cnt - q * kMT);
+      tl[1] = off + q * kGM;
+      tl[2] = min(kGM, cnt - q * kGM);
     }
   }
-  if (e == 0) {
+  if (threadIdx.x == 0) {
     route[0] = s_tot[0];
     route[1 + E + s_tot[0]] = T * k;
     p.tiles[0] = s_tot[1];
@@ -315,168 +461,232 @@ __global__ __launch_bounds__(kThreads) void prefill_scatter_kernel(LayerArgs a) 
 
 // ---------------------------------------------------------------- 4. gate/up
 
-// Work items: (shared tiles, then routed tiles) x 4 quarters of the 512 h
-// columns; each of the 4 waves owns 32 h columns = 32 gate + 32 up rows.
-__global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs a, int n_shared_tiles,
-                                                                  int n_items) {
+// Block tile: 128 slots x 256 rows of w13 = the gate and up rows of 128 h
+// columns.  Wave (wm, wn) owns slots [64 wm, +64) and h columns
+// [64 wn, +64) of the block's 128: its B tiles ct = 0, 1 are gate rows and
+// ct = 2, 3 the up rows of the same columns, so SiLU-and-mul pairs
+// acc[.][ct] with acc[.][ct + 2] in registers.
+using GateUpGemm = BlockGemm<kGM, 256, 2, 2, false, 3>;
+constexpr int kGuColBlocks = I / 128;   // 4
+
+__global__ __launch_bounds__(kThreads, 2) void prefill_gateup_kernel(LayerArgs a, int n_shared_tiles,
+                                                                     int n_items) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GateUpGemm::kLds];
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / 2, wn = wave % 2;
   const int T = a.T, k = a.k, E = a.E;
-  const int n_tiles = n_items / 4;
-  const int quarter = item / n_tiles;          // column range major: tiles of one expert adjacent
-  const int ti = item - quarter * n_tiles;
+  const int q = item / kGuColBlocks, nb = item % kGuColBlocks;   // column blocks of a tile adjacent
   const PrefillWs& p = a.ws.pre;
   const int32_t* slots = a.ws.route + 2 + 2 * E;
 
   const uint8_t* w13;
   int start, count, hrow0;
-  bool shared = ti < n_shared_tiles;
+  const bool shared = q < n_shared_tiles;
   if (shared) {
-    start = ti * kMT;
-    count = min(kMT, T - start);
+    start = q * kGM;
+    count = min(kGM, T - start);
     hrow0 = T * k + start;
     w13 = a.shared.w13;
   } else {
-    const int rt = ti - n_shared_tiles;
-    if (rt >= p.tiles[0]) return;
-    const int32_t* tl = p.tiles + 1 + 3 * rt;
+    const int rq = q - n_shared_tiles;
+    if (rq >= p.tiles[0]) return;
+    const int32_t* tl = p.tiles + 1 + 3 * rq;
     w13 = a.routed.w13 + (size_t)tl[0] * 2 * I * H * 2;
     start = tl[1];
     count = tl[2];
     hrow0 = start;
   }
   const uint16_t* W = reinterpret_cast<const uint16_t*>(w13);
-  const int col = quarter * 128 + wave * 32 + (lane & 31);   // h column of this lane
-  const uint16_t* ap[2];
+  const uint16_t* ag[GateUpGemm::NA];
+  const uint16_t* bg[GateUpGemm::NB];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = min(rt * 32 + (lane & 31), count - 1);
+  for (int i = 0; i < GateUpGemm::NA; ++i) {
+    const int fr = GateUpGemm::fetch_row_a(i);
+    const int r = min(fr, count - 1);
     const int tok = shared ? start + r : slots[start + r] / k;
-    ap[rt] = a.x + (size_t)tok * H;
+    ag[i] = a.x + (size_t)tok * H + GateUpGemm::chunk_elems(fr);
   }
-  const uint16_t* bp[2] = {W + (size_t)col * H, W + (size_t)(I + col) * H};
-  Tile64 tile;
-  tile.zero();
-  mma_k<H, false>(tile, ap, bp);
-  _Float16* h16 = a.ws.pre.h16;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int i = 0; i < GateUpGemm::NB; ++i) {
+    const int n = GateUpGemm::fetch_row_b(i);          // B row of the block tile
+    const int bw = n >> 7, ct = (n >> 5) & 3;          // owning wave column, MFMA tile
+    const int col = nb * 128 + bw * 64 + (ct & 1) * 32 + (n & 31);
+    bg[i] = W + (size_t)((ct >> 1) * I + col) * H + GateUpGemm::chunk_elems(n);
+  }
+  const int rt_n = max(0, min(GateUpGemm::RT, (count - wm * GateUpGemm::TM + 31) / 32));
+  GateUpGemm g;
+  g.run(lds, ag, bg, H, rt_n);
+
+  _Float16* h16 = p.h16;
+#pragma unroll
+  for (int rt = 0; rt < GateUpGemm::RT; ++rt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = rt * 32 + acc_row(r, lane);
+      const int row = wm * GateUpGemm::TM + rt * 32 + acc_row(r, lane);
       if (row < count) {
-        const float g = tile.acc[rt][0][r], u = tile.acc[rt][1][r];
-        h16[(size_t)(hrow0 + row) * I + col] = (_Float16)(silu(g) * u);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const int col = nb * 128 + wn * 64 + ct * 32 + (lane & 31);
+          const float gv = g.acc[rt][ct][r], uv = g.acc[rt][ct + 2][r];
+          h16[(size_t)(hrow0 + row) * I + col] = (_Float16)(silu(gv) * uv);
+        }
       }
     }
 }
 
 // ---------------------------------------------------------------- 5. down (routed)
 
-// Work items: 8 eighths of the 2048 output columns x routed tiles; each wave
-// owns 64 columns (two 32-column tiles).
-__global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs a, int n_items) {
+// Block tile: 128 slots x 256 output columns; wave (wm, wn) owns slots
+// [64 wm, +64) x columns [128 wn, +128).
+using DownGemm = BlockGemm<kGM, 256, 2, 2, true, 3>;
+constexpr int kDnColBlocks = H / 256;   // 8
+
+__global__ __launch_bounds__(kThreads, 2) void prefill_down_kernel(LayerArgs a, int n_items) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemm::kLds];
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_tiles = n_items / 8;
-  const int eighth = item / n_tiles;
-  const int ti = item - eighth * n_tiles;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / 2, wn = wave % 2;
+  const int q = item / kDnColBlocks, nb = item % kDnColBlocks;
   const PrefillWs& p = a.ws.pre;
-  if (ti >= p.tiles[0]) return;
-  const int32_t* tl = p.tiles + 1 + 3 * ti;
+  if (q >= p.tiles[0]) return;
+  const int32_t* tl = p.tiles + 1 + 3 * q;
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)tl[0] * H * I;
   const int start = tl[1], count = tl[2];
   const uint16_t* h16 = reinterpret_cast<const uint16_t*>(p.h16);
-  const uint16_t* ap[2];
+  const uint16_t* ag[DownGemm::NA];
+  const uint16_t* bg[DownGemm::NB];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-    ap[rt] = h16 + (size_t)(start + min(rt * 32 + (lane & 31), count - 1)) * I;
-  const int c0 = eighth * 256 + wave * 64;
-  const uint16_t* bp[2] = {W + (size_t)(c0 + (lane & 31)) * I, W + (size_t)(c0 + 32 + (lane & 31)) * I};
-  Tile64 tile;
-  tile.zero();
-  mma_k<I, true>(tile, ap, bp);
+  for (int i = 0; i < DownGemm::NA; ++i) {
+    const int fr = DownGemm::fetch_row_a(i);
+    ag[i] = h16 + (size_t)(start + min(fr, count - 1)) * I + DownGemm::chunk_elems(fr);
+  }
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int i = 0; i < DownGemm::NB; ++i) {
+    const int n = DownGemm::fetch_row_b(i);
+    bg[i] = W + (size_t)(nb * 256 + n) * I + DownGemm::chunk_elems(n);
+  }
+  const int rt_n = max(0, min(DownGemm::RT, (count - wm * DownGemm::TM + 31) / 32));
+  DownGemm g;
+  g.run(lds, ag, bg, I, rt_n);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+  for (int rt = 0; rt < DownGemm::RT; ++rt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rt * 32 + acc_row(r, lane);
-        if (row < count) p.y32[(size_t)(start + row) * H + c0 + ct * 32 + (lane & 31)] = tile.acc[rt][ct][r];
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * DownGemm::TM + rt * 32 + acc_row(r, lane);
+      if (row < count) {
+#pragma unroll
+        for (int ct = 0; ct < DownGemm::CT; ++ct) {
+          const int col = nb * 256 + wn * DownGemm::TN + ct * 32 + (lane & 31);
+          p.y16[(size_t)(start + row) * H + col] = (_Float16)g.acc[rt][ct][r];
+        }
       }
+    }
 }
 
 // ---------------------------------------------------------------- 6. shared down + combine
 
-__global__ __launch_bounds__(kThreads) void prefill_shared_combine_kernel(LayerArgs a, int n_items) {
+// Block tile: 128 tokens x 256 output columns of the shared expert's down
+// GEMM.  Epilogue in two halves of 64 tokens: the owning waves park their
+// accumulators in LDS, then every thread finishes 8 consecutive columns of a
+// token at a time: out = shared + sum_j w_j y_j in rank order, one bf16
+// rounding, 16-byte loads of y and stores of out.
+constexpr int kCbRow = 256 + 4;   // floats per LDS row of the parked tile
+constexpr int kCbLds = cmax(DownGemm::kLds, 64 * kCbRow * 4);
+
+__global__ __launch_bounds__(kThreads, 2) void prefill_shared_combine_kernel(LayerArgs a, int n_items) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kCbLds];
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / 2, wn = wave % 2;
   const int T = a.T, k = a.k;
-  const int n_tiles = n_items / 8;
-  const int eighth = item / n_tiles;
-  const int ti = item - eighth * n_tiles;
+  const int q = item / kDnColBlocks, nb = item % kDnColBlocks;
   const PrefillWs& p = a.ws.pre;
-  const int t0 = ti * kMT, count = min(kMT, T - t0);
+  const int t0 = q * kGM, count = min(kGM, T - t0);
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.shared.w2);
   const uint16_t* h16 = reinterpret_cast<const uint16_t*>(p.h16);
-  const uint16_t* ap[2];
+  const uint16_t* ag[DownGemm::NA];
+  const uint16_t* bg[DownGemm::NB];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-    ap[rt] = h16 + (size_t)(T * k + t0 + min(rt * 32 + (lane & 31), count - 1)) * I;
-  const int c0 = eighth * 256 + wave * 64;
-  const uint16_t* bp[2] = {W + (size_t)(c0 + (lane & 31)) * I, W + (size_t)(c0 + 32 + (lane & 31)) * I};
-  Tile64 tile;
-  tile.zero();
-  mma_k<I, true>(tile, ap, bp);
+  for (int i = 0; i < DownGemm::NA; ++i) {
+    const int fr = DownGemm::fetch_row_a(i);
+    ag[i] = h16 + (size_t)(T * k + t0 + min(fr, count - 1)) * I + DownGemm::chunk_elems(fr);
+  }
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int i = 0; i < DownGemm::NB; ++i) {
+    const int n = DownGemm::fetch_row_b(i);
+    bg[i] = W + (size_t)(nb * 256 + n) * I + DownGemm::chunk_elems(n);
+  }
+  const int rt_n = max(0, min(DownGemm::RT, (count - wm * DownGemm::TM + 31) / 32));
+  DownGemm g;
+  g.run(lds, ag, bg, I, rt_n);   // LDS is free afterwards
+
+  float* park = reinterpret_cast<float*>(lds);
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = rt * 32 + acc_row(r, lane);
-      if (row >= count) continue;
-      const int t = t0 + row;
-      int pos[kMaxTopK];
-      float w[kMaxTopK];
+      for (int rt = 0; rt < DownGemm::RT; ++rt)
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j)
-        if (j < k) {
-          pos[j] = p.pos[t * k + j];
-          w[j] = a.ws.wts[t * k + j];
-        }
+        for (int ct = 0; ct < DownGemm::CT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const int c = c0 + ct * 32 + (lane & 31);
-        float o = tile.acc[rt][ct][r];
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j)
-          if (j < k) o = fmaf(w[j], p.y32[(size_t)pos[j] * H + c], o);
-        a.out[(size_t)t * H + c] = f32_to_bf16_rne(o);
-      }
+          for (int r = 0; r < 16; ++r)
+            park[(rt * 32 + acc_row(r, lane)) * kCbRow + wn * DownGemm::TN + ct * 32 + (lane & 31)] =
+                g.acc[rt][ct][r];
     }
+    __syncthreads();
+    // 64 tokens x 32 groups of 8 columns = 2048 units, 8 per thread.
+    for (int u = tid; u < 64 * 32; u += kThreads) {
+      const int row = u >> 5, c8 = (u & 31) * 8;
+      const int lrow = half * 64 + row;
+      if (lrow >= count) continue;
+      const int t = t0 + lrow;
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(park + row * kCbRow + c8);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(park + row * kCbRow + c8 + 4);
+      float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      for (int j = 0; j < k; ++j) {
+        const float w = a.ws.wts[t * k + j];
+        const u32x4 y = *reinterpret_cast<const u32x4*>(p.y16 + (size_t)p.pos[t * k + j] * H + nb * 256 + c8);
+        o[0] = fmaf(w, f16_lo(y.x), o[0]);
+        o[1] = fmaf(w, f16_hi(y.x), o[1]);
+        o[2] = fmaf(w, f16_lo(y.y), o[2]);
+        o[3] = fmaf(w, f16_hi(y.y), o[3]);
+        o[4] = fmaf(w, f16_lo(y.z), o[4]);
+        o[5] = fmaf(w, f16_hi(y.z), o[5]);
+        o[6] = fmaf(w, f16_lo(y.w), o[6]);
+        o[7] = fmaf(w, f16_hi(y.w), o[7]);
+      }
+      u32x4 ob;
+      ob.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+      ob.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+      ob.z = (uint32_t)f32_to_bf16_rne(o[4]) | ((uint32_t)f32_to_bf16_rne(o[5]) << 16);
+      ob.w = (uint32_t)f32_to_bf16_rne(o[6]) | ((uint32_t)f32_to_bf16_rne(o[7]) << 16);
+      *reinterpret_cast<u32x4*>(a.out + (size_t)t * H + nb * 256 + c8) = ob;
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace
 
 int prefill_tiles_max(int T, int E, int k) {
-  return (T * k + kMT - 1) / kMT + E;  // sum over experts of ceil(count / 64)
+  return (T * k + kGM - 1) / kGM + E;  // sum over experts of ceil(count / 128)
 }
 
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
   const int nb = (a.T + kMT - 1) / kMT;
   const int n_routed_max = prefill_tiles_max(a.T, a.E, a.k);
-  const int n_shared = nb;
+  const int n_shared = (a.T + kGM - 1) / kGM;
   launch(prefill_router_kernel, dim3(nb), dim3(kThreads), stream, a);
-  launch(prefill_scan_kernel, dim3(1), dim3(kThreads), stream, a, nb);
+  launch(prefill_scan_kernel, dim3(1), dim3(kScanThreads), stream, a, nb);
   launch(prefill_scatter_kernel, dim3(nb), dim3(kThreads), stream, a);
-  const int n_gu = (n_shared + n_routed_max) * 4;
+  const int n_gu = (n_shared + n_routed_max) * kGuColBlocks;
   launch(prefill_gateup_kernel, dim3(round8(n_gu)), dim3(kThreads), stream, a, n_shared, n_gu);
-  const int n_dn = n_routed_max * 8;
+  const int n_dn = n_routed_max * kDnColBlocks;
   launch(prefill_down_kernel, dim3(round8(n_dn)), dim3(kThreads), stream, a, n_dn);
-  const int n_sc = n_shared * 8;
+  const int n_sc = n_shared * kDnColBlocks;
   launch(prefill_shared_combine_kernel, dim3(round8(n_sc)), dim3(kThreads), stream, a, n_sc);
   return hipGetLastError();
 }
