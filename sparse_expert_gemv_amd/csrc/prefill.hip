@@ -286,52 +286,60 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
       for (int r = 0; r < 16; ++r) zs[(rt * 32 + acc_row(r, lane)) * kZRow + e] = g.acc[rt][ct][r] + b;
     }
   __syncthreads();
-  for (int q = tid; q < kMT * E; q += kThreads) {
-    const int i = q / E, e = q - i * E;
-    if (t0 + i < T) a.ws.logits[(size_t)(t0 + i) * E + e] = zs[i * kZRow + e];
-  }
+  if (tid < E)
+    for (int i = 0; i < kMT && t0 + i < T; ++i) a.ws.logits[(size_t)(t0 + i) * E + tid] = zs[i * kZRow + tid];
 
-  // Top-k per token, one wave per token: ties to the lower expert index.
-  for (int i = wave; i < kMT && t0 + i < T; i += 4) {
-    const int t = t0 + i;
-    uint64_t key[4];
+  // Top-k: four threads per token, each keeping the k largest keys of its 64
+  // experts in a descending list (insertion by compare-exchange), then two
+  // exchange rounds within the quad merge the four lists.  Key = (order-
+  // preserving bits of the logit) << 32 | ~expert, so equal logits rank the
+  // lower expert index first, and sigmoid's monotonicity makes the ranking by
+  // logit the ranking by score.
+  {
+    const int i = tid >> 2, quarter = tid & 3;
+    uint64_t top[kMaxTopK];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      key[q] = e < E ? (((uint64_t)ord_f32(zs[i * kZRow + e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e))
-                     : 0;
-    }
-    float zsel[kMaxTopK];
-    int isel[kMaxTopK];
+    for (int j = 0; j < kMaxTopK; ++j) top[j] = 0;
+    auto insert = [&](uint64_t c) {
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      zsel[j] = 0.f;
-      isel[j] = 0;
-      if (j < k) {
-        const uint64_t best =
-            wave_max_u64(max_u64(max_u64(key[0], key[1]), max_u64(key[2], key[3])));
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (key[q] == best) key[q] = 0;
-        isel[j] = (int)(0xFFFFFFFFu - (uint32_t)best);
-        zsel[j] = unord_f32((uint32_t)(best >> 32));
+      for (int j = 0; j < kMaxTopK; ++j) {
+        const uint64_t hi = max_u64(top[j], c);
+        c = top[j] < c ? top[j] : c;
+        top[j] = hi;
       }
+    };
+    for (int q = 0; q < 64; ++q) {
+      const int e = quarter * 64 + q;
+      if (e < E) insert(((uint64_t)ord_f32(zs[i * kZRow + e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e));
     }
-    float s[kMaxTopK], sum = 0.f;
+    uint64_t other[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      s[j] = sigmoid(zsel[j]);
-      if (j < k) sum += s[j];
-    }
+    for (int j = 0; j < kMaxTopK; ++j) other[j] = dpp64<0xB1, 0xF>(top[j]);   // lane ^ 1
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k && lane == j) {
-        const float w = (a.renormalize ? s[j] / sum : s[j]) * a.routed_scale;
-        a.ws.ids[t * k + j] = isel[j];
-        a.ws.wts[t * k + j] = w;
-        if (a.ids_out) a.ids_out[t * k + j] = isel[j];
-        if (a.wts_out) a.wts_out[t * k + j] = w;
-        atomicAdd(&hist[isel[j]], 1);
+    for (int j = 0; j < kMaxTopK; ++j) insert(other[j]);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) other[j] = dpp64<0x4E, 0xF>(top[j]);   // lane ^ 2
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) insert(other[j]);
+    const int t = t0 + i;
+    if (quarter == 0 && t < T) {
+      float sc[kMaxTopK], sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        sc[j] = sigmoid(unord_f32((uint32_t)(top[j] >> 32)));
+        if (j < k) sum += sc[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+          const int id = (int)(0xFFFFFFFFu - (uint32_t)top[j]);
+          const float w = (a.renormalize ? sc[j] / sum : sc[j]) * a.routed_scale;
+          a.ws.ids[t * k + j] = id;
+          a.ws.wts[t * k + j] = w;
+          if (a.ids_out) a.ids_out[t * k + j] = id;
+          if (a.wts_out) a.wts_out[t * k + j] = w;
+          atomicAdd(&hist[id], 1);
+        }
       }
     }
   }
