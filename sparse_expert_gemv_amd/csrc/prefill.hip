@@ -110,44 +110,55 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Block GEMM C[BM x BN] = A[BM x K] B[BN x K]^T with both operands K-
-// contiguous in global memory, fed through an S-stage LDS ring of 32-wide K
-// chunks.  Global -> LDS moves are LDS-direct loads (global_load_lds, 16
-// bytes per lane): one instruction of a wave fills 16 consecutive 64-byte
-// LDS rows, lane i writing 16-byte chunk i % 4 of row i / 4.  Within a row
-// the four 16-byte K chunks are XOR-swizzled by swz(row), which spreads the
-// MFMA fragment reads of consecutive rows over all LDS banks; each lane
-// therefore fetches the K chunk that belongs at its physical slot.  Thread
-// (wave w, lane i) fetches A rows (w * NA + j) * 16 + i / 4 and B rows
-// (w * NB + j) * 16 + i / 4; the caller hands over one global pointer per
+// contiguous in global memory, fed through an S-stage LDS ring of KC-wide K
+// chunks (KC * 2 bytes per row and stage).  KC = 32 keeps two blocks per CU;
+// KC = 64 moves whole 128-byte lines but its ring needs the LDS of a CU.
+// Global -> LDS moves are LDS-direct loads (global_load_lds, 16 bytes per
+// lane): one instruction of a wave fills 1 KiB of LDS, i.e. RPI consecutive
+// rows, lane i writing 16-byte chunk i % CPR of row i / CPR.  Within a row
+// the 16-byte K chunks are XOR-swizzled by swz(row), which spreads the MFMA
+// fragment reads of consecutive rows over all LDS banks; each lane therefore
+// fetches the K chunk that belongs at its physical slot.  Thread (wave w,
+// lane i) fetches A rows (w * NA + j) * RPI + i / CPR and B rows
+// (w * NB + j) * RPI + i / CPR; the caller hands over one global pointer per
 // such row, already advanced by chunk_elems(row) elements (fetch_row_a/b and
 // chunk_elems give the mapping).  Waves form a WM x WN grid; each owns a
 // (BM / WM) x (BN / WN) tile of 32x32x16 MFMAs.  kF16: A is fp16 and B (bf16
 // in memory) is converted to fp16 in registers before the MFMA; otherwise
 // both are bf16.
-template <int BM, int BN, int WM, int WN, bool kF16, int S>
+template <int BM, int BN, int WM, int WN, bool kF16, int S, int KC>
 struct BlockGemm {
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int RT = TM / 32, CT = TN / 32;
-  static constexpr int NA = BM / 64, NB = BN / 64;   // LDS-direct loads per thread per stage
+  static constexpr int kRow = KC * 2;                 // LDS bytes per row
+  static constexpr int CPR = kRow / 16;               // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;                // rows per LDS-direct instruction
+  static constexpr int NA = BM / (4 * RPI), NB = BN / (4 * RPI);   // instructions per thread per stage
   static constexpr int NL = NA + NB;
-  static constexpr int kKC = 32;                     // K elements per stage
-  static constexpr int kRow = kKC * 2;               // LDS bytes per row
   static constexpr int kStage = (BM + BN) * kRow;
   static constexpr int kLds = S * kStage;
   static_assert(WM * WN == kThreads / 64, "one wave per tile");
-  static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % 64 == 0 && BN % 64 == 0, "tile shape");
+  static_assert(KC == 32 || KC == 64, "K chunk");
+  static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile shape");
   static_assert(S >= 2 && (S - 2) * NL < 64, "pipeline depth");
 
   f32x16 acc[RT][CT];
 
-  __device__ static __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+  // Conflict-free for the fragment reads (16 consecutive rows, one chunk
+  // column) whether the LDS serves 8 lanes x 16 bytes over 32 banks or 16
+  // lanes over 64 banks per cycle.
+  __device__ static __forceinline__ int swz(int row) {
+    return CPR == 4 ? ((row >> 1) ^ (row >> 3)) & 3 : (row ^ (row >> 1)) & 7;
+  }
   __device__ static __forceinline__ int fetch_row_a(int j) {
-    return ((threadIdx.x >> 6) * NA + j) * 16 + ((threadIdx.x & 63) >> 2);
+    return ((threadIdx.x >> 6) * NA + j) * RPI + ((threadIdx.x & 63) / CPR);
   }
   __device__ static __forceinline__ int fetch_row_b(int j) {
-    return ((threadIdx.x >> 6) * NB + j) * 16 + ((threadIdx.x & 63) >> 2);
+    return ((threadIdx.x >> 6) * NB + j) * RPI + ((threadIdx.x & 63) / CPR);
   }
-  __device__ static __forceinline__ int chunk_elems(int row) { return ((threadIdx.x & 3) ^ swz(row)) * 8; }
+  __device__ static __forceinline__ int chunk_elems(int row) {
+    return (((int)threadIdx.x & (CPR - 1)) ^ swz(row)) * 8;
+  }
 
   // rt_n: 32-row sub-tiles of this wave that hold data (the rest are skipped).
   // Returns after a barrier, with the LDS free for reuse.
@@ -162,10 +173,10 @@ struct BlockGemm {
       for (int j = 0; j < CT; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    const int nk = K / kKC;
+    const int nk = K / KC;
     auto issue = [&](int kc) {
       uint8_t* st = lds + (kc % S) * kStage;
-      const int k0 = kc * kKC;
+      const int k0 = kc * KC;
 #pragma unroll
       for (int j = 0; j < NA; ++j)
         __builtin_amdgcn_global_load_lds(ag[j] + k0, (lds_ptr_t)(st + (wave * NA + j) * 1024), 16, 0, 0);
@@ -176,9 +187,9 @@ struct BlockGemm {
     };
     // Fragment reads: rows wm*TM + rt*32 + lane%32 (A) and BM + wn*TN +
     // ct*32 + lane%32 (B) all have swz == swz(lane % 32).
-    int koff[kKC / 16];
+    int koff[KC / 16];
 #pragma unroll
-    for (int ks = 0; ks < kKC / 16; ++ks) koff[ks] = (((ks * 2 + (lane >> 5)) ^ swz(lane & 31)) * 16);
+    for (int ks = 0; ks < KC / 16; ++ks) koff[ks] = (((ks * 2 + (lane >> 5)) ^ swz(lane & 31)) * 16);
     const int a_rd = (wm * TM + (lane & 31)) * kRow;
     const int b_rd = (BM + wn * TN + (lane & 31)) * kRow;
 #pragma unroll
@@ -191,7 +202,7 @@ struct BlockGemm {
       if (kc + S - 1 < nk) issue(kc + S - 1);
       const uint8_t* st = lds + (kc % S) * kStage;
       // All fragments of the stage first, then its MFMAs.
-      constexpr int KS = kKC / 16;
+      constexpr int KS = KC / 16;
       u32x4 af[KS][RT], bfr[KS][CT];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -248,7 +259,7 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-using RouterGemm = BlockGemm<kMT, kMaxExperts, 1, 4, false, 3>;
+using RouterGemm = BlockGemm<kMT, kMaxExperts, 1, 4, false, 3, 32>;
 constexpr int kZRow = kMaxExperts + 1;   // logits row stride in LDS (floats)
 
 __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void prefill_scatter_kernel(LayerArgs a) 
 // [64 wn, +64) of the block's 128: its B tiles ct = 0, 1 are gate rows and
 // ct = 2, 3 the up rows of the same columns, so SiLU-and-mul pairs
 // acc[.][ct] with acc[.][ct + 2] in registers.
-using GateUpGemm = BlockGemm<kGM, 256, 2, 2, false, 3>;
+using GateUpGemm = BlockGemm<kGM, 256, 2, 2, false, 3, 32>;
 constexpr int kGuColBlocks = I / 128;   // 4
 
 __global__ __launch_bounds__(kThreads, 2) void prefill_gateup_kernel(LayerArgs a, int n_shared_tiles,
@@ -548,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gateup_kernel(LayerArgs a
 
 // Block tile: 128 slots x 256 output columns; wave (wm, wn) owns slots
 // [64 wm, +64) x columns [128 wn, +128).
-using DownGemm = BlockGemm<kGM, 256, 2, 2, true, 3>;
+using DownGemm = BlockGemm<kGM, 256, 2, 2, true, 3, 32>;
 constexpr int kDnColBlocks = H / 256;   // 8
 
 __global__ __launch_bounds__(kThreads, 2) void prefill_down_kernel(LayerArgs a, int n_items) {
