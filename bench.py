@@ -256,7 +256,8 @@ def main():
     layer_bytes = ROUTER_BYTES + (n_active + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 2
     if T <= 64:
         # Dominant kernel: the routed gate/up GEMV, |U| experts' gate/up weights.
-        dom_name, dom_bytes, dom_us = names[1], n_active * w13_bytes, float(kern_us[1])
+        gi = names.index("gateup")
+        dom_name, dom_bytes, dom_us = names[gi], n_active * w13_bytes, float(kern_us[gi])
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roof = {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -265,7 +266,8 @@ def main():
                 "avg_launch_us": round(dom_us, 3)}
     else:
         # Dominant kernel: the grouped gate/up GEMM, 2 * (T * 7) * 1024 * 2048 flops.
-        dom_name, dom_us = names[3], float(kern_us[3])
+        gi = names.index("gateup")
+        dom_name, dom_us = names[gi], float(kern_us[gi])
         flops = 2.0 * T * (K_TOP + 1) * (2 * I) * H
         achieved = flops / (dom_us * 1e-6) / 1e12
         roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),

@@ -1,26 +1,28 @@
 // Decode-sized (T <= 64) path of the Flint MoE layer on gfx950, for bf16 and
 // NVFP4 (W4A16) expert weights.
 //
-// Three launches on the caller's stream, each cut into blocks that move
-// ~64 KiB of weights:
-//   1. route   : router GEMV, 16 rows x one token per block.  The last block
-//                of a token picks its top-k by sigmoid score; the last token
-//                to finish buckets every (token, rank) slot by expert into
-//                the routing table (U ascending, slots grouped by expert in
-//                ascending slot order).  Extra blocks of the same launch run
-//                the shared expert's gate/up GEMV, which needs only x.
-//   2. gate/up : (active expert a, 8 gate/up row pairs) per block: the rows
-//                are streamed once for all of a's tokens; SiLU-and-mul in
+// Three launches on the caller's stream:
+//   1. route   : router GEMV, one expert row per wave for all T tokens (64
+//                blocks of 4 waves).  The last block to finish picks every
+//                token's top-k by sigmoid score (a wave per token), computes
+//                the routing weights and buckets every (token, rank) slot by
+//                expert into the routing table (U ascending, slots grouped
+//                by expert in ascending slot order).
+//   2. gate/up : 64 blocks for the shared expert (first, so that they stream
+//                from the start: they need no routing), then (active expert
+//                a, 8 gate/up row pairs) per block; the rows are streamed
+//                once for all of the expert's tokens; SiLU-and-mul in
 //                registers; h stays fp32.
 //   3. down    : 8 output rows of every token per block, over the |U| active
 //                experts and the shared expert, each expert's w2 rows read
 //                once; the partial dot products meet in LDS and combine as
 //                out = shared + sum_j w_j * routed_j in a fixed order,
 //                rounded once to bf16.
-// Hand-offs inside a launch use completion tickets in the workspace header
-// and coherent (write-through) stores/loads, never whole-cache flushes;
-// between launches the stream order is enough.
-//
+// The one hand-off inside a launch (router blocks -> routing block) uses a
+// completion ticket in the workspace header and coherent (write-through)
+// stores/loads, never whole-cache flushes; between launches the stream
+// order is enough.
+
 // What is computed follows "vLLM Day-0 Support for Recursive's Flint"
 // (section "Flint Model Architecture", bullet "MoE Structure"; section
 // "Optimization Strategies", bullets "Small-batch MoE Kernels" and
@@ -38,16 +40,49 @@ constexpr int I = kInter;
 constexpr int kThreads = 256;
 constexpr int kVecH = H / 8;                  // 16-byte vectors per H row (256)
 constexpr int kVecPerLaneH = kVecH / kWave;   // 4
-constexpr int kRouterRowsPerItem = 16;        // 4 waves x 4 rows
+constexpr int kRouteWaves = kThreads / kWave;
+constexpr int kRouterRows = kRouteWaves;      // router: one expert row per wave
+constexpr int kRouteXChunk = 8;               // tokens staged in LDS at a time (32 KiB)
 constexpr int kPairsPerItem = 8;              // gate/up item: 8 (gate, up) row pairs
 constexpr int kUnitsPerExpert = I / kPairsPerItem;  // 64
 constexpr int kXChunk = 4;                    // tokens staged in LDS at a time (16 KiB)
 
 static_assert(H % (8 * kWave) == 0, "H must be a multiple of 512");
+static_assert(kVecH == kThreads, "x staging: one 16-byte vector of a token per thread");
+static_assert(kDecodeMaxT <= kThreads, "gate/up: one slot per thread");
 static_assert(I == 8 * kWave, "down GEMV maps one 16-byte vector of a w2 row per lane");
 static_assert(kDecodeMaxT * kMaxTopK <= 32767 && kMaxExperts <= 32767, "int16 routing table");
 
 // ---------------------------------------------------------------- gate/up
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One x row (H bf16 = kVecH 16-byte vectors, one per thread) into LDS with
+// an LDS-direct load: no registers, and a thread's loads for several rows
+// are all in flight before the barrier that waits for them.  Lane l of a
+// wave writes the 16 bytes at the wave's LDS base + 16 l.
+// Barrier for LDS hand-offs only: waits for this wave's LDS operations, not
+// for its outstanding global loads (which __syncthreads also waits for), so
+// weight loads issued earlier stay in flight across it.  Also a compiler
+// barrier for memory operations.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt: no wait
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Waits until this wave's vector-memory operations, LDS-direct loads
+// included, have completed.  The compiler does not reliably count LDS-direct
+// loads as outstanding LDS writes at a later __syncthreads, so every barrier
+// that publishes them is preceded by this explicit wait.
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: no wait
+}
+
+__device__ __forceinline__ void stage_x_row(u32x4* dst, const uint16_t* row) {
+  const int wave_base = threadIdx.x & ~(kWave - 1);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(row) + threadIdx.x,
+                                   (lds_ptr_t)(dst + wave_base), 16, 0, 0);
+}
 
 // Tokens of one gate/up or down item.  Routed: entry j is slot
 // s = slots[j] (token s / k, h row s).  Shared: entry j is token j, h row
@@ -143,14 +178,16 @@ __device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int
                                                float* h, u32x4* xs) {
   const int lane = threadIdx.x & (kWave - 1);
   const int p = p0 + 2 * (threadIdx.x / kWave);
+  // The first chunk's x rows are requested while the weights are still in
+  // flight; the barrier at the top of the loop waits for both.
+  auto stage = [&](int c0) {
+    const int n = min(kXChunk, count - c0);
+    for (int j = 0; j < n; ++j) stage_x_row(xs + j * kVecH, x + (size_t)list.tok(c0 + j) * H);
+  };
+  if (count > 0) stage(0);
   for (int c0 = 0; c0 < count; c0 += kXChunk) {
     const int n = min(kXChunk, count - c0);
-    __syncthreads();
-    for (int q = threadIdx.x; q < n * kVecH; q += kThreads) {
-      const int j = q / kVecH;
-      const int col = q - j * kVecH;
-      xs[q] = reinterpret_cast<const u32x4*>(x + (size_t)list.tok(c0 + j) * H)[col];
-    }
+    wait_vmem_all();
     __syncthreads();
     for (int j = 0; j < n; ++j) {
       wv.pin();
@@ -169,6 +206,10 @@ __device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int
         hr[1] = silu(acc[1]) * acc[3];
       }
     }
+    if (c0 + kXChunk < count) {
+      lds_barrier();   // every wave is done with this chunk's x
+      stage(c0 + kXChunk);
+    }
   }
 }
 
@@ -185,18 +226,19 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
 
 // Top-k of token t by score, one wave.  Ranks on the logit (the sigmoid is
 // strictly increasing), ties to the lower expert index: key = (logit, ~e).
-__device__ void route_token(const LayerArgs& a, int t) {
+// The selected experts also go to s_ids[t * k + j] (LDS) for the bucketing.
+__device__ void route_token(const LayerArgs& a, int t, int* s_ids) {
   const int lane = threadIdx.x & (kWave - 1);
   const int E = a.E, k = a.k;
   uint64_t key[4];
+  float z[4];
+  // Unconditional (clamped) loads: all four in flight at once.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) z[q] = load_coherent(a.ws.logits + (size_t)t * E + min(lane * 4 + q, E - 1));
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane * 4 + q;
-    key[q] = 0;
-    if (e < E) {
-      const float z = load_coherent(a.ws.logits + (size_t)t * E + e);
-      key[q] = ((uint64_t)ord_f32(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-    }
+    key[q] = e < E ? ((uint64_t)ord_f32(z[q]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e) : 0;
   }
   float zsel[kMaxTopK];
   int isel[kMaxTopK];
@@ -226,37 +268,39 @@ __device__ void route_token(const LayerArgs& a, int t) {
     if (j < k && lane == j) {
       const int e = isel[j];
       const float w = (a.renormalize ? s[j] / sum : s[j]) * a.routed_scale;
-      store_coherent(a.ws.ids + t * k + j, e);
-      store_coherent(a.ws.wts + t * k + j, w);
+      a.ws.ids[t * k + j] = e;
+      a.ws.wts[t * k + j] = w;
+      s_ids[t * k + j] = e;
       if (a.ids_out) a.ids_out[t * k + j] = e;
       if (a.wts_out) a.wts_out[t * k + j] = w;
     }
   }
 }
 
-// Bucket every (token, rank) slot by expert into the routing table, one
-// block of 256 threads.  U is ascending; the slots of one expert are in
-// ascending slot order: the rank of slot s among its expert's slots is the
-// number of set bits below s in that expert's occupancy mask.
-__device__ void build_route_table(const LayerArgs& a, void* smem) {
-  constexpr int kMaskWords = kDecodeMaxT * kMaxTopK / 32;  // 16
-  int* cnt = reinterpret_cast<int*>(smem);                   // [256]
-  int* aoff = cnt + kMaxExperts;                             // [256] offset of expert e
-  uint32_t* occ = reinterpret_cast<uint32_t*>(aoff + kMaxExperts);  // [256][16]
+// Bucket every (token, rank) slot by expert into the routing table (one
+// block; s_ids holds the selected experts).  U is ascending; the slots of one
+// expert are in ascending slot order: the rank of slot s among its expert's
+// slots is the number of set bits below s in that expert's occupancy mask.
+constexpr int kMaskWords = kDecodeMaxT * kMaxTopK / 32;  // 16
+struct RouteLds {
+  int ids[kDecodeMaxT * kMaxTopK];
+  int cnt[kMaxExperts];
+  int aoff[kMaxExperts];     // offset of expert e's slots
+  uint32_t occ[kMaxExperts * kMaskWords];
+};
+
+__device__ void build_route_table(const LayerArgs& a, RouteLds& L) {
   const int E = a.E;
   const int nslots = a.T * a.k;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, nthr = blockDim.x;
   int32_t* route = a.ws.route;
   int32_t* r_active = route + 1;
   int32_t* r_off = route + 1 + E;
   int32_t* r_slots = route + 2 + 2 * E;
-  for (int i = tid; i < kMaxExperts; i += kThreads) cnt[i] = 0;
-  for (int i = tid; i < kMaxExperts * kMaskWords; i += kThreads) occ[i] = 0;
-  __syncthreads();
-  for (int s = tid; s < nslots; s += kThreads) {
-    const int e = load_coherent(a.ws.ids + s);
-    atomicAdd(&cnt[e], 1);
-    atomicOr(&occ[e * kMaskWords + (s >> 5)], 1u << (s & 31));
+  for (int s = tid; s < nslots; s += nthr) {
+    const int e = L.ids[s];
+    atomicAdd(&L.cnt[e], 1);
+    atomicOr(&L.occ[e * kMaskWords + (s >> 5)], 1u << (s & 31));
   }
   __syncthreads();
   if (tid < kWave) {
@@ -265,7 +309,7 @@ __device__ void build_route_table(const LayerArgs& a, void* smem) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      c[q] = e < E ? cnt[e] : 0;
+      c[q] = e < E ? L.cnt[e] : 0;
       sc += c[q];
       sf += c[q] > 0;
     }
@@ -275,101 +319,102 @@ __device__ void build_route_table(const LayerArgs& a, void* smem) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      aoff[e] = o;
+      L.aoff[e] = o;
       if (c[q] > 0) {
-        store_coherent(r_active + act, e);
-        store_coherent(r_off + act, o);
+        r_active[act] = e;
+        r_off[act] = o;
         ++act;
       }
       o += c[q];
     }
     if (lane == kWave - 1) {
-      store_coherent(route, iff);
-      store_coherent(r_off + iff, ic);
+      route[0] = iff;
+      r_off[iff] = ic;
     }
   }
   __syncthreads();
-  for (int s = tid; s < nslots; s += kThreads) {
-    const int e = load_coherent(a.ws.ids + s);
-    const uint32_t* m = occ + e * kMaskWords;
+  for (int s = tid; s < nslots; s += nthr) {
+    const int e = L.ids[s];
+    const uint32_t* m = L.occ + e * kMaskWords;
     int rank = __popc(m[s >> 5] & ((1u << (s & 31)) - 1u));
     for (int w = 0; w < (s >> 5); ++w) rank += __popc(m[w]);
-    store_coherent(r_slots + aoff[e] + rank, s);
+    r_slots[L.aoff[e] + rank] = s;
   }
 }
 
-__device__ void router_block(const LayerArgs& a, int rg, int item, int* s_flag, void* smem) {
+// Router: wave w of block b computes the logits of expert 4b + w for all T
+// tokens; the tokens' x vectors stream through LDS kRouteXChunk at a time.
+// The last block to finish routes every token and builds the routing table.
+__global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
+  __shared__ u32x4 xs[kRouteXChunk * kVecH];
+  __shared__ RouteLds L;
+  __shared__ int s_flag;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int t = item / rg;
-  const int g = item - t * rg;
-  const int e0 = g * kRouterRowsPerItem + wave * 4;
-
-  const u32x4* xr = reinterpret_cast<const u32x4*>(a.x + (size_t)t * H);
-  u32x4 xv[kVecPerLaneH];
-  u32x4 wv[4][kVecPerLaneH];
+  const int e = blockIdx.x * kRouterRows + wave;
+  const int er = min(e, a.E - 1);
+  for (int i = threadIdx.x; i < kMaxExperts; i += kThreads) L.cnt[i] = 0;
+  for (int i = threadIdx.x; i < kMaxExperts * kMaskWords; i += kThreads) L.occ[i] = 0;
+  u32x4 wv[kVecPerLaneH];
+  const u32x4* row = reinterpret_cast<const u32x4*>(a.router_w + (size_t)er * H);
 #pragma unroll
-  for (int i = 0; i < kVecPerLaneH; ++i) xv[i] = xr[lane + i * kWave];
+  for (int i = 0; i < kVecPerLaneH; ++i) wv[i] = row[lane + i * kWave];
+  const float bias = a.router_b ? a.router_b[er] : 0.f;
+  auto stage = [&](int c0) {
+    const int n = min(kRouteXChunk, a.T - c0);
+    for (int j = 0; j < n; ++j) stage_x_row(xs + j * kVecH, a.x + (size_t)(c0 + j) * H);
+  };
+  stage(0);   // in flight together with the router rows
+  for (int c0 = 0; c0 < a.T; c0 += kRouteXChunk) {
+    const int n = min(kRouteXChunk, a.T - c0);
+    wait_vmem_all();
+    __syncthreads();
+    float acc[kRouteXChunk];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int e = min(e0 + r, a.E - 1);
-    const u32x4* row = reinterpret_cast<const u32x4*>(a.router_w + (size_t)e * H);
+    for (int j = 0; j < kRouteXChunk; ++j) {
+      acc[j] = 0.f;
+      if (j < n) {
 #pragma unroll
-    for (int i = 0; i < kVecPerLaneH; ++i) wv[r][i] = row[lane + i * kWave];
+        for (int i = 0; i < kVecPerLaneH; ++i) acc[j] = dot8_bf16(wv[i], xs[j * kVecH + lane + i * kWave], acc[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRouteXChunk; ++j) {
+      if (j < n) {
+        const float z = wave_sum_lane63(acc[j]);
+        if (lane == kWave - 1 && e < a.E) store_coherent(a.ws.logits + (size_t)(c0 + j) * a.E + e, z + bias);
+      }
+    }
+    if (c0 + kRouteXChunk < a.T) {
+      lds_barrier();   // every wave is done with this chunk's x
+      stage(c0 + kRouteXChunk);
+    }
   }
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < kVecPerLaneH; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = dot8_bf16(wv[r][i], xv[i], acc[r]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    acc[r] = wave_sum_lane63(acc[r]);
-    const int e = e0 + r;
-    if (lane == kWave - 1 && e < a.E)
-      store_coherent(a.ws.logits + (size_t)t * a.E + e,
-                     acc[r] + (a.router_b ? a.router_b[e] : 0.f));
-  }
-  uint32_t* hdr = a.ws.header;
-  // The last router item of token t sees every logit of t.
-  if (!last_block_ticket(hdr + kHdrTokTicket + t * kLine, rg, s_flag)) return;
-  if (wave == 0) route_token(a, t);
-  // The last token to finish sees every token's selection: it builds the
-  // routing table (read by the next launches).
-  if (!last_block_ticket(hdr + kHdrTokensDone, a.T, s_flag)) return;
-  build_route_table(a, smem);
+  // The last router block sees every logit.
+  if (!last_block_ticket(a.ws.header + kHdrTokensDone, gridDim.x, &s_flag)) return;
+  for (int t = wave; t < a.T; t += kRouteWaves) route_token(a, t, L.ids);
+  __syncthreads();
+  build_route_table(a, L);
 }
 
-// ---------------------------------------------------------------- kernels
-
-// LDS of the route kernel: x staging, or the bucketing tables (counts,
-// offsets and 16-word occupancy masks of 256 experts).
-constexpr int kRouteLdsVec = (2 * kMaxExperts * 4 + kMaxExperts * (kDecodeMaxT * kMaxTopK / 32) * 4) / 16;
-static_assert(kRouteLdsVec >= kXChunk * kVecH, "route LDS holds the x staging");
-
-template <bool kFp4>
-__global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a, int rg, int n_router) {
-  __shared__ u32x4 xs[kRouteLdsVec];
-  __shared__ int s_flag;
-  if ((int)blockIdx.x < n_router) {
-    router_block(a, rg, blockIdx.x, &s_flag, xs);
-  } else {
-    // Shared expert gate/up: all T tokens, h rows T*k + t.
-    const int unit = blockIdx.x - n_router;
-    GateUpRows<kFp4> wv;
-    wv.load(a.shared, 0, unit * kPairsPerItem);
-    gateup_compute(wv, unit * kPairsPerItem, a.T, TokenList{nullptr, a.k, a.T * a.k}, a.x, a.ws.h, xs);
-  }
-}
-
+// Blocks [0, kUnitsPerExpert): the shared expert for all T tokens (h rows
+// T*k + t); then routed items.
 template <bool kFp4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void gateup_kernel(LayerArgs a) {
   __shared__ u32x4 xs[kXChunk * kVecH];
   __shared__ int16_t s_slots[kDecodeMaxT];
   __shared__ int s_meta[4];
-  const int ai = blockIdx.x / kUnitsPerExpert;
-  const int unit = blockIdx.x - ai * kUnitsPerExpert;
+  if ((int)blockIdx.x < kUnitsPerExpert) {
+    const int unit = blockIdx.x;
+    GateUpRows<kFp4> wv;
+    wv.load(a.shared, 0, unit * kPairsPerItem);
+    gateup_compute(wv, unit * kPairsPerItem, a.T, TokenList{nullptr, a.k, a.T * a.k}, a.x, a.ws.h, xs);
+    return;
+  }
+  const int b = blockIdx.x - kUnitsPerExpert;
+  const int ai = b / kUnitsPerExpert;
+  const int unit = b - ai * kUnitsPerExpert;
   const int32_t* route = a.ws.route;
   const int E = a.E;
   // |U|, U[ai] and its slot range in one round trip (all in bounds: ai < E).
@@ -382,9 +427,12 @@ void gateup_kernel(LayerArgs a) {
   __syncthreads();
   if (ai >= s_meta[0]) return;
   const int e = s_meta[1], off = s_meta[2], cnt = s_meta[3] - s_meta[2];
+  // The slot list is requested before the weights, so that only its load
+  // is waited for before the x rows are requested (cnt <= T <= kThreads).
+  const int my_slot = (int)threadIdx.x < cnt ? route[2 + 2 * E + off + threadIdx.x] : 0;
   GateUpRows<kFp4> wv;
   wv.load(a.routed, e, unit * kPairsPerItem);
-  for (int q = threadIdx.x; q < cnt; q += kThreads) s_slots[q] = (int16_t)route[2 + 2 * E + off + q];
+  if ((int)threadIdx.x < cnt) s_slots[threadIdx.x] = (int16_t)my_slot;
   __syncthreads();
   gateup_compute(wv, unit * kPairsPerItem, cnt, TokenList{s_slots, a.k, 0}, a.x, a.ws.h, xs);
 }
@@ -587,11 +635,10 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
 
 template <bool kFp4>
 static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
-  const int rg = (a.E + kRouterRowsPerItem - 1) / kRouterRowsPerItem;
-  const int n_router = a.T * rg;
-  const int max_active = min(a.E, a.T * a.k);
-  launch(route_kernel<kFp4>, dim3(n_router + kUnitsPerExpert), dim3(kThreads), stream, a, rg, n_router);
-  launch(gateup_kernel<kFp4>, dim3(max_active * kUnitsPerExpert), dim3(kThreads), stream, a);
+  const int n_router = (a.E + kRouterRows - 1) / kRouterRows;
+  const int n_routed = min(a.E, a.T * a.k) * kUnitsPerExpert;
+  launch(route_kernel, dim3(n_router), dim3(kThreads), stream, a);
+  launch(gateup_kernel<kFp4>, dim3(kUnitsPerExpert + n_routed), dim3(kThreads), stream, a);
   launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
   return hipGetLastError();
 }
