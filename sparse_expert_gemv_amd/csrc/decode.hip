@@ -224,55 +224,75 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Top-k of token t by score, one wave.  Ranks on the logit (the sigmoid is
-// strictly increasing), ties to the lower expert index: key = (logit, ~e).
-// The selected experts also go to s_ids[t * k + j] (LDS) for the bucketing.
-__device__ void route_token(const LayerArgs& a, int t, int* s_ids) {
+// Top-k by score of tokens t0, t0 + dt, ... (n <= G of them), one wave,
+// the G selections interleaved round by round.  Ranks on the logit (the
+// sigmoid is strictly increasing), ties to the lower expert index.  Lane l
+// holds the order-preserving keys of experts 4l .. 4l + 3 (0 = empty: no
+// finite logit maps to 0); round j takes the wave maximum M and, among the
+// experts whose key equals M, the lowest index (first set bit of a ballot
+// per column); lane j keeps the j-th pick, computes its sigmoid score and
+// writes its slot.  The selected experts also go to s_ids[t * k + j] (LDS).
+template <int G>
+__device__ void route_tokens(const LayerArgs& a, int t0, int dt, int n, int* s_ids) {
   const int lane = threadIdx.x & (kWave - 1);
   const int E = a.E, k = a.k;
-  uint64_t key[4];
-  float z[4];
-  // Unconditional (clamped) loads: all four in flight at once.
+  uint32_t key[G][4];
+  float z[G][4];
+  // Unconditional (clamped) loads: all of them in flight at once.
 #pragma unroll
-  for (int q = 0; q < 4; ++q) z[q] = load_coherent(a.ws.logits + (size_t)t * E + min(lane * 4 + q, E - 1));
+  for (int g = 0; g < G; ++g) {
+    const int t = min(t0 + min(g, n - 1) * dt, a.T - 1);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane * 4 + q;
-    key[q] = e < E ? ((uint64_t)ord_f32(z[q]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e) : 0;
+    for (int q = 0; q < 4; ++q) z[g][q] = load_coherent(a.ws.logits + (size_t)t * E + min(lane * 4 + q, E - 1));
   }
-  float zsel[kMaxTopK];
-  int isel[kMaxTopK];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    zsel[j] = 0.f;
-    isel[j] = 0;
-    if (j < k) {
-      const uint64_t best =
-          wave_max_u64(max_u64(max_u64(key[0], key[1]), max_u64(key[2], key[3])));
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) key[g][q] = lane * 4 + q < E ? ord_f32(z[g][q]) : 0u;
+  int my_e[G];
+  uint32_t my_key[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    my_e[g] = 0;
+    my_key[g] = 0;
+  }
+#pragma unroll 1
+  for (int j = 0; j < k; ++j) {
+    uint32_t m[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = max(max(key[g][0], key[g][1]), max(key[g][2], key[g][3]));
+    wave_max_u32_lane63_multi<G>(m);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t M = (uint32_t)__builtin_amdgcn_readlane((int)m[g], 63);
+      int best = 4 * kWave;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint64_t hit = __ballot(key[g][q] == M);
+        if (hit) best = min(best, 4 * (int)__builtin_ctzll(hit) + q);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (key[q] == best) key[q] = 0;
-      isel[j] = (int)(0xFFFFFFFFu - (uint32_t)best);
-      zsel[j] = unord_f32((uint32_t)(best >> 32));
+        if (lane * 4 + q == best) key[g][q] = 0u;
+      if (lane == j) {
+        my_e[g] = best;
+        my_key[g] = M;
+      }
     }
   }
-  float s[kMaxTopK];
-  float sum = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    s[j] = sigmoid(zsel[j]);
-    if (j < k) sum += s[j];
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j < k && lane == j) {
-      const int e = isel[j];
-      const float w = (a.renormalize ? s[j] / sum : s[j]) * a.routed_scale;
-      a.ws.ids[t * k + j] = e;
-      a.ws.wts[t * k + j] = w;
-      s_ids[t * k + j] = e;
-      if (a.ids_out) a.ids_out[t * k + j] = e;
-      if (a.wts_out) a.wts_out[t * k + j] = w;
+  for (int g = 0; g < G; ++g) {
+    if (g >= n) break;
+    const int t = t0 + g * dt;
+    const float sc = lane < k ? sigmoid(unord_f32(my_key[g])) : 0.f;
+    const float sum = __shfl(wave_sum_lane63(sc), kWave - 1);
+    if (lane < k) {
+      const float w = (a.renormalize ? sc / sum : sc) * a.routed_scale;
+      a.ws.ids[t * k + lane] = my_e[g];
+      a.ws.wts[t * k + lane] = w;
+      s_ids[t * k + lane] = my_e[g];
+      if (a.ids_out) a.ids_out[t * k + lane] = my_e[g];
+      if (a.wts_out) a.wts_out[t * k + lane] = w;
     }
   }
 }
@@ -392,8 +412,17 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   }
   // The last router block sees every logit.
   if (!last_block_ticket(a.ws.header + kHdrTokensDone, gridDim.x, &s_flag)) return;
-  for (int t = wave; t < a.T; t += kRouteWaves) route_token(a, t, L.ids);
-  __syncthreads();
+  // Wave w routes tokens w, w + 4, ...: up to 4 at a time, interleaved.
+  const int mine = (a.T - wave + kRouteWaves - 1) / kRouteWaves;
+  if (mine == 1) {
+    route_tokens<1>(a, wave, kRouteWaves, 1, L.ids);
+  } else if (mine == 2) {
+    route_tokens<2>(a, wave, kRouteWaves, 2, L.ids);
+  } else {
+    for (int g0 = 0; g0 < mine; g0 += 4)
+      route_tokens<4>(a, wave + g0 * kRouteWaves, kRouteWaves, min(4, mine - g0), L.ids);
+  }
+  lds_barrier();   // the selections are in LDS; their global stores need not land yet
   build_route_table(a, L);
 }
 

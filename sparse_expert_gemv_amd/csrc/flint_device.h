@@ -71,6 +71,38 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   return v;
 }
 
+// Unsigned maximum over the 64 lanes, complete in lane 63 (0 is the
+// identity: lanes outside a row mask and out-of-range sources read 0).
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, true);
+}
+// G independent maxima at once (their DPP chains interleave); lane 63.
+template <int G>
+__device__ __forceinline__ void wave_max_u32_lane63_multi(uint32_t (&v)[G]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max(v[g], dpp_u32<0xB1>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max(v[g], dpp_u32<0x4E>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max(v[g], dpp_u32<0x141>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max(v[g], dpp_u32<0x140>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max(v[g], dpp_u32<0x142, 0xA>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max(v[g], dpp_u32<0x143, 0xC>(v[g]));
+}
+__device__ __forceinline__ uint32_t wave_max_u32_lane63(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  v = max(v, dpp_u32<0x142, 0xA>(v));
+  v = max(v, dpp_u32<0x143, 0xC>(v));
+  return v;
+}
+
 // Cross-block hand-off without whole-L2 writeback/invalidate: values that
 // another block reads in the same launch are stored and loaded as relaxed
 // agent-scope atomics (write-through / coherent-level accesses, "sc1"); a
@@ -124,6 +156,31 @@ __device__ __forceinline__ uint64_t dpp64(uint64_t v) {
 }
 
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maxima over the 64 lanes of G independent values, returned to every lane;
+// each step is applied to all G values before the next, so their DPP chains
+// interleave.
+template <int G>
+__device__ __forceinline__ void wave_max_u64_multi(uint64_t (&v)[G]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max_u64(v[g], dpp64<0xB1>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max_u64(v[g], dpp64<0x4E>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max_u64(v[g], dpp64<0x141>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max_u64(v[g], dpp64<0x140>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max_u64(v[g], dpp64<0x142, 0xA>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = max_u64(v[g], dpp64<0x143, 0xC>(v[g]));
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v[g], 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v[g] >> 32), 63);
+    v[g] = ((uint64_t)hi << 32) | lo;
+  }
+}
 
 // Maximum over the 64 lanes, returned to every lane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
