@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
     }
   }
   // The last router block sees every logit.
-  if (!last_block_ticket(a.ws.header + kHdrTokensDone, gridDim.x, &s_flag)) return;
+  if (!last_block_ticket(a.ws.header + kHdrRouterDone, gridDim.x, &s_flag)) return;
   // Wave w routes tokens w, w + 4, ...: up to 4 at a time, interleaved.
   const int mine = (a.T - wave + kRouteWaves - 1) / kRouteWaves;
   if (mine == 1) {
@@ -465,6 +465,60 @@ void gateup_kernel(LayerArgs a) {
   __syncthreads();
   gateup_compute(wv, unit * kPairsPerItem, cnt, TokenList{s_slots, a.k, 0}, a.x, a.ws.h, xs);
 }
+
+// Lane exchange for the transposed reduction: lane l reads lane l ^ 4 (or
+// l ^ 8) within its row of 16, as two bank-masked DPP row shifts.
+__device__ __forceinline__ float xor4(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int r = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0x5, true);   // row_shl:4 into banks 0, 2
+  r = __builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, true);       // row_shr:4 into banks 1, 3
+  return __builtin_bit_cast(float, r);
+}
+__device__ __forceinline__ float xor8(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int r = __builtin_amdgcn_update_dpp(0, x, 0x108, 0xF, 0x3, true);   // row_shl:8 into banks 0, 1
+  r = __builtin_amdgcn_update_dpp(r, x, 0x118, 0xF, 0xC, true);       // row_shr:8 into banks 2, 3
+  return __builtin_bit_cast(float, r);
+}
+
+// Sums v[0..7] over the 64 lanes: each exchange step halves the values a
+// lane keeps (lanes that differ in bit b keep complementary halves), so the
+// 8 sums cost 3 + 3 lane exchanges instead of 8 full reductions.  On return
+// lane l holds the total of v[bitrev3(l % 8)].
+__device__ __forceinline__ float wave_sum8_transposed(float (&v)[8]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  {
+    const bool b = lane & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float send = b ? v[i] : v[i + 4];
+      const float keep = b ? v[i + 4] : v[i];
+      v[i] = keep + dpp<0xB1>(send);   // lane ^ 1
+    }
+  }
+  {
+    const bool b = lane & 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float send = b ? v[i] : v[i + 2];
+      const float keep = b ? v[i + 2] : v[i];
+      v[i] = keep + dpp<0x4E>(send);   // lane ^ 2
+    }
+  }
+  float t;
+  {
+    const bool b = lane & 4;
+    const float send = b ? v[0] : v[1];
+    const float keep = b ? v[1] : v[0];
+    t = keep + xor4(send);
+  }
+  t += xor8(t);
+  t += __shfl_xor(t, 16);
+  t += __shfl_xor(t, 32);
+  return t;
+}
+
+__device__ __forceinline__ int bitrev3(int x) { return ((x & 1) << 2) | (x & 2) | ((x & 4) >> 2); }
 
 // Down + combine.  Block b owns output rows [8b, 8b + 8) of every token and
 // walks the |U| active experts and then the shared expert; wave w takes
@@ -599,12 +653,11 @@ __device__ __forceinline__ void down_item_rows(const LayerArgs& a, const DownIte
       h0 = hp[0];
       h1 = hp[1];
     }
-    float acc[kDownRowsPerBlock];
+    float v[kDownRowsPerBlock];
 #pragma unroll
-    for (int r = 0; r < kDownRowsPerBlock; ++r) acc[r] = wave_sum_lane63(p.partial(r, h0, h1));
-    if (lane == kWave - 1)
-#pragma unroll
-      for (int r = 0; r < kDownRowsPerBlock; ++r) part[hrow * kDownRowsPerBlock + r] = acc[r] * p.scale();
+    for (int r = 0; r < kDownRowsPerBlock; ++r) v[r] = p.partial(r, h0, h1);
+    const float tot = wave_sum8_transposed(v);
+    if (lane < kDownRowsPerBlock) part[hrow * kDownRowsPerBlock + bitrev3(lane)] = tot * p.scale();
   }
 }
 

@@ -19,8 +19,7 @@ constexpr int kGroupTile = 128;    // slots per grouped-GEMM M-tile (prefill-siz
 // line so that tickets on one never queue behind atomics on another.  All
 // are zero before a forward starts and zero after it ends.
 constexpr int kLine = 64;                       // words per 256-byte line
-constexpr int kHdrTokensDone = 0 * kLine;       // tokens whose selection is complete
-constexpr int kHdrTokTicket = 20 * kLine;       // [64 lines] router items done per token
+constexpr int kHdrRouterDone = 0 * kLine;       // decode: router blocks done
 constexpr int kHeaderWords = 84 * kLine;        // 21 KiB
 
 // Routing table (int32), written once per forward by the block that
