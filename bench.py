@@ -255,9 +255,10 @@ def main():
     w13_bytes, w2_bytes = EXPERT_BYTES[fmt]
     layer_bytes = ROUTER_BYTES + (n_active + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 2
     if T <= 64:
-        # Dominant kernel: the routed gate/up GEMV, |U| experts' gate/up weights.
+        # Dominant kernel: the gate/up GEMV launch, which streams the gate/up
+        # weights of the |U| selected experts and of the shared expert.
         gi = names.index("gateup")
-        dom_name, dom_bytes, dom_us = names[gi], n_active * w13_bytes, float(kern_us[gi])
+        dom_name, dom_bytes, dom_us = names[gi], (n_active + 1) * w13_bytes, float(kern_us[gi])
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roof = {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
