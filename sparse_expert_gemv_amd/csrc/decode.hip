@@ -50,6 +50,7 @@ constexpr int kXChunk = 4;                    // tokens staged in LDS at a time 
 static_assert(H % (8 * kWave) == 0, "H must be a multiple of 512");
 static_assert(kVecH == kThreads, "x staging: one 16-byte vector of a token per thread");
 static_assert(kDecodeMaxT <= kThreads, "gate/up: one slot per thread");
+static_assert(kMaxExperts + 1 <= 512, "down: one work-list item per thread");
 static_assert(I == 8 * kWave, "down GEMV maps one 16-byte vector of a w2 row per lane");
 static_assert(kDecodeMaxT * kMaxTopK <= 32767 && kMaxExperts <= 32767, "int16 routing table");
 
@@ -530,41 +531,46 @@ __device__ __forceinline__ int bitrev3(int x) { return ((x & 1) << 2) | (x & 2) 
 constexpr int kDownRowsPerBlock = 8;
 constexpr int kDownThreads = 512;
 constexpr int kDownWaves = kDownThreads / kWave;
+constexpr int kDnSlots = 4;       // slots per work entry (their h rows prefetched together)
+constexpr int kMaxDownWork = 512; // >= T*k/4 + (E + 1) + T/4 for T <= 64, k <= 8
+// Work entry code: item << 4 | sub-entry (int16: item <= 256, sub-entry < 16).
+static_assert(kDecodeMaxT / kDnSlots <= 16 && (kMaxExperts << 4) + 15 <= 32767, "work entry code");
 
+// A work entry: slots [j0, j0 + nj) of one item (an active expert, or the
+// shared expert whose slots are the T tokens).
 struct DownItem {
   int e;            // expert index in its bank
   bool shared;
-  int off, cnt;     // routed: slots[off, off + cnt); shared: cnt = T, off < 0
-  int hrow0;        // h row of the first slot
+  int off;          // routed: the item's slots start at slots[off]
+  int j0, nj;
 };
 
-__device__ __forceinline__ DownItem down_item(const LayerArgs& a, int item, int n,
-                                              const int16_t* s_active, const int16_t* s_off,
-                                              const int16_t* s_slots) {
+__device__ __forceinline__ DownItem down_entry(const LayerArgs& a, int entry, int n,
+                                               const int16_t* s_active, const int16_t* s_off) {
+  const int item = entry >> 4, q = entry & 15;
   DownItem d;
   d.shared = item >= n;
-  if (!d.shared) {
-    d.e = s_active[item];
-    d.off = s_off[item];
-    d.cnt = s_off[item + 1] - s_off[item];
-    d.hrow0 = s_slots[d.off];
-  } else {
-    d.e = 0;
-    d.off = -1;
-    d.cnt = a.T;
-    d.hrow0 = a.T * a.k;
-  }
+  const int cnt = d.shared ? a.T : s_off[item + 1] - s_off[item];
+  d.e = d.shared ? 0 : s_active[item];
+  d.off = d.shared ? 0 : s_off[item];
+  d.j0 = q * kDnSlots;
+  d.nj = min(kDnSlots, cnt - d.j0);
   return d;
 }
 
-// The 8 rows of one item in a lane, plus the item's first slot's h.
+__device__ __forceinline__ int down_hrow(const LayerArgs& a, const DownItem& d, int j,
+                                         const int16_t* s_slots) {
+  return d.shared ? a.T * a.k + d.j0 + j : s_slots[d.off + d.j0 + j];
+}
+
+// The 8 rows of one work entry in a lane, plus the h of its slots.
 template <bool kFp4>
 struct DownRows;
 
 template <>
 struct DownRows<false> {
   u32x4 w[kDownRowsPerBlock];
-  f32x4 h0, h1;
+  f32x4 h0[kDnSlots], h1[kDnSlots];
   __device__ __forceinline__ void load(const LayerArgs& a, const DownItem& d, int r0) {
     const Bank& bank = d.shared ? a.shared : a.routed;
     const uint16_t* w2 = reinterpret_cast<const uint16_t*>(bank.w2) + (size_t)d.e * H * I;
@@ -597,7 +603,7 @@ struct DownRows<true> {
   uint32_t q[kDownRowsPerBlock];
   uint32_t sc[kDownRowsPerBlock];
   float g;
-  f32x4 h0, h1;
+  f32x4 h0[kDnSlots], h1[kDnSlots];
   __device__ __forceinline__ void load(const LayerArgs& a, const DownItem& d, int r0) {
     const Bank& bank = d.shared ? a.shared : a.routed;
     const uint8_t* w2 = bank.w2 + (size_t)d.e * H * (I / 2);
@@ -630,43 +636,54 @@ struct DownRows<true> {
 };
 
 template <bool kFp4>
-__device__ __forceinline__ void prefetch_item(DownRows<kFp4>& p, const LayerArgs& a,
-                                              const DownItem& d, int r0) {
+__device__ __forceinline__ void prefetch_entry(DownRows<kFp4>& p, const LayerArgs& a, const DownItem& d,
+                                               int r0, const int16_t* s_slots) {
   const int lane = threadIdx.x & (kWave - 1);
   p.load(a, d, r0);
-  const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)d.hrow0 * I) + lane * 2;
-  p.h0 = hp[0];
-  p.h1 = hp[1];
-}
-
-template <bool kFp4>
-__device__ __forceinline__ void down_item_rows(const LayerArgs& a, const DownItem& d,
-                                               const DownRows<kFp4>& p, const int16_t* s_slots,
-                                               float* part) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int T = a.T, k = a.k;
-  f32x4 h0 = p.h0, h1 = p.h1;
-  for (int j = 0; j < d.cnt; ++j) {
-    const int hrow = d.off >= 0 ? s_slots[d.off + j] : T * k + j;
-    if (j > 0) {
-      const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)hrow * I) + lane * 2;
-      h0 = hp[0];
-      h1 = hp[1];
-    }
-    float v[kDownRowsPerBlock];
 #pragma unroll
-    for (int r = 0; r < kDownRowsPerBlock; ++r) v[r] = p.partial(r, h0, h1);
-    const float tot = wave_sum8_transposed(v);
-    if (lane < kDownRowsPerBlock) part[hrow * kDownRowsPerBlock + bitrev3(lane)] = tot * p.scale();
+  for (int j = 0; j < kDnSlots; ++j) {
+    // Entries past nj re-read slot 0's h (in bounds, unused).
+    const int hrow = down_hrow(a, d, j < d.nj ? j : 0, s_slots);
+    const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)hrow * I) + lane * 2;
+    p.h0[j] = hp[0];
+    p.h1[j] = hp[1];
   }
 }
 
+template <bool kFp4>
+__device__ __forceinline__ void down_entry_rows(const LayerArgs& a, const DownItem& d,
+                                                const DownRows<kFp4>& p, const int16_t* s_slots,
+                                                float* part) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int j = 0; j < kDnSlots; ++j) {
+    if (j >= d.nj) break;
+    float v[kDownRowsPerBlock];
+#pragma unroll
+    for (int r = 0; r < kDownRowsPerBlock; ++r) v[r] = p.partial(r, p.h0[j], p.h1[j]);
+    const float tot = wave_sum8_transposed(v);
+    if (lane < kDownRowsPerBlock)
+      part[down_hrow(a, d, j, s_slots) * kDownRowsPerBlock + bitrev3(lane)] = tot * p.scale();
+  }
+}
+
+// Down + combine.  Block b owns output rows [8b, 8b + 8) of every token.
+// Its work: every active expert and the shared expert, cut into entries of
+// up to kDnSlots slots (an expert hit by many tokens spreads over several
+// waves); wave w takes entries w, w + 8, ... and keeps the next entry's w2
+// rows and h rows in flight while it reduces the current one.  Lane l holds
+// columns [8l, 8l + 8) of each row.  Per (h row, output row) the 64-lane
+// partial dot products are summed in a fixed tree and parked in LDS; the
+// block then combines out = shared + sum_j w_j * routed_j in a fixed order.
 template <bool kFp4>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   __shared__ int16_t s_active[kMaxExperts];
   __shared__ int16_t s_off[kMaxExperts + 1];
   __shared__ int16_t s_slots[kDecodeMaxT * kMaxTopK];
+  __shared__ int16_t s_work[kMaxDownWork];
+  __shared__ int s_scan[kDownWaves];
   __shared__ float part[(kMaxTopK + 1) * kDecodeMaxT * kDownRowsPerBlock];
+  const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int r0 = blockIdx.x * kDownRowsPerBlock;
   const int T = a.T, k = a.k, E = a.E;
@@ -678,29 +695,44 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   const int n = route[0];
   __syncthreads();
 
-  // Items 0..n-1: active experts; item n: the shared expert.
+  // Work list: item i (i < n: active expert i; i == n: shared) contributes
+  // ceil(cnt_i / kDnSlots) entries, laid out by an exclusive scan.
+  const int it = threadIdx.x;
+  const int cnt = it < n ? s_off[it + 1] - s_off[it] : (it == n ? T : 0);
+  const int nsub = (cnt + kDnSlots - 1) / kDnSlots;
+  const int incl = wave_incl_scan(nsub);
+  if (lane == kWave - 1) s_scan[wave] = incl;
+  __syncthreads();
+  int base = incl - nsub, total = 0;
+  for (int w = 0; w < kDownWaves; ++w) {
+    if (w < wave) base += s_scan[w];
+    total += s_scan[w];
+  }
+  for (int q = 0; q < nsub; ++q) s_work[base + q] = (int16_t)((it << 4) | q);
+  __syncthreads();
+
   DownRows<kFp4> pa, pb;
   DownItem da{}, db{};
-  int item = wave;
-  if (item <= n) {
-    da = down_item(a, item, n, s_active, s_off, s_slots);
-    prefetch_item(pa, a, da, r0);
+  int w = wave;
+  if (w < total) {
+    da = down_entry(a, s_work[w], n, s_active, s_off);
+    prefetch_entry(pa, a, da, r0, s_slots);
   }
-  while (item <= n) {
-    const int nx = item + kDownWaves;
-    if (nx <= n) {
-      db = down_item(a, nx, n, s_active, s_off, s_slots);
-      prefetch_item(pb, a, db, r0);
+  while (w < total) {
+    const int nx = w + kDownWaves;
+    if (nx < total) {
+      db = down_entry(a, s_work[nx], n, s_active, s_off);
+      prefetch_entry(pb, a, db, r0, s_slots);
     }
-    down_item_rows(a, da, pa, s_slots, part);
-    if (nx > n) break;
+    down_entry_rows(a, da, pa, s_slots, part);
+    if (nx >= total) break;
     const int nx2 = nx + kDownWaves;
-    if (nx2 <= n) {
-      da = down_item(a, nx2, n, s_active, s_off, s_slots);
-      prefetch_item(pa, a, da, r0);
+    if (nx2 < total) {
+      da = down_entry(a, s_work[nx2], n, s_active, s_off);
+      prefetch_entry(pa, a, da, r0, s_slots);
     }
-    down_item_rows(a, db, pb, s_slots, part);
-    item = nx2;
+    down_entry_rows(a, db, pb, s_slots, part);
+    w = nx2;
   }
   __syncthreads();
   for (int q = threadIdx.x; q < T * kDownRowsPerBlock; q += kDownThreads) {
