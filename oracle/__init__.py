@@ -13,7 +13,10 @@ below is checked against something other than itself — closed forms, brute
 force over all subsets on tiny inputs, structured weights whose output has a
 closed form, invariants of the layer (shared-expert-only output, permutation
 equivariance, batch independence, linearity), special cases that reduce to a
-dense mixture, and the FP8/FP4 code tables of the format definitions.
+dense mixture, and the FP8/FP4 code tables of the format definitions.  The
+pre-norm block (``block``) is pinned by a worked example, closed forms of the
+norm, every bf16 rounding midpoint, and reductions to the residual alone and to
+the bare layer.
 
 Parity unpinned: agreement with Recursive's own runtime at the real Flint
 shape cannot be checked here (neither that runtime nor trained weights are
@@ -35,4 +38,5 @@ from .moe import (  # noqa: F401
     bucket,
     route_all,
 )
+from .block import BlockResult, block_forward, block_token, f64_to_bf16_bits, rmsnorm  # noqa: F401
 from .nvfp4 import e2m1_to_f64, e4m3fn_to_f64, nvfp4_dequant  # noqa: F401

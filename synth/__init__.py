@@ -16,5 +16,6 @@ from .flint_layer import (  # noqa: F401
     f32_to_bf16_bits,
     bf16_bits_to_f32,
     make_x,
+    make_residual,
 )
 from .nvfp4_pack import quantize_nvfp4, NvFp4Tensor  # noqa: F401

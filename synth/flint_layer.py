@@ -13,6 +13,9 @@ Value distributions (the pages publish no weights):
   expert w2      bf16 [H, I]          ~ N(0, 0.02)
   router bias    fp32 [E]             ~ N(0, 1)      (skewed-load workload only)
   x              bf16 [T, H]          ~ N(0, 1)
+  norm gamma     bf16 [H]             ~ 1 + N(0, 0.25)   (pre-norm block only)
+  residual r     bf16 [T, H]          ~ s_t * N(0, 1), s_t = 4 exp(N(0, 0.5)) per token,
+                                        with 8 outlier channels per layer seed scaled x20
 
 Every tensor has its own random stream, spawned from one integer seed in a
 fixed order, so any single tensor can be regenerated without the others:
@@ -20,7 +23,9 @@ fixed order, so any single tensor can be regenerated without the others:
   child 1, 2         shared expert w13, w2
   child 3+2e, 4+2e   routed expert e w13, w2
   child 3+2E         router bias
-Activations use a separate SeedSequence keyed by (seed, T, x_seed).
+  child 4+2E         norm gamma
+Activations use a separate SeedSequence keyed by (seed, T, x_seed); the
+residual stream another, and its outlier channels one keyed by the seed alone.
 
 fp32 -> bf16 conversion is round-to-nearest-even on the bit pattern.
 """
@@ -41,8 +46,14 @@ FLINT_INTER = 512
 WEIGHT_STD = 0.02
 X_STD = 1.0
 BIAS_STD = 1.0
+GAMMA_STD = 0.25
+RESID_SCALE = 4.0
+RESID_LOG_STD = 0.5
+RESID_OUTLIERS = 8
+RESID_OUTLIER_GAIN = 20.0
 
 _X_DOMAIN = 0x5EED_0001  # keeps activation streams apart from weight streams
+_R_DOMAIN = 0x5EED_0002  # residual-stream inputs of the pre-norm block
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -81,7 +92,7 @@ class SyntheticLayer:
         self.seed = int(seed)
         self.shape = shape
         E = shape.n_experts
-        self._children = np.random.SeedSequence(self.seed).spawn(4 + 2 * E)
+        self._children = np.random.SeedSequence(self.seed).spawn(5 + 2 * E)
         self._cache: dict = {}
 
     # -- single tensors ---------------------------------------------------
@@ -100,6 +111,15 @@ class SyntheticLayer:
             E = self.shape.n_experts
             rng = np.random.default_rng(self._children[3 + 2 * E])
             self._cache[key] = (rng.standard_normal(E, dtype=np.float32) * np.float32(BIAS_STD)).astype(np.float32)
+        return self._cache[key]
+
+    def norm_weight(self) -> np.ndarray:
+        """bf16 bits [H]: the pre-norm block's RMSNorm gain, ~ 1 + N(0, 0.25)."""
+        key = "gamma"
+        if key not in self._cache:
+            rng = np.random.default_rng(self._children[4 + 2 * self.shape.n_experts])
+            g = np.float32(1.0) + rng.standard_normal(self.shape.hidden, dtype=np.float32) * np.float32(GAMMA_STD)
+            self._cache[key] = f32_to_bf16_bits(g)
         return self._cache[key]
 
     def _child_w13(self, e: int):
@@ -157,3 +177,18 @@ def make_x(T: int, hidden: int = FLINT_HIDDEN, seed: int = 0, x_seed: int = 0) -
     """bf16 bits [T, H] ~ N(0, 1), keyed by (seed, T, x_seed)."""
     seq = np.random.SeedSequence([_X_DOMAIN, int(seed), int(T), int(x_seed)])
     return _normal_bf16(seq, (int(T), int(hidden)), X_STD)
+
+
+def make_residual(T: int, hidden: int = FLINT_HIDDEN, seed: int = 0, x_seed: int = 0) -> np.ndarray:
+    """bf16 bits [T, H] of a residual stream, keyed by (seed, T, x_seed).
+
+    Token t is s_t * N(0, 1) with s_t = 4 exp(N(0, 0.5)); the same 8 channels
+    (chosen by the seed alone, like a trained model's outlier features) are
+    scaled by 20 in every token."""
+    ch = np.random.default_rng(np.random.SeedSequence([_R_DOMAIN, int(seed)]))
+    outliers = ch.choice(int(hidden), size=RESID_OUTLIERS, replace=False)
+    rng = np.random.default_rng(np.random.SeedSequence([_R_DOMAIN, int(seed), int(T), int(x_seed)]))
+    s = np.float32(RESID_SCALE) * np.exp(rng.standard_normal((int(T), 1), dtype=np.float32) * np.float32(RESID_LOG_STD))
+    v = rng.standard_normal((int(T), int(hidden)), dtype=np.float32) * s
+    v[:, outliers] *= np.float32(RESID_OUTLIER_GAIN)
+    return f32_to_bf16_bits(v.astype(np.float32)).reshape(int(T), int(hidden))
