@@ -65,8 +65,15 @@ struct Bank {
 };
 
 struct LayerArgs {
-  const uint16_t* x;         // [T][H]
+  const uint16_t* x;         // [T][H]: the layer's input (the block's normalised r)
   uint16_t* out;             // [T][H]
+  // Pre-norm block only (all nullptr for the bare layer): x is the workspace
+  // buffer `normed`, filled by the first kernel from r and gamma; the last
+  // kernel adds r to the output before its bf16 rounding.
+  const uint16_t* resid;     // r [T][H]
+  const uint16_t* norm_w;    // gamma [H]
+  uint16_t* normed;          // [T][H], == x
+  float eps;
   const uint16_t* router_w;  // [E][H]
   const float* router_b;     // [E] or nullptr
   Bank routed, shared;
