@@ -131,6 +131,8 @@ typedef struct flint_moe_ws_layout {
   size_t h;          /* fp32 [T*k + T][I]: h of slot s in row s; h of the shared expert
                         for token t in row T*k + t */
   size_t extra;      /* path-private scratch (prefill-sized T only) */
+  size_t normed;     /* bf16 [T][H]: the block's normalised input n (flint_moe_block_forward
+                        only; unused by flint_moe_forward) */
 } flint_moe_ws_layout;
 
 /* Validate `cfg` and create a context.  Touches no GPU state.
@@ -175,6 +177,35 @@ flint_status flint_moe_forward_timed(flint_moe_ctx* ctx, const flint_moe_weights
                                      int32_t* topk_ids, float* topk_w, void* workspace,
                                      size_t workspace_bytes, void* stream,
                                      void* const* events, int32_t n_events, int32_t* n_kernels);
+
+/* The pre-norm block around the layer, with the norm and the residual add
+ * fused into the layer's first and last kernels.  Flint is a pre-norm decoder
+ * ("vLLM Day-0 Support for Recursive's Flint", section "Flint Model
+ * Architecture"): the block input r is normalised by RMSNorm, whose output is
+ * bf16 ("Flint on Arc Pro B70", section "norm.py: Triton kernels that assumed
+ * CUDA"), the layer runs on it, and its output is added back to r:
+ *   n_t   = bf16_rne( r_t[k] / sqrt(mean_k r_t[k]^2 + eps) * gamma[k] )   (fp32)
+ *   out_t = bf16_rne( r_t + layer(n_t) )        (the layer's fp32 sum, then + r_t, one rounding)
+ *   r         device bf16 [T][H] (16-byte aligned): the residual stream
+ *   gamma     device bf16 [H] (16-byte aligned): the RMSNorm gain
+ *   eps       finite, >= 0 (Flint: 1e-6)
+ *   out       device bf16 [T][H] (16-byte aligned; must not overlap r)
+ * n_t is left in the workspace region `normed`; the other arguments, the
+ * validation and the errors are those of flint_moe_forward.  The decode path
+ * (T <= 64) launches no extra kernel: the router kernel normalises the rows it
+ * stages, and the down kernel adds r.  Prefill-sized T adds one norm kernel. */
+flint_status flint_moe_block_forward(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                     const uint16_t* gamma, float eps, const uint16_t* r,
+                                     int32_t T, uint16_t* out, int32_t* topk_ids, float* topk_w,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* flint_moe_block_forward with the per-kernel timing of flint_moe_forward_timed. */
+flint_status flint_moe_block_forward_timed(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                           const uint16_t* gamma, float eps, const uint16_t* r,
+                                           int32_t T, uint16_t* out, int32_t* topk_ids,
+                                           float* topk_w, void* workspace, size_t workspace_bytes,
+                                           void* stream, void* const* events, int32_t n_events,
+                                           int32_t* n_kernels);
 
 /* Release a context.  NULL is allowed. */
 void flint_moe_destroy(flint_moe_ctx* ctx);

@@ -3,7 +3,8 @@
 //
 // Three launches on the caller's stream:
 //   1. route   : router GEMV, one expert row per wave for all T tokens (64
-//                blocks of 4 waves).  The last block to finish picks every
+//                blocks of 4 waves; for the pre-norm block each block
+//                normalises the rows it stages, and block 0 stores them).  The last block to finish picks every
 //                token's top-k by sigmoid score (a wave per token), computes
 //                the routing weights and buckets every (token, rank) slot by
 //                expert into the routing table (U ascending, slots grouped
@@ -16,8 +17,8 @@
 //   3. down    : 8 output rows of every token per block, over the |U| active
 //                experts and the shared expert, each expert's w2 rows read
 //                once; the partial dot products meet in LDS and combine as
-//                out = shared + sum_j w_j * routed_j in a fixed order,
-//                rounded once to bf16.
+//                out = shared + sum_j w_j * routed_j (+ r for the pre-norm
+//                block) in a fixed order, rounded once to bf16.
 // The one hand-off inside a launch (router blocks -> routing block) uses a
 // completion ticket in the workspace header and coherent (write-through)
 // stores/loads, never whole-cache flushes; between launches the stream
@@ -363,13 +364,50 @@ __device__ void build_route_table(const LayerArgs& a, RouteLds& L) {
   }
 }
 
+// Pre-norm block: rows c0 .. c0+n-1 of n = bf16(r / rms(r) * gamma) into
+// LDS, made in registers from r (thread i owns the 16-byte vector i of each
+// row, gv the matching 8 gains).  The sums of squares meet in s_ss; block 0
+// also stores the rows to `normed`, the input of the gate/up launch.
+// Contains a __syncthreads: every thread of the block calls it.
+__device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, int n, u32x4* xs,
+                                                  const u32x4& gv, float* s_ss) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  u32x4 rv[kRouteXChunk];
+#pragma unroll
+  for (int j = 0; j < kRouteXChunk; ++j)
+    if (j < n) rv[j] = reinterpret_cast<const u32x4*>(a.resid + (size_t)(c0 + j) * H)[threadIdx.x];
+#pragma unroll
+  for (int j = 0; j < kRouteXChunk; ++j) {
+    if (j < n) {
+      const float ss = wave_sum_lane63(sumsq_bf16x8(rv[j]));
+      if (lane == kWave - 1) s_ss[wave * kRouteXChunk + j] = ss;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kRouteXChunk; ++j) {
+    if (j < n) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < kRouteWaves; ++w) tot += s_ss[w * kRouteXChunk + j];
+      const u32x4 v = rms_scale_bf16x8(rv[j], gv, rms_inv<H>(tot, a.eps));
+      xs[j * kVecH + threadIdx.x] = v;
+      if (blockIdx.x == 0) reinterpret_cast<u32x4*>(a.normed + (size_t)(c0 + j) * H)[threadIdx.x] = v;
+    }
+  }
+}
+
 // Router: wave w of block b computes the logits of expert 4b + w for all T
-// tokens; the tokens' x vectors stream through LDS kRouteXChunk at a time.
-// The last block to finish routes every token and builds the routing table.
+// tokens; the tokens' x vectors stream through LDS kRouteXChunk at a time
+// (for the pre-norm block, normalised from r on the way in).  The last
+// block to finish routes every token and builds the routing table.
+template <bool kNorm>
 __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   __shared__ u32x4 xs[kRouteXChunk * kVecH];
   __shared__ RouteLds L;
   __shared__ int s_flag;
+  __shared__ float s_ss[kRouteWaves * kRouteXChunk];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int e = blockIdx.x * kRouterRows + wave;
@@ -381,9 +419,15 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
 #pragma unroll
   for (int i = 0; i < kVecPerLaneH; ++i) wv[i] = row[lane + i * kWave];
   const float bias = a.router_b ? a.router_b[er] : 0.f;
-  auto stage = [&](int c0) {
+  u32x4 gv{};
+  if (kNorm) gv = reinterpret_cast<const u32x4*>(a.norm_w)[threadIdx.x];
+  auto stage = [&](int c0) __attribute__((always_inline)) {
     const int n = min(kRouteXChunk, a.T - c0);
-    for (int j = 0; j < n; ++j) stage_x_row(xs + j * kVecH, a.x + (size_t)(c0 + j) * H);
+    if (kNorm) {
+      stage_normed_rows(a, c0, n, xs, gv, s_ss);
+    } else {
+      for (int j = 0; j < n; ++j) stage_x_row(xs + j * kVecH, a.x + (size_t)(c0 + j) * H);
+    }
   };
   stage(0);   // in flight together with the router rows
   for (int c0 = 0; c0 < a.T; c0 += kRouteXChunk) {
@@ -741,6 +785,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
     float o = part[(T * k + t) * kDownRowsPerBlock + r];
     for (int j = 0; j < k; ++j)
       o = fmaf(a.ws.wts[t * k + j], part[(t * k + j) * kDownRowsPerBlock + r], o);
+    if (a.resid) o += bf16_lo(a.resid[(size_t)t * H + r0 + r]);
     a.out[(size_t)t * H + r0 + r] = f32_to_bf16_rne(o);
   }
 }
@@ -751,7 +796,10 @@ template <bool kFp4>
 static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
   const int n_router = (a.E + kRouterRows - 1) / kRouterRows;
   const int n_routed = min(a.E, a.T * a.k) * kUnitsPerExpert;
-  launch(route_kernel, dim3(n_router), dim3(kThreads), stream, a);
+  if (a.norm_w)
+    launch(route_kernel<true>, dim3(n_router), dim3(kThreads), stream, a);
+  else
+    launch(route_kernel<false>, dim3(n_router), dim3(kThreads), stream, a);
   launch(gateup_kernel<kFp4>, dim3(kUnitsPerExpert + n_routed), dim3(kThreads), stream, a);
   launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
   return hipGetLastError();

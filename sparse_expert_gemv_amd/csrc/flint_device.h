@@ -48,6 +48,42 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // SiLU in the form g / (1 + exp(-g)).
+// Sum of the squares of 8 bf16 values (one 16-byte vector), fp32.
+__device__ __forceinline__ float sumsq_bf16x8(const u32x4& v) {
+  float s = 0.f;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
+    s = fmaf(lo, lo, s);
+    s = fmaf(hi, hi, s);
+  }
+  return s;
+}
+
+// RMSNorm's scale 1 / sqrt(mean of squares + eps) for a row of kN elements
+// whose squares sum to `sumsq` (the form of "Flint on Arc Pro B70", section
+// "norm.py: Triton kernels that assumed CUDA": a division by the square
+// root, no approximate reciprocal square root).
+template <int kN>
+__device__ __forceinline__ float rms_inv(float sumsq, float eps) {
+  return 1.0f / __builtin_sqrtf(sumsq * (1.0f / kN) + eps);
+}
+
+// bf16(x * inv * gamma) for 8 elements: x and gamma bf16, result RNE.
+__device__ __forceinline__ u32x4 rms_scale_bf16x8(const u32x4& x, const u32x4& g, float inv) {
+  const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = bf16_lo(xw[i]) * inv * bf16_lo(gw[i]);
+    const float hi = bf16_hi(xw[i]) * inv * bf16_hi(gw[i]);
+    o[i] = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }

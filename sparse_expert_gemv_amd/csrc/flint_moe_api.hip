@@ -63,6 +63,7 @@ void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L
   L->topk_ids = o; o = align_up(o + t * k * sizeof(int32_t));
   L->topk_w = o;   o = align_up(o + t * k * sizeof(float));
   L->route = o;    o = align_up(o + (size_t)flint::route_table_ints((int)E, T, (int)k) * sizeof(int32_t));
+  L->normed = o;   o = align_up(o + t * H * sizeof(uint16_t));
   const bool prefill = T > flint::kDecodeMaxT;
   L->h = o;        o = align_up(o + (prefill ? 0 : (t * k + t) * I * sizeof(float)));
   L->extra = o;
@@ -147,10 +148,16 @@ FLINT_API flint_status flint_moe_workspace_layout(const flint_moe_ctx* ctx, int3
 
 namespace {
 
+// Pre-norm block arguments: gamma == nullptr runs the bare layer on x.
+struct NormArgs {
+  const uint16_t* gamma = nullptr;
+  float eps = 0.f;
+};
+
 flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const uint16_t* x,
                           int32_t T, uint16_t* out, int32_t* topk_ids, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* stream,
-                          flint::Launcher& launch) {
+                          flint::Launcher& launch, const NormArgs& norm = NormArgs()) {
   if (!ctx) return FLINT_ERR_INVALID_ARG;
   ctx->last_error.clear();
   const flint_moe_config& c = ctx->cfg;
@@ -162,6 +169,10 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   if (T == 0) return FLINT_OK;
   if (!w || !x || !out || !workspace)
     return fail(ctx, FLINT_ERR_INVALID_ARG, "weights, x, out and workspace must be non-NULL");
+  if (norm.gamma && !aligned(norm.gamma, 16))
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "gamma must be 16-byte aligned");
+  if (norm.gamma && !(std::isfinite(norm.eps) && norm.eps >= 0.f))
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (!w->router_w || !w->routed.w13 || !w->routed.w2 || !w->shared.w13 || !w->shared.w2)
     return fail(ctx, FLINT_ERR_INVALID_ARG, "router and expert weight pointers must be non-NULL");
   const void* p16[] = {w->router_w, w->routed.w13, w->routed.w2, w->shared.w13, w->shared.w2, x, out};
@@ -184,7 +195,7 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
     return fail(ctx, FLINT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const size_t act_bytes = (size_t)T * c.hidden * sizeof(uint16_t);
   if (ranges_overlap(x, act_bytes, out, act_bytes))
-    return fail(ctx, FLINT_ERR_INVALID_ARG, "out overlaps x");
+    return fail(ctx, FLINT_ERR_INVALID_ARG, norm.gamma ? "out overlaps r" : "out overlaps x");
 
   flint_moe_ws_layout L;
   compute_layout(c, T, &L);
@@ -202,6 +213,13 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   flint::LayerArgs a{};
   a.x = x;
   a.out = out;
+  if (norm.gamma) {
+    a.normed = reinterpret_cast<uint16_t*>(ws + L.normed);
+    a.x = a.normed;
+    a.resid = x;
+    a.norm_w = norm.gamma;
+    a.eps = norm.eps;
+  }
   a.router_w = w->router_w;
   a.router_b = w->router_b;
   a.routed = {static_cast<const uint8_t*>(w->routed.w13), static_cast<const uint8_t*>(w->routed.w2),
@@ -259,6 +277,44 @@ FLINT_API flint_status flint_moe_forward_timed(flint_moe_ctx* ctx, const flint_m
   launch.n = n_events;
   const flint_status s = forward_impl(ctx, w, x, T, out, topk_ids, topk_w, workspace,
                                       workspace_bytes, stream, launch);
+  *n_kernels = launch.used;
+  return s;
+}
+
+FLINT_API flint_status flint_moe_block_forward(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                               const uint16_t* gamma, float eps, const uint16_t* r,
+                                               int32_t T, uint16_t* out, int32_t* topk_ids,
+                                               float* topk_w, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  if (!gamma && T != 0) return fail(ctx, FLINT_ERR_INVALID_ARG, "gamma must be non-NULL");
+  flint::Launcher launch;
+  NormArgs norm;
+  norm.gamma = gamma;
+  norm.eps = eps;
+  return forward_impl(ctx, w, r, T, out, topk_ids, topk_w, workspace, workspace_bytes, stream,
+                      launch, norm);
+}
+
+FLINT_API flint_status flint_moe_block_forward_timed(
+    flint_moe_ctx* ctx, const flint_moe_weights* w, const uint16_t* gamma, float eps,
+    const uint16_t* r, int32_t T, uint16_t* out, int32_t* topk_ids, float* topk_w,
+    void* workspace, size_t workspace_bytes, void* stream, void* const* events, int32_t n_events,
+    int32_t* n_kernels) {
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  if (!gamma && T != 0) return fail(ctx, FLINT_ERR_INVALID_ARG, "gamma must be non-NULL");
+  if (!events || n_events < 16 || !n_kernels)
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "events (>= 16) and n_kernels are required");
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return fail(ctx, FLINT_ERR_INVALID_ARG, "NULL event handle");
+  flint::Launcher launch;
+  launch.events = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  launch.n = n_events;
+  NormArgs norm;
+  norm.gamma = gamma;
+  norm.eps = eps;
+  const flint_status s = forward_impl(ctx, w, r, T, out, topk_ids, topk_w, workspace,
+                                      workspace_bytes, stream, launch, norm);
   *n_kernels = launch.used;
   return s;
 }

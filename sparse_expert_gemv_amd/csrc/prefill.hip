@@ -23,6 +23,9 @@
 //   6. shared down + combine : the shared expert's down GEMM per (128 tokens,
 //                256 columns) whose epilogue adds sum_j w_j * y_j in rank order
 //                and rounds once to bf16.
+// The pre-norm block adds a first launch, the RMSNorm of r into the workspace
+// buffer the router and gate/up GEMMs then read as x (one wave per token),
+// and the combine adds r before its one rounding.
 // All GEMMs share one block-level scheme: 256 threads (4 waves); A and B
 // tiles move from global memory straight into LDS (LDS-direct loads, no
 // register staging) 32 K-elements at a time through a three-stage ring, so
@@ -260,6 +263,33 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
 }
 
 using RouterGemm = BlockGemm<kMT, kMaxExperts, 1, 4, false, 3, 32>;
+// Pre-norm block: n = bf16(r / rms(r) * gamma), one wave per token; lane l
+// owns the 16-byte vectors l, l + 64, l + 128, l + 192 of the row.
+constexpr int kNormVecPerLane = H / 8 / 64;   // 4
+
+__global__ __launch_bounds__(kThreads) void prefill_norm_kernel(LayerArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / 64) + (int)(threadIdx.x / 64);
+  if (t >= a.T) return;
+  const u32x4* row = reinterpret_cast<const u32x4*>(a.resid + (size_t)t * H);
+  const u32x4* gam = reinterpret_cast<const u32x4*>(a.norm_w);
+  u32x4 rv[kNormVecPerLane], gv[kNormVecPerLane];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormVecPerLane; ++i) {
+    rv[i] = row[lane + 64 * i];
+    gv[i] = gam[lane + 64 * i];
+  }
+#pragma unroll
+  for (int i = 0; i < kNormVecPerLane; ++i) ss += sumsq_bf16x8(rv[i]);
+  ss = wave_sum_lane63(ss);
+  const float inv = rms_inv<H>(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                   __builtin_bit_cast(int, ss), 63)), a.eps);
+  u32x4* dst = reinterpret_cast<u32x4*>(a.normed + (size_t)t * H);
+#pragma unroll
+  for (int i = 0; i < kNormVecPerLane; ++i) dst[lane + 64 * i] = rms_scale_bf16x8(rv[i], gv[i], inv);
+}
+
 constexpr int kZRow = kMaxExperts + 1;   // logits row stride in LDS (floats)
 
 __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
@@ -677,6 +707,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_shared_combine_kernel(Lay
         o[6] = fmaf(w, f16_lo(y.w), o[6]);
         o[7] = fmaf(w, f16_hi(y.w), o[7]);
       }
+      if (a.resid) {
+        const u32x4 rr = *reinterpret_cast<const u32x4*>(a.resid + (size_t)t * H + nb * 256 + c8);
+        o[0] += bf16_lo(rr.x);
+        o[1] += bf16_hi(rr.x);
+        o[2] += bf16_lo(rr.y);
+        o[3] += bf16_hi(rr.y);
+        o[4] += bf16_lo(rr.z);
+        o[5] += bf16_hi(rr.z);
+        o[6] += bf16_lo(rr.w);
+        o[7] += bf16_hi(rr.w);
+      }
       u32x4 ob;
       ob.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
       ob.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
@@ -698,6 +739,9 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& laun
   const int nb = (a.T + kMT - 1) / kMT;
   const int n_routed_max = prefill_tiles_max(a.T, a.E, a.k);
   const int n_shared = (a.T + kGM - 1) / kGM;
+  if (a.norm_w)
+    launch(prefill_norm_kernel, dim3((a.T + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads),
+           stream, a);
   launch(prefill_router_kernel, dim3(nb), dim3(kThreads), stream, a);
   launch(prefill_scan_kernel, dim3(1), dim3(kScanThreads), stream, a, nb);
   launch(prefill_scatter_kernel, dim3(nb), dim3(kThreads), stream, a);

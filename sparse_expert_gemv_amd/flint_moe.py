@@ -35,6 +35,8 @@ ABI_SYMBOLS = (
     "flint_moe_workspace_layout",
     "flint_moe_forward",
     "flint_moe_forward_timed",
+    "flint_moe_block_forward",
+    "flint_moe_block_forward_timed",
     "flint_moe_destroy",
     "flint_moe_status_string",
     "flint_moe_last_error",
@@ -62,7 +64,7 @@ class Weights(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("total_bytes", "header", "logits", "topk_ids", "topk_w",
-                 "route", "h", "extra")]
+                 "route", "h", "extra", "normed")]
 
 
 class FlintError(RuntimeError):
@@ -98,6 +100,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             P, ctypes.c_size_t, P, ctypes.POINTER(P),
                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.flint_moe_forward_timed.restype = ctypes.c_int
+    lib.flint_moe_block_forward.argtypes = [P, ctypes.POINTER(Weights), P, ctypes.c_float, P,
+                                            ctypes.c_int32, P, P, P, P, ctypes.c_size_t, P]
+    lib.flint_moe_block_forward.restype = ctypes.c_int
+    lib.flint_moe_block_forward_timed.argtypes = [P, ctypes.POINTER(Weights), P, ctypes.c_float, P,
+                                                  ctypes.c_int32, P, P, P, P, ctypes.c_size_t, P,
+                                                  ctypes.POINTER(P), ctypes.c_int32,
+                                                  ctypes.POINTER(ctypes.c_int32)]
+    lib.flint_moe_block_forward_timed.restype = ctypes.c_int
     lib.flint_moe_destroy.argtypes = [P]
     lib.flint_moe_destroy.restype = None
     lib.flint_moe_status_string.argtypes = [ctypes.c_int]
@@ -218,6 +228,42 @@ class FlintMoE:
                               stream.cuda_stream)
         if st != FLINT_OK:
             raise FlintError(st, f"flint_moe_forward: {status_string(st)}: {self.last_error()}")
+
+    def block_forward_raw(self, weights: Weights, gamma_ptr, eps, r_ptr, T, out_ptr, ids_ptr, w_ptr,
+                          ws_ptr, ws_bytes, stream_ptr) -> int:
+        """The pre-norm block's C call with raw addresses; returns the status code."""
+        return self.lib.flint_moe_block_forward(self.handle, ctypes.byref(weights), gamma_ptr,
+                                                float(eps), r_ptr, T, out_ptr, ids_ptr, w_ptr,
+                                                ws_ptr, ws_bytes, stream_ptr)
+
+    def block_forward_timed_raw(self, weights: Weights, gamma_ptr, eps, r_ptr, T, out_ptr, ids_ptr,
+                                w_ptr, ws_ptr, ws_bytes, stream_ptr, event_handles) -> tuple:
+        """The pre-norm block's timed C call; returns (status, number of kernels launched)."""
+        n = len(event_handles)
+        arr = (ctypes.c_void_p * n)(*event_handles)
+        nk = ctypes.c_int32(0)
+        st = self.lib.flint_moe_block_forward_timed(self.handle, ctypes.byref(weights), gamma_ptr,
+                                                    float(eps), r_ptr, T, out_ptr, ids_ptr, w_ptr,
+                                                    ws_ptr, ws_bytes, stream_ptr, arr, n,
+                                                    ctypes.byref(nk))
+        return st, nk.value
+
+    def block_forward(self, weights: DeviceWeights, gamma, r, out, eps=1e-6, topk_ids=None,
+                      topk_w=None, workspace=None, stream=None,
+                      weights_struct: Optional[Weights] = None) -> None:
+        """out[T, H] = r + layer(RMSNorm(r) * gamma), the pre-norm block.  Raises on error."""
+        import torch
+        T = int(r.shape[0])
+        if workspace is None:
+            workspace = self.new_workspace(T, r.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(r.device)
+        ws = weights_struct if weights_struct is not None else weights.struct()
+        st = self.block_forward_raw(ws, _ptr(gamma), eps, _ptr(r), T, _ptr(out), _ptr(topk_ids),
+                                    _ptr(topk_w), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), stream.cuda_stream)
+        if st != FLINT_OK:
+            raise FlintError(st, f"flint_moe_block_forward: {status_string(st)}: {self.last_error()}")
 
     def new_workspace(self, T: int, device):
         """A zero-filled workspace for up to T tokens (the header must start at zero)."""

@@ -107,3 +107,39 @@ def test_forward_host_validation_without_gpu():
     lib = sg.load_library()
     assert lib.flint_moe_forward(None, None, None, 1, None, None, None, None, 0, None) == \
         sg.FLINT_ERR_INVALID_ARG
+
+
+def test_block_forward_host_validation_without_gpu():
+    """The pre-norm block's own checks (gamma, eps, out vs r), all on the host."""
+    m = sg.FlintMoE(max_tokens=8)
+    W = _fake_weights()
+    r, out, ws, g = 1 << 30, 1 << 31, 1 << 32, 1 << 29
+    need = m.workspace_bytes(4)
+    f = lambda **k: m.block_forward_raw(W, k.get("g", g), k.get("eps", 1e-6), k.get("r", r),
+                                        k.get("T", 4), k.get("out", out), None, None, ws,
+                                        k.get("nbytes", need), None)
+    assert f(g=None) == sg.FLINT_ERR_INVALID_ARG and "gamma" in m.last_error()
+    assert f(g=g + 8) == sg.FLINT_ERR_INVALID_ARG and "gamma" in m.last_error()
+    assert f(eps=-1.0) == sg.FLINT_ERR_INVALID_ARG and "eps" in m.last_error()
+    assert f(eps=float("nan")) == sg.FLINT_ERR_INVALID_ARG and "eps" in m.last_error()
+    assert f(eps=float("inf")) == sg.FLINT_ERR_INVALID_ARG
+    assert f(out=r + 2048) == sg.FLINT_ERR_INVALID_ARG and "overlaps r" in m.last_error()
+    assert f(T=9) == sg.FLINT_ERR_INVALID_ARG
+    assert f(nbytes=need - 1) == sg.FLINT_ERR_WORKSPACE
+    assert f(T=0, g=None) == sg.FLINT_OK
+    lib = sg.load_library()
+    assert lib.flint_moe_block_forward(None, None, None, 0.0, None, 1, None, None, None, None, 0,
+                                       None) == sg.FLINT_ERR_INVALID_ARG
+    nk = ctypes.c_int32(0)
+    assert m.block_forward_timed_raw(W, g, 1e-6, r, 4, out, None, None, ws, need, None,
+                                     [None] * 4)[0] == sg.FLINT_ERR_INVALID_ARG
+
+
+def test_workspace_has_a_normed_region():
+    m = sg.FlintMoE(max_tokens=8192)
+    for T in (1, 8, 64, 65, 8192):
+        lay = m.workspace_layout(T)
+        assert lay["normed"] % 256 == 0
+        assert lay["normed"] >= lay["route"] + (2 + 2 * 256 + T * 6) * 4
+        assert lay["normed"] + T * 2048 * 2 <= min(v for k, v in lay.items()
+                                                    if v > lay["normed"] or k == "total_bytes")

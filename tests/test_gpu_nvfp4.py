@@ -124,3 +124,27 @@ def test_nvfp4_intermediate_h(dev4):
             sc = np.max(np.abs(r.h_routed[j]))
             np.testing.assert_allclose(h[t * 6 + j], r.h_routed[j], rtol=0, atol=1e-4 * sc,
                                        err_msg=f"routed h of token {t} rank {j}")
+
+
+@pytest.mark.parametrize("T,x_seed", [(1, 0), (8, 1)])
+def test_nvfp4_block_matches_oracle(dev4, T, x_seed):
+    """The pre-norm block over NVFP4 experts: out = r + layer(RMSNorm(r) * gamma)."""
+    from oracle.block import block_forward
+    from oracle.grading import grade_block
+    from synth import make_residual
+    sg = dev4["sg"]
+    say(f"nvfp4 block parity T={T} x_seed={x_seed}")
+    gamma = SyntheticLayer(SEED).norm_weight()
+    rb = make_residual(T, seed=SEED, x_seed=x_seed)
+    moe = sg.FlintMoE(max_tokens=64, fmt=sg.FLINT_W_NVFP4)
+    r = sg.bf16_tensor(rb, "cuda")
+    out = torch.empty_like(r)
+    ids = torch.full((T, 6), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((T, 6), dtype=torch.float32, device="cuda")
+    moe.block_forward(dev4["W"], sg.bf16_tensor(gamma, "cuda"), r, out, eps=1e-6,
+                      topk_ids=ids, topk_w=w)
+    torch.cuda.synchronize()
+    res = block_forward(dev4["L"], rb, gamma, eps=1e-6)
+    g = grade_block(sg.bf16_bits(out), ids.cpu().numpy(), res, tol=TOL_NVFP4)
+    print(g)
+    assert g.ok, str(g)
