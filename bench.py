@@ -19,7 +19,11 @@ counter table in profiles/hbm_traffic.md when its row was measured on the
 kernel sources as they are now (SHA-256 of the path's .hip file and the two
 shared headers); otherwise it is null.
 
-Prints ONE JSON line.  Default workload: decode T=8 (bf16).
+With --block, one step is the pre-norm block around the layer instead
+(flint_moe_block_forward: RMSNorm of the residual stream r, the layer, and
+the residual add), on a synthetic residual stream and norm gain.
+
+Prints ONE JSON line.  Default workload: decode T=8 (bf16), bare layer.
 """
 
 from __future__ import annotations
@@ -51,6 +55,7 @@ WORKLOADS = {
     "prefill_t8192": dict(T=8192, bias=False, fmt="bf16"),
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+EPS = 1e-6                                 # RMSNorm eps of the pre-norm block
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -98,15 +103,18 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
                    help="CPU time budget of the oracle baseline (0 disables it)")
+    p.add_argument("--block", action="store_true",
+                   help="time the pre-norm block (RMSNorm + layer + residual add)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run a device copy of this many MiB (FETCH_SIZE calibration)")
     return p.parse_args()
 
 
-def cpu_baseline(syn, x_bits, bias, budget_s):
-    """The oracle, as it stands, on the same tokens: whole-layer forwards until
-    the time budget is used (at least two)."""
+def cpu_baseline(syn, x_bits, bias, budget_s, block=False):
+    """The oracle, as it stands, on the same tokens: whole-layer (or whole-block)
+    forwards until the time budget is used (at least two)."""
     from oracle import OracleLayer, moe_forward
+    from oracle.block import block_forward
     try:
         from threadpoolctl import threadpool_info
         threads = max([d.get("num_threads", 1) for d in threadpool_info()
@@ -119,13 +127,16 @@ def cpu_baseline(syn, x_bits, bias, budget_s):
     t_end = time.perf_counter() + budget_s
     while len(times) < 2 or time.perf_counter() < t_end:
         t0 = time.perf_counter()
-        moe_forward(layer, x_bits)
+        if block:
+            block_forward(layer, x_bits, syn.norm_weight())
+        else:
+            moe_forward(layer, x_bits)
         times.append(time.perf_counter() - t0)
     times.sort()
     med = times[len(times) // 2]
     T = x_bits.shape[0]
     return {"value": med * 1e6, "unit": "us/layer", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(times)} whole-layer forwards of the same {T} tokens "
+            "sample": f"{len(times)} whole-{'block' if block else 'layer'} forwards of the same {T} tokens "
                       f"(fp64 numpy, per-token loop); median",
             "tokens_per_s": T / med}
 
@@ -142,7 +153,7 @@ def main():
     import torch
 
     import sparse_expert_gemv_amd as sg
-    from synth import SyntheticLayer, make_x
+    from synth import SyntheticLayer, make_residual, make_x
     from synth.device import nvfp4_layer, upload_bf16, upload_nvfp4
 
     wl = WORKLOADS[args.workload]
@@ -172,8 +183,11 @@ def main():
     log(f"{args.copies} layer copies resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
 
     moe = sg.FlintMoE(max_tokens=max(T, 1), fmt=sg.FLINT_W_BF16 if fmt == "bf16" else sg.FLINT_W_NVFP4)
-    x_bits = make_x(T, seed=args.seed, x_seed=0)
+    # The step's input: x for the bare layer, the residual stream r for the block.
+    x_bits = (make_residual if args.block else make_x)(T, seed=args.seed, x_seed=0)
     x = sg.bf16_tensor(x_bits, dev)
+    gamma = sg.bf16_tensor(syn.norm_weight(), dev)
+    gamma_ptr = int(gamma.data_ptr())
     out = torch.empty_like(x)
     ids = torch.empty((T, K_TOP), dtype=torch.int32, device=dev)
     wts = torch.empty((T, K_TOP), dtype=torch.float32, device=dev)
@@ -184,10 +198,22 @@ def main():
             int(ws.data_ptr()))
 
     def step(i, stream_handle):
-        st = moe.forward_raw(structs[i % len(structs)], ptrs[0], T, ptrs[1], ptrs[2], ptrs[3],
-                             ptrs[4], ws_bytes, stream_handle)
+        if args.block:
+            st = moe.block_forward_raw(structs[i % len(structs)], gamma_ptr, EPS, ptrs[0], T,
+                                       ptrs[1], ptrs[2], ptrs[3], ptrs[4], ws_bytes, stream_handle)
+        else:
+            st = moe.forward_raw(structs[i % len(structs)], ptrs[0], T, ptrs[1], ptrs[2], ptrs[3],
+                                 ptrs[4], ws_bytes, stream_handle)
         if st != sg.FLINT_OK:
             raise sg.FlintError(st, moe.last_error())
+
+    def timed_step(i, stream_handle, events):
+        if args.block:
+            return moe.block_forward_timed_raw(structs[i % len(structs)], gamma_ptr, EPS, ptrs[0],
+                                               T, ptrs[1], ptrs[2], ptrs[3], ptrs[4], ws_bytes,
+                                               stream_handle, events)
+        return moe.forward_timed_raw(structs[i % len(structs)], ptrs[0], T, ptrs[1], ptrs[2],
+                                     ptrs[3], ptrs[4], ws_bytes, stream_handle, events)
 
     stream = torch.cuda.current_stream(dev)
     for i in range(args.warmup):
@@ -207,9 +233,7 @@ def main():
     nk = 0
     t0 = time.perf_counter()
     for i in range(args.steps):
-        st, nk = moe.forward_timed_raw(structs[i % len(structs)], ptrs[0], T, ptrs[1], ptrs[2],
-                                       ptrs[3], ptrs[4], ws_bytes, stream.cuda_stream,
-                                       [e.cuda_event for e in evs[i]])
+        st, nk = timed_step(i, stream.cuda_stream, [e.cuda_event for e in evs[i]])
         if st != sg.FLINT_OK:
             raise sg.FlintError(st, moe.last_error())
     torch.cuda.synchronize()
@@ -221,6 +245,8 @@ def main():
         names = ["route", "gateup", "down"]
     elif nk == 6:
         names = ["router", "scan", "scatter", "gateup", "down", "shared_down_combine"]
+    elif nk == 7:
+        names = ["norm", "router", "scan", "scatter", "gateup", "down", "shared_down_combine"]
     else:
         names = [f"kernel{i}" for i in range(nk)]
     log("per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_us)))
@@ -252,8 +278,13 @@ def main():
     log(f"graph: {us_step:.2f} us/step over {args.steps} steps")
 
     sha = kernel_sources_sha("decode.hip" if T <= 64 else "prefill.hip")
+    wl_name = ("block_" if args.block else "") + args.workload
     w13_bytes, w2_bytes = EXPERT_BYTES[fmt]
+    # Weights read once, the input read once, the output written once (+ the
+    # norm gain for the block).
     layer_bytes = ROUTER_BYTES + (n_active + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 2
+    if args.block:
+        layer_bytes += H * 2
     if T <= 64:
         # Dominant kernel: the gate/up GEMV launch, which streams the gate/up
         # weights of the |U| selected experts and of the shared expert.
@@ -262,7 +293,7 @@ def main():
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roof = {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(args.workload, dom_name, sha),
+                "traffic": measured_traffic(wl_name, dom_name, sha),
                 "algorithmic_bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_us, 3)}
     else:
@@ -274,7 +305,7 @@ def main():
         roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(args.workload, dom_name, sha),
+                "traffic": measured_traffic(wl_name, dom_name, sha),
                 "algorithmic_flops_per_launch": flops, "avg_launch_us": round(dom_us, 3)}
 
     if args.calibrate_copy_mib:
@@ -298,10 +329,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if fmt == "bf16" else "nvfp4 weights (e2m1 + e4m3 scales), bf16 activations",
         "data": "synthetic",
-        "config": {"workload": f"flint_moe_{args.workload}", "T": T, "hidden": H,
+        "config": {"workload": f"flint_moe_{wl_name}", "T": T, "hidden": H,
                    "n_experts": E, "top_k": K_TOP, "inter": I, "shared_experts": 1,
                    "router_bias": bias, "seed": args.seed, "n_active": n_active,
-                   "layer_copies": args.copies, "timing": "one HIP-graph replay of K steps"},
+                   "layer_copies": args.copies, "timing": "one HIP-graph replay of K steps",
+                   **({"prenorm_block": {"norm": "RMSNorm", "eps": EPS, "residual_add": True}}
+                      if args.block else {})},
         "tokens_per_s": round(T / (us_step * 1e-6), 1),
         "layer_algorithmic_bytes": layer_bytes,
         "layer_GBps": round(layer_bytes / (us_step * 1e-6) / 1e9, 1),
@@ -315,7 +348,8 @@ def main():
     }
     if rank == 0 and args.cpu_baseline_seconds > 0:
         log("timing the oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(syn, x_bits, bias, args.cpu_baseline_seconds)
+        result["cpu_baseline"] = cpu_baseline(syn, x_bits, bias, args.cpu_baseline_seconds,
+                                              block=args.block)
     print(json.dumps(result), flush=True)
 
 

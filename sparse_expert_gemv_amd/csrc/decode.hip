@@ -364,6 +364,60 @@ __device__ void build_route_table(const LayerArgs& a, RouteLds& L) {
   }
 }
 
+// Lane exchange for the transposed reduction: lane l reads lane l ^ 4 (or
+// l ^ 8) within its row of 16, as two bank-masked DPP row shifts.
+__device__ __forceinline__ float xor4(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int r = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0x5, true);   // row_shl:4 into banks 0, 2
+  r = __builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, true);       // row_shr:4 into banks 1, 3
+  return __builtin_bit_cast(float, r);
+}
+__device__ __forceinline__ float xor8(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int r = __builtin_amdgcn_update_dpp(0, x, 0x108, 0xF, 0x3, true);   // row_shl:8 into banks 0, 1
+  r = __builtin_amdgcn_update_dpp(r, x, 0x118, 0xF, 0xC, true);       // row_shr:8 into banks 2, 3
+  return __builtin_bit_cast(float, r);
+}
+
+// Sums v[0..7] over the 64 lanes: each exchange step halves the values a
+// lane keeps (lanes that differ in bit b keep complementary halves), so the
+// 8 sums cost 3 + 3 lane exchanges instead of 8 full reductions.  On return
+// lane l holds the total of v[bitrev3(l % 8)].
+__device__ __forceinline__ float wave_sum8_transposed(float (&v)[8]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  {
+    const bool b = lane & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float send = b ? v[i] : v[i + 4];
+      const float keep = b ? v[i + 4] : v[i];
+      v[i] = keep + dpp<0xB1>(send);   // lane ^ 1
+    }
+  }
+  {
+    const bool b = lane & 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float send = b ? v[i] : v[i + 2];
+      const float keep = b ? v[i + 2] : v[i];
+      v[i] = keep + dpp<0x4E>(send);   // lane ^ 2
+    }
+  }
+  float t;
+  {
+    const bool b = lane & 4;
+    const float send = b ? v[0] : v[1];
+    const float keep = b ? v[1] : v[0];
+    t = keep + xor4(send);
+  }
+  t += xor8(t);
+  t += __shfl_xor(t, 16);
+  t += __shfl_xor(t, 32);
+  return t;
+}
+
+__device__ __forceinline__ int bitrev3(int x) { return ((x & 1) << 2) | (x & 2) | ((x & 4) >> 2); }
+
 // Pre-norm block: rows c0 .. c0+n-1 of n = bf16(r / rms(r) * gamma) into
 // LDS, made in registers from r (thread i owns the 16-byte vector i of each
 // row, gv the matching 8 gains).  The sums of squares meet in s_ss; block 0
@@ -371,27 +425,33 @@ __device__ void build_route_table(const LayerArgs& a, RouteLds& L) {
 // Contains a __syncthreads: every thread of the block calls it.
 __device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, int n, u32x4* xs,
                                                   const u32x4& gv, float* s_ss) {
+  static_assert(kRouteXChunk == 8, "one transposed 8-value reduction per chunk");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   u32x4 rv[kRouteXChunk];
+  float ss[kRouteXChunk];
 #pragma unroll
-  for (int j = 0; j < kRouteXChunk; ++j)
+  for (int j = 0; j < kRouteXChunk; ++j) {
+    rv[j] = u32x4{0u, 0u, 0u, 0u};
     if (j < n) rv[j] = reinterpret_cast<const u32x4*>(a.resid + (size_t)(c0 + j) * H)[threadIdx.x];
-#pragma unroll
-  for (int j = 0; j < kRouteXChunk; ++j) {
-    if (j < n) {
-      const float ss = wave_sum_lane63(sumsq_bf16x8(rv[j]));
-      if (lane == kWave - 1) s_ss[wave * kRouteXChunk + j] = ss;
-    }
   }
+#pragma unroll
+  for (int j = 0; j < kRouteXChunk; ++j) ss[j] = sumsq_bf16x8(rv[j]);
+  // Lane l < 8 of each wave gets the wave's sum for row bitrev3(l).
+  const float t = wave_sum8_transposed(ss);
+  if (lane < kRouteXChunk) s_ss[wave * kRouteXChunk + bitrev3(lane)] = t;
   __syncthreads();
+  // Lane l computes the scale of row l % 8 once; the rows' scales are then
+  // read from lanes 0..7.
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kRouteWaves; ++w) tot += s_ss[w * kRouteXChunk + (lane & (kRouteXChunk - 1))];
+  const float inv = rms_inv<H>(tot, a.eps);
 #pragma unroll
   for (int j = 0; j < kRouteXChunk; ++j) {
     if (j < n) {
-      float tot = 0.f;
-#pragma unroll
-      for (int w = 0; w < kRouteWaves; ++w) tot += s_ss[w * kRouteXChunk + j];
-      const u32x4 v = rms_scale_bf16x8(rv[j], gv, rms_inv<H>(tot, a.eps));
+      const float inv_j = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), j));
+      const u32x4 v = rms_scale_bf16x8(rv[j], gv, inv_j);
       xs[j * kVecH + threadIdx.x] = v;
       if (blockIdx.x == 0) reinterpret_cast<u32x4*>(a.normed + (size_t)(c0 + j) * H)[threadIdx.x] = v;
     }
@@ -511,59 +571,6 @@ void gateup_kernel(LayerArgs a) {
   gateup_compute(wv, unit * kPairsPerItem, cnt, TokenList{s_slots, a.k, 0}, a.x, a.ws.h, xs);
 }
 
-// Lane exchange for the transposed reduction: lane l reads lane l ^ 4 (or
-// l ^ 8) within its row of 16, as two bank-masked DPP row shifts.
-__device__ __forceinline__ float xor4(float v) {
-  const int x = __builtin_bit_cast(int, v);
-  int r = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0x5, true);   // row_shl:4 into banks 0, 2
-  r = __builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, true);       // row_shr:4 into banks 1, 3
-  return __builtin_bit_cast(float, r);
-}
-__device__ __forceinline__ float xor8(float v) {
-  const int x = __builtin_bit_cast(int, v);
-  int r = __builtin_amdgcn_update_dpp(0, x, 0x108, 0xF, 0x3, true);   // row_shl:8 into banks 0, 1
-  r = __builtin_amdgcn_update_dpp(r, x, 0x118, 0xF, 0xC, true);       // row_shr:8 into banks 2, 3
-  return __builtin_bit_cast(float, r);
-}
-
-// Sums v[0..7] over the 64 lanes: each exchange step halves the values a
-// lane keeps (lanes that differ in bit b keep complementary halves), so the
-// 8 sums cost 3 + 3 lane exchanges instead of 8 full reductions.  On return
-// lane l holds the total of v[bitrev3(l % 8)].
-__device__ __forceinline__ float wave_sum8_transposed(float (&v)[8]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  {
-    const bool b = lane & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float send = b ? v[i] : v[i + 4];
-      const float keep = b ? v[i + 4] : v[i];
-      v[i] = keep + dpp<0xB1>(send);   // lane ^ 1
-    }
-  }
-  {
-    const bool b = lane & 2;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float send = b ? v[i] : v[i + 2];
-      const float keep = b ? v[i + 2] : v[i];
-      v[i] = keep + dpp<0x4E>(send);   // lane ^ 2
-    }
-  }
-  float t;
-  {
-    const bool b = lane & 4;
-    const float send = b ? v[0] : v[1];
-    const float keep = b ? v[1] : v[0];
-    t = keep + xor4(send);
-  }
-  t += xor8(t);
-  t += __shfl_xor(t, 16);
-  t += __shfl_xor(t, 32);
-  return t;
-}
-
-__device__ __forceinline__ int bitrev3(int x) { return ((x & 1) << 2) | (x & 2) | ((x & 4) >> 2); }
 
 // Down + combine.  Block b owns output rows [8b, 8b + 8) of every token and
 // walks the |U| active experts and then the shared expert; wave w takes

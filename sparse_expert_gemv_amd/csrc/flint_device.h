@@ -39,15 +39,21 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t c) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
+// fp32 -> bf16, round to nearest even, two values at a time (lo in bits
+// 0..15): gfx950's packed conversion v_cvt_pk_bf16_f32 in the default
+// rounding mode.  Checked on the device against the integer form
+// (u + 0x7FFF + bit 16 of u) >> 16 for every non-NaN fp32 pattern: identical;
+// NaN stays NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return (uint16_t)(pack_bf16x2_rne(f, 0.f) & 0xFFFFu);
 }
 
-// SiLU in the form g / (1 + exp(-g)).
 // Sum of the squares of 8 bf16 values (one 16-byte vector), fp32.
 __device__ __forceinline__ float sumsq_bf16x8(const u32x4& v) {
   float s = 0.f;
@@ -79,7 +85,7 @@ __device__ __forceinline__ u32x4 rms_scale_bf16x8(const u32x4& x, const u32x4& g
   for (int i = 0; i < 4; ++i) {
     const float lo = bf16_lo(xw[i]) * inv * bf16_lo(gw[i]);
     const float hi = bf16_hi(xw[i]) * inv * bf16_hi(gw[i]);
-    o[i] = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+    o[i] = pack_bf16x2_rne(lo, hi);
   }
   return u32x4{o[0], o[1], o[2], o[3]};
 }

@@ -719,10 +719,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_shared_combine_kernel(Lay
         o[7] += bf16_hi(rr.w);
       }
       u32x4 ob;
-      ob.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-      ob.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-      ob.z = (uint32_t)f32_to_bf16_rne(o[4]) | ((uint32_t)f32_to_bf16_rne(o[5]) << 16);
-      ob.w = (uint32_t)f32_to_bf16_rne(o[6]) | ((uint32_t)f32_to_bf16_rne(o[7]) << 16);
+      ob.x = pack_bf16x2_rne(o[0], o[1]);
+      ob.y = pack_bf16x2_rne(o[2], o[3]);
+      ob.z = pack_bf16x2_rne(o[4], o[5]);
+      ob.w = pack_bf16x2_rne(o[6], o[7]);
       *reinterpret_cast<u32x4*>(a.out + (size_t)t * H + nb * 256 + c8) = ob;
     }
     __syncthreads();
