@@ -16,7 +16,9 @@ equivariance, batch independence, linearity), special cases that reduce to a
 dense mixture, and the FP8/FP4 code tables of the format definitions.  The
 pre-norm block (``block``) is pinned by a worked example, closed forms of the
 norm, every bf16 rounding midpoint, and reductions to the residual alone and to
-the bare layer.
+the bare layer.  The dense MLP of layers 0 and 1 (``dense``) is pinned by a
+worked example, structured rows with a closed form, additivity over
+intermediate channels, and its reduction to the layer's shared expert.
 
 Parity unpinned: agreement with Recursive's own runtime at the real Flint
 shape cannot be checked here (neither that runtime nor trained weights are
@@ -39,4 +41,5 @@ from .moe import (  # noqa: F401
     route_all,
 )
 from .block import BlockResult, block_forward, block_token, f64_to_bf16_bits, rmsnorm  # noqa: F401
+from .dense import DenseMLP, mlp_block_forward, mlp_forward, mlp_token  # noqa: F401
 from .nvfp4 import e2m1_to_f64, e4m3fn_to_f64, nvfp4_dequant  # noqa: F401

@@ -13,6 +13,7 @@ from .flint_layer import (  # noqa: F401
     FLINT_INTER,
     LayerShape,
     SyntheticLayer,
+    SyntheticDenseMLP,
     f32_to_bf16_bits,
     bf16_bits_to_f32,
     make_x,

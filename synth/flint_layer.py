@@ -54,6 +54,7 @@ RESID_OUTLIER_GAIN = 20.0
 
 _X_DOMAIN = 0x5EED_0001  # keeps activation streams apart from weight streams
 _R_DOMAIN = 0x5EED_0002  # residual-stream inputs of the pre-norm block
+_D_DOMAIN = 0x5EED_0003  # dense-MLP weights (layers 0 and 1)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -192,3 +193,31 @@ def make_residual(T: int, hidden: int = FLINT_HIDDEN, seed: int = 0, x_seed: int
     v = rng.standard_normal((int(T), int(hidden)), dtype=np.float32) * s
     v[:, outliers] *= np.float32(RESID_OUTLIER_GAIN)
     return f32_to_bf16_bits(v.astype(np.float32)).reshape(int(T), int(hidden))
+
+
+class SyntheticDenseMLP:
+    """Seeded weights of a dense SwiGLU MLP: w13 bf16 [2 I_d, H] (gate rows
+    first) and w2 bf16 [H, I_d], both ~ N(0, 0.02), each from its own stream
+    keyed by (seed, I_d); the norm gain from a third, ~ 1 + N(0, 0.25)."""
+
+    def __init__(self, seed: int = 0, inter: int = 14336, hidden: int = FLINT_HIDDEN):
+        self.seed, self.inter, self.hidden = int(seed), int(inter), int(hidden)
+        self._seqs = np.random.SeedSequence([_D_DOMAIN, self.seed, self.inter]).spawn(3)
+        self._cache: dict = {}
+
+    def w13(self) -> np.ndarray:
+        if "w13" not in self._cache:
+            self._cache["w13"] = _normal_bf16(self._seqs[0], (2 * self.inter, self.hidden), WEIGHT_STD)
+        return self._cache["w13"]
+
+    def w2(self) -> np.ndarray:
+        if "w2" not in self._cache:
+            self._cache["w2"] = _normal_bf16(self._seqs[1], (self.hidden, self.inter), WEIGHT_STD)
+        return self._cache["w2"]
+
+    def norm_weight(self) -> np.ndarray:
+        if "gamma" not in self._cache:
+            rng = np.random.default_rng(self._seqs[2])
+            g = np.float32(1.0) + rng.standard_normal(self.hidden, dtype=np.float32) * np.float32(GAMMA_STD)
+            self._cache["gamma"] = f32_to_bf16_bits(g)
+        return self._cache["gamma"]
