@@ -21,7 +21,9 @@ shared headers); otherwise it is null.
 
 With --block, one step is the pre-norm block around the layer instead
 (flint_moe_block_forward: RMSNorm of the residual stream r, the layer, and
-the residual add), on a synthetic residual stream and norm gain.
+the residual add), on a synthetic residual stream and norm gain.  With
+--mlp, one step is the dense SwiGLU MLP of Flint's first two layers
+(flint_mlp_forward; intermediate size --mlp-inter), bare or with --block.
 
 Prints ONE JSON line.  Default workload: decode T=8 (bf16), bare layer.
 """
@@ -105,9 +107,23 @@ def parse():
                    help="CPU time budget of the oracle baseline (0 disables it)")
     p.add_argument("--block", action="store_true",
                    help="time the pre-norm block (RMSNorm + layer + residual add)")
+    p.add_argument("--mlp", action="store_true",
+                   help="time the dense MLP of layers 0-1 instead of the MoE layer")
+    p.add_argument("--mlp-inter", type=int, default=14336,
+                   help="intermediate size of the dense MLP")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run a device copy of this many MiB (FETCH_SIZE calibration)")
     return p.parse_args()
+
+
+def blas_threads() -> int:
+    """Threads the BLAS library behind numpy actually uses."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()
+                    if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        return 1
 
 
 def cpu_baseline(syn, x_bits, bias, budget_s, block=False):
@@ -115,12 +131,7 @@ def cpu_baseline(syn, x_bits, bias, budget_s, block=False):
     forwards until the time budget is used (at least two)."""
     from oracle import OracleLayer, moe_forward
     from oracle.block import block_forward
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()
-                       if d.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
+    threads = blas_threads()
     layer = OracleLayer(H, E, K_TOP, I, syn.router_w(), syn.router_bias() if bias else None,
                         syn.expert)
     times = []
@@ -141,6 +152,225 @@ def cpu_baseline(syn, x_bits, bias, budget_s, block=False):
             "tokens_per_s": T / med}
 
 
+def kernel_names(nk: int, mlp: bool):
+    if mlp:
+        return {2: ["gateup", "down"], 3: ["norm", "gateup", "down"]}.get(
+            nk, [f"kernel{i}" for i in range(nk)])
+    return {3: ["route", "gateup", "down"],
+            6: ["router", "scan", "scatter", "gateup", "down", "shared_down_combine"],
+            7: ["norm", "router", "scan", "scatter", "gateup", "down", "shared_down_combine"]}.get(
+                nk, [f"kernel{i}" for i in range(nk)])
+
+
+def time_kernels(timed_step, steps, stream, mlp=False):
+    """K eager steps, each kernel bracketed by its own start/stop events.
+    Returns (names, mean us per kernel, eager wall us per step)."""
+    import numpy as np
+    import torch
+    n_ev = 16
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    nk = 0
+    t0 = time.perf_counter()
+    for i in range(steps):
+        nk = timed_step(i, stream.cuda_stream, [e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+    eager_wall = (time.perf_counter() - t0) / steps
+    kern_ms = np.array([[evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for j in range(nk)]
+                        for i in range(steps)])
+    names = kernel_names(nk, mlp)
+    kern_us = kern_ms.mean(axis=0) * 1e3
+    log("per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_us)))
+    return names, kern_us, eager_wall * 1e6
+
+
+def time_graph(step, steps, dev):
+    """The timed region: one HIP-graph replay of exactly K steps between events
+    on the replay stream.  Returns us per step."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step(0, side.cuda_stream)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(steps):
+            step(i, cap)
+    torch.cuda.synchronize()
+    g.replay()                       # upload + first launch, untimed
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) * 1e3 / steps
+    log(f"graph: {us_step:.2f} us/step over {steps} steps")
+    return us_step
+
+
+def calibration_copy(args, dev):
+    import torch
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n} bytes done")
+
+
+def common_result(args, us_step, dtype, config):
+    return {
+        "metric": METRIC,
+        "value": round(us_step, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": config,
+    }
+
+
+def run_mlp(args, rank):
+    """The dense MLP of layers 0 and 1 (bare, or the pre-norm block)."""
+    import torch
+
+    import sparse_expert_gemv_amd as sg
+    from synth import SyntheticDenseMLP, make_residual, make_x
+
+    wl = WORKLOADS[args.workload]
+    T, Id = wl["T"], args.mlp_inter
+    if wl["fmt"] != "bf16" or wl["bias"]:
+        raise SystemExit("--mlp takes the bf16 workloads without router bias "
+                         "(decode_t1, decode_t8, prefill_t8192)")
+    if args.copies <= 0:
+        args.copies = 8 if T <= 64 else 4
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"dense MLP I_d={Id}, workload {args.workload}: generating seeded weights {args.seed}")
+    S = SyntheticDenseMLP(args.seed, Id)
+    w13 = [sg.bf16_tensor(S.w13(), dev)]
+    w2 = [sg.bf16_tensor(S.w2(), dev)]
+    for _ in range(1, args.copies):
+        w13.append(w13[0].clone())
+        w2.append(w2[0].clone())
+    torch.cuda.synchronize()
+    log(f"{args.copies} weight copies resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    m = sg.FlintMLP(inter=Id, max_tokens=max(T, 1))
+    x_bits = (make_residual if args.block else make_x)(T, seed=args.seed, x_seed=0)
+    x = sg.bf16_tensor(x_bits, dev)
+    gamma = sg.bf16_tensor(S.norm_weight(), dev)
+    out = torch.empty_like(x)
+    ws = m.new_workspace(T, dev)
+    gp = int(gamma.data_ptr()) if args.block else None
+    wp = [(int(a.data_ptr()), int(b.data_ptr())) for a, b in zip(w13, w2)]
+    xp, op, wsp, wsb = int(x.data_ptr()), int(out.data_ptr()), int(ws.data_ptr()), ws.numel()
+
+    def step(i, sh):
+        a, b = wp[i % len(wp)]
+        st = m.forward_raw(a, b, gp, EPS, xp, T, op, wsp, wsb, sh)
+        if st != sg.FLINT_OK:
+            raise sg.FlintError(st, m.last_error())
+
+    def timed_step(i, sh, events):
+        a, b = wp[i % len(wp)]
+        st, nk = m.forward_timed_raw(a, b, gp, EPS, xp, T, op, wsp, wsb, sh, events)
+        if st != sg.FLINT_OK:
+            raise sg.FlintError(st, m.last_error())
+        return nk
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        step(i, stream.cuda_stream)
+    torch.cuda.synchronize()
+    names, kern_us, eager_us = time_kernels(timed_step, args.steps, stream, mlp=True)
+    us_step = time_graph(step, args.steps, dev)
+
+    w13_bytes, w2_bytes = 2 * Id * H * 2, H * Id * 2
+    layer_bytes = w13_bytes + w2_bytes + 2 * T * H * 2 + (H * 2 if args.block else 0)
+    flops = 2.0 * T * 3 * Id * H
+    sha = kernel_sources_sha("decode.hip" if T <= 64 else "prefill.hip")
+    wl_name = "mlp_" + ("block_" if args.block else "") + args.workload
+    gi = names.index("gateup")
+    dom_us = float(kern_us[gi])
+    if T <= 64:
+        achieved = w13_bytes / (dom_us * 1e-6) / 1e9
+        roof = {"kernel": "gateup", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(wl_name, "gateup", sha),
+                "algorithmic_bytes_per_launch": w13_bytes, "avg_launch_us": round(dom_us, 3)}
+    else:
+        gu_flops = 2.0 * T * 2 * Id * H
+        achieved = gu_flops / (dom_us * 1e-6) / 1e12
+        roof = {"kernel": "gateup", "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(wl_name, "gateup", sha),
+                "algorithmic_flops_per_launch": gu_flops, "avg_launch_us": round(dom_us, 3)}
+    calibration_copy(args, dev)
+    config = {"workload": f"flint_dense_{wl_name}", "T": T, "hidden": H, "inter": Id,
+              "seed": args.seed, "weight_copies": args.copies,
+              "timing": "one HIP-graph replay of K steps",
+              **({"prenorm_block": {"norm": "RMSNorm", "eps": EPS, "residual_add": True}}
+                 if args.block else {})}
+    result = common_result(args, us_step, "bf16", config)
+    result.update({
+        "tokens_per_s": round(T / (us_step * 1e-6), 1),
+        "layer_algorithmic_bytes": layer_bytes,
+        "layer_GBps": round(layer_bytes / (us_step * 1e-6) / 1e9, 1),
+        "layer_hbm_frac": round(layer_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "layer_algorithmic_flops": flops,
+        "kernels_us": {n: round(float(v), 3) for n, v in zip(names, kern_us)},
+        "kernel_timing": "start/stop timestamps of each kernel's execution (hipExtLaunchKernelGGL "
+                         "events), averaged over K eager steps",
+        "eager_wall_us_per_step": round(eager_us, 2),
+        "roofline": roof,
+    })
+    if rank == 0 and args.cpu_baseline_seconds > 0:
+        log("timing the oracle on the host")
+        result["cpu_baseline"] = mlp_cpu_baseline(S, x_bits, args.block, args.cpu_baseline_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def mlp_cpu_baseline(S, x_bits, block, budget_s):
+    """The dense-MLP oracle, as it stands, on the same tokens (at least two runs)."""
+    from oracle.dense import DenseMLP, mlp_block_forward, mlp_forward
+    threads = blas_threads()
+    M = DenseMLP(H, S.inter, S.w13(), S.w2())
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while len(times) < 2 or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        if block:
+            mlp_block_forward(M, x_bits, S.norm_weight())
+        else:
+            mlp_forward(M, x_bits)
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    med = times[len(times) // 2]
+    T = x_bits.shape[0]
+    return {"value": med * 1e6, "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} whole-MLP forwards of the same {T} tokens "
+                      f"(fp64 numpy, per-token loop); median",
+            "tokens_per_s": T / med}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -148,6 +378,8 @@ def main():
               "(expert parallelism is a design note, not code). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     rank = int(os.environ.get("RANK", "0"))
+    if args.mlp:
+        return run_mlp(args, rank)
 
     import numpy as np
     import torch
@@ -222,60 +454,14 @@ def main():
     n_active = int(np.unique(ids.cpu().numpy()).size)
     log(f"warmup done: |U| = {n_active}")
 
-    # Per-kernel durations: K eager steps; each kernel's own start and end
-    # timestamps land in a pair of HIP events.
-    n_ev = 16
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    for row in evs:
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    nk = 0
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        st, nk = timed_step(i, stream.cuda_stream, [e.cuda_event for e in evs[i]])
+    def timed(i, sh, events):
+        st, nk = timed_step(i, sh, events)
         if st != sg.FLINT_OK:
             raise sg.FlintError(st, moe.last_error())
-    torch.cuda.synchronize()
-    eager_wall = (time.perf_counter() - t0) / args.steps
-    kern_ms = np.array([[evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for j in range(nk)]
-                        for i in range(args.steps)])
-    kern_us = kern_ms.mean(axis=0) * 1e3
-    if nk == 3:
-        names = ["route", "gateup", "down"]
-    elif nk == 6:
-        names = ["router", "scan", "scatter", "gateup", "down", "shared_down_combine"]
-    elif nk == 7:
-        names = ["norm", "router", "scan", "scatter", "gateup", "down", "shared_down_combine"]
-    else:
-        names = [f"kernel{i}" for i in range(nk)]
-    log("per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_us)))
+        return nk
 
-    # Timed region: one graph replay of exactly K steps.
-    g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step(0, side.cuda_stream)
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        cap = torch.cuda.current_stream(dev).cuda_stream
-        for i in range(args.steps):
-            step(i, cap)
-    torch.cuda.synchronize()
-    g.replay()                       # upload + first launch, untimed
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    us_step = ms_total * 1e3 / args.steps
-    log(f"graph: {us_step:.2f} us/step over {args.steps} steps")
+    names, kern_us, eager_us = time_kernels(timed, args.steps, stream)
+    us_step = time_graph(step, args.steps, dev)
 
     sha = kernel_sources_sha("decode.hip" if T <= 64 else "prefill.hip")
     wl_name = ("block_" if args.block else "") + args.workload
@@ -308,33 +494,19 @@ def main():
                 "traffic": measured_traffic(wl_name, dom_name, sha),
                 "algorithmic_flops_per_launch": flops, "avg_launch_us": round(dom_us, 3)}
 
-    if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib * 2**20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy of {n} bytes done")
+    calibration_copy(args, dev)
 
-    result = {
-        "metric": METRIC,
-        "value": round(us_step, 3),
-        "unit": "us/layer",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(us_step / 1e3, 6),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if fmt == "bf16" else "nvfp4 weights (e2m1 + e4m3 scales), bf16 activations",
-        "data": "synthetic",
-        "config": {"workload": f"flint_moe_{wl_name}", "T": T, "hidden": H,
-                   "n_experts": E, "top_k": K_TOP, "inter": I, "shared_experts": 1,
-                   "router_bias": bias, "seed": args.seed, "n_active": n_active,
-                   "layer_copies": args.copies, "timing": "one HIP-graph replay of K steps",
-                   **({"prenorm_block": {"norm": "RMSNorm", "eps": EPS, "residual_add": True}}
-                      if args.block else {})},
+    config = {"workload": f"flint_moe_{wl_name}", "T": T, "hidden": H,
+              "n_experts": E, "top_k": K_TOP, "inter": I, "shared_experts": 1,
+              "router_bias": bias, "seed": args.seed, "n_active": n_active,
+              "layer_copies": args.copies, "timing": "one HIP-graph replay of K steps",
+              **({"prenorm_block": {"norm": "RMSNorm", "eps": EPS, "residual_add": True}}
+                 if args.block else {})}
+    result = common_result(
+        args, us_step,
+        "bf16" if fmt == "bf16" else "nvfp4 weights (e2m1 + e4m3 scales), bf16 activations",
+        config)
+    result.update({
         "tokens_per_s": round(T / (us_step * 1e-6), 1),
         "layer_algorithmic_bytes": layer_bytes,
         "layer_GBps": round(layer_bytes / (us_step * 1e-6) / 1e9, 1),
@@ -343,9 +515,9 @@ def main():
         "kernels_us": {n: round(float(v), 3) for n, v in zip(names, kern_us)},
         "kernel_timing": "start/stop timestamps of each kernel's execution (hipExtLaunchKernelGGL "
                          "events), averaged over K eager steps",
-        "eager_wall_us_per_step": round(eager_wall * 1e6, 2),
+        "eager_wall_us_per_step": round(eager_us, 2),
         "roofline": roof,
-    }
+    })
     if rank == 0 and args.cpu_baseline_seconds > 0:
         log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(syn, x_bits, bias, args.cpu_baseline_seconds,

@@ -210,6 +210,63 @@ flint_status flint_moe_block_forward_timed(flint_moe_ctx* ctx, const flint_moe_w
 /* Release a context.  NULL is allowed. */
 void flint_moe_destroy(flint_moe_ctx* ctx);
 
+/* ------------------------------------------------------------------------
+ * Dense MLP of Flint's first two layers, which use a dense MLP in place of the
+ * MoE ("vLLM Day-0 Support for Recursive's Flint", section "Flint Model
+ * Architecture", bullet "MoE Structure").  Its form is read as the experts'
+ * SwiGLU ("Flint on Arc Pro B70", section "norm.py: Triton kernels that
+ * assumed CUDA"); its intermediate size I_d is not on the pages and is a
+ * parameter here.  For token t with bf16 input x_t[H]:
+ *   h_t   = silu(W13[0:I_d] x_t) * (W13[I_d:2 I_d] x_t)    (fp32, never rounded for T <= 64)
+ *   out_t = bf16_rne( W2 h_t )                             (fp32 accumulate)
+ * and with a norm gain (the pre-norm block, as for flint_moe_block_forward):
+ *   out_t = bf16_rne( r_t + W2 h(n_t) ),  n_t = bf16_rne(RMSNorm(r_t) * gamma)
+ * T <= 64 runs GEMV kernels; larger T runs MFMA GEMMs that keep h in fp16
+ * between the two products.  Same conventions as the layer above (caller-owned
+ * memory, asynchronous on `stream`, host-side validation). */
+typedef struct flint_mlp_ctx flint_mlp_ctx; /* opaque, host memory */
+
+typedef struct flint_mlp_config {
+  int32_t hidden;      /* H: must be 2048 */
+  int32_t inter;       /* I_d: a multiple of 512 in [512, 32768] */
+  int32_t max_tokens;  /* >= 1 */
+} flint_mlp_config;
+
+typedef struct flint_mlp_ws_layout {
+  size_t total_bytes;
+  size_t normed;  /* bf16 [T][H]: n (pre-norm block only) */
+  size_t h;       /* [T][I_d]: fp32 for T <= 64, fp16 above */
+} flint_mlp_ws_layout;
+
+/* INVALID_ARG for NULL or out-of-range fields, UNSUPPORTED for H != 2048. */
+flint_status flint_mlp_init(const flint_mlp_config* cfg, flint_mlp_ctx** ctx_out);
+size_t flint_mlp_workspace_bytes(const flint_mlp_ctx* ctx, int32_t T);  /* 0 for T <= 0 */
+flint_status flint_mlp_workspace_layout(const flint_mlp_ctx* ctx, int32_t T,
+                                        flint_mlp_ws_layout* layout);
+
+/* One forward over T tokens.
+ *   w13   device bf16 [2 I_d][H] (rows [0, I_d) gate, [I_d, 2 I_d) up), 16-byte aligned
+ *   w2    device bf16 [H][I_d], 16-byte aligned
+ *   gamma device bf16 [H] or NULL: NULL runs the bare MLP on x; otherwise x is the
+ *         residual stream r and the pre-norm block is computed (eps finite, >= 0)
+ *   x     device bf16 [T][H];  out device bf16 [T][H] (must not overlap x)
+ *   workspace device, >= flint_mlp_workspace_bytes(ctx, T), 256-byte aligned
+ * T == 0 is a no-op; T < 0 or T > max_tokens: INVALID_ARG. */
+flint_status flint_mlp_forward(flint_mlp_ctx* ctx, const uint16_t* w13, const uint16_t* w2,
+                               const uint16_t* gamma, float eps, const uint16_t* x, int32_t T,
+                               uint16_t* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* flint_mlp_forward with the per-kernel timing of flint_moe_forward_timed. */
+flint_status flint_mlp_forward_timed(flint_mlp_ctx* ctx, const uint16_t* w13, const uint16_t* w2,
+                                     const uint16_t* gamma, float eps, const uint16_t* x,
+                                     int32_t T, uint16_t* out, void* workspace,
+                                     size_t workspace_bytes, void* stream, void* const* events,
+                                     int32_t n_events, int32_t* n_kernels);
+
+void flint_mlp_destroy(flint_mlp_ctx* ctx);                   /* NULL-safe */
+const char* flint_mlp_last_error(const flint_mlp_ctx* ctx);  /* "" if none */
+
 /* Static name of a status code. */
 const char* flint_moe_status_string(flint_status s);
 

@@ -107,17 +107,20 @@ template <>
 struct GateUpRows<false> {
   u32x4 w[4][kVecPerLaneH];
   float g;  // tensor scale (1 for bf16)
-  __device__ __forceinline__ void load(const Bank& bank, int e, int p0) {
-    const uint16_t* w13 = reinterpret_cast<const uint16_t*>(bank.w13) + (size_t)e * 2 * I * H;
+  // Gate rows p, p+1 and up rows inter+p, inter+p+1 of a w13 [2 inter][H].
+  __device__ __forceinline__ void load_rows(const uint16_t* w13, int inter, int p0) {
     const int lane = threadIdx.x & (kWave - 1);
     const int p = p0 + 2 * (threadIdx.x / kWave);
-    const int row[4] = {p, p + 1, I + p, I + p + 1};
+    const int row[4] = {p, p + 1, inter + p, inter + p + 1};
 #pragma unroll
     for (int i = 0; i < kVecPerLaneH; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         w[r][i] = reinterpret_cast<const u32x4*>(w13 + (size_t)row[r] * H)[lane + i * kWave];
     g = 1.0f;
+  }
+  __device__ __forceinline__ void load(const Bank& bank, int e, int p0) {
+    load_rows(reinterpret_cast<const uint16_t*>(bank.w13) + (size_t)e * 2 * I * H, I, p0);
   }
   __device__ __forceinline__ float dot(int r, int i, const u32x4& xv, float acc) const {
     return dot8_bf16(w[r][i], xv, acc);
@@ -177,7 +180,7 @@ struct GateUpRows<true> {
 template <bool kFp4>
 __device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int count,
                                                const TokenList& list, const uint16_t* __restrict__ x,
-                                               float* h, u32x4* xs) {
+                                               float* h, u32x4* xs, int hstride = I) {
   const int lane = threadIdx.x & (kWave - 1);
   const int p = p0 + 2 * (threadIdx.x / kWave);
   // The first chunk's x rows are requested while the weights are still in
@@ -203,7 +206,7 @@ __device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = wave_sum_lane63(acc[r]) * wv.g;
       if (lane == kWave - 1) {
-        float* hr = h + (size_t)list.hrow(c0 + j) * I + p;
+        float* hr = h + (size_t)list.hrow(c0 + j) * hstride + p;
         hr[0] = silu(acc[0]) * acc[2];
         hr[1] = silu(acc[1]) * acc[3];
       }
@@ -797,7 +800,120 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- dense MLP
+
+// Gate/up of the dense MLP: block u computes gate rows [8u, 8u + 8) and the
+// matching up rows of w13 [2 I_d][H] for all T tokens (the routed gate/up
+// scheme with the whole MLP as one group of tokens), h fp32 [T][I_d].
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
+void dense_gateup_kernel(DenseArgs a) {
+  __shared__ u32x4 xs[kXChunk * kVecH];
+  const int p0 = blockIdx.x * kPairsPerItem;
+  GateUpRows<false> wv;
+  wv.load_rows(a.w13, a.inter, p0);
+  gateup_compute(wv, p0, a.T, TokenList{nullptr, 1, 0}, a.x, a.h, xs, a.inter);
+}
+
+// Down of the dense MLP: block b owns output rows [8b, 8b + 8) for every
+// token; wave w takes the 512-column K chunks w, w + 8, ... of those rows
+// (lane l: columns [8l, 8l + 8) of a chunk), with the next chunk's rows in
+// flight while it computes.  Tokens go in groups of 8 whose lane partials
+// stay in registers across all of the wave's chunks and are reduced across
+// lanes once per token; the 8 waves' sums meet in LDS and are added in wave
+// order, then r (pre-norm block) and one bf16 rounding.
+constexpr int kDenseG = 8;
+
+// One wave's 8 rows x 8 columns of a w2 chunk, widened to fp32.
+struct DenseW2Rows {
+  u32x4 w[kDownRowsPerBlock];
+  __device__ __forceinline__ void load(const DenseArgs& a, int r0, int c) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int r = 0; r < kDownRowsPerBlock; ++r)
+      w[r] = reinterpret_cast<const u32x4*>(a.w2 + (size_t)(r0 + r) * a.inter + c * kDenseChunk)[lane];
+  }
+  __device__ __forceinline__ void widen(float (&f)[kDownRowsPerBlock][8]) const {
+#pragma unroll
+    for (int r = 0; r < kDownRowsPerBlock; ++r) {
+      f[r][0] = bf16_lo(w[r].x); f[r][1] = bf16_hi(w[r].x);
+      f[r][2] = bf16_lo(w[r].y); f[r][3] = bf16_hi(w[r].y);
+      f[r][4] = bf16_lo(w[r].z); f[r][5] = bf16_hi(w[r].z);
+      f[r][6] = bf16_lo(w[r].w); f[r][7] = bf16_hi(w[r].w);
+    }
+  }
+};
+
+__device__ __forceinline__ void dense_accumulate(const DenseArgs& a, const float (&wf)[kDownRowsPerBlock][8],
+                                                 int c, int t0, int G,
+                                                 float (&acc)[kDenseG][kDownRowsPerBlock]) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int t = 0; t < kDenseG; ++t) {
+    if (t < G) {
+      const f32x4* hp = reinterpret_cast<const f32x4*>(a.h + (size_t)(t0 + t) * a.inter + c * kDenseChunk) + lane * 2;
+      const f32x4 h0 = hp[0], h1 = hp[1];
+      const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+      for (int r = 0; r < kDownRowsPerBlock; ++r) {
+        float s = acc[t][r];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(wf[r][i], hv[i], s);
+        acc[t][r] = s;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kDownThreads) void dense_down_kernel(DenseArgs a) {
+  __shared__ float part[kDownWaves * kDenseG * kDownRowsPerBlock];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int r0 = blockIdx.x * kDownRowsPerBlock;
+  const int C = a.inter / kDenseChunk;
+  for (int t0 = 0; t0 < a.T; t0 += kDenseG) {
+    const int G = min(kDenseG, a.T - t0);
+    float acc[kDenseG][kDownRowsPerBlock];
+#pragma unroll
+    for (int t = 0; t < kDenseG; ++t)
+#pragma unroll
+      for (int r = 0; r < kDownRowsPerBlock; ++r) acc[t][r] = 0.f;
+    // The next chunk's rows are requested as soon as the current ones are
+    // widened, so one chunk is always in flight while the wave computes.
+    DenseW2Rows p;
+    if (wave < C) p.load(a, r0, wave);
+    for (int c = wave; c < C; c += kDownWaves) {
+      float wf[kDownRowsPerBlock][8];
+      p.widen(wf);
+      if (c + kDownWaves < C) p.load(a, r0, c + kDownWaves);
+      dense_accumulate(a, wf, c, t0, G, acc);
+    }
+#pragma unroll
+    for (int t = 0; t < kDenseG; ++t) {
+      const float tot = wave_sum8_transposed(acc[t]);
+      if (lane < kDownRowsPerBlock)
+        part[(wave * kDenseG + t) * kDownRowsPerBlock + bitrev3(lane)] = tot;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < G * kDownRowsPerBlock) {
+      const int t = threadIdx.x / kDownRowsPerBlock;
+      const int r = threadIdx.x - t * kDownRowsPerBlock;
+      float o = 0.f;
+      for (int w = 0; w < kDownWaves; ++w) o += part[(w * kDenseG + t) * kDownRowsPerBlock + r];
+      const size_t idx = (size_t)(t0 + t) * H + r0 + r;
+      if (a.resid) o += bf16_lo(a.resid[idx]);
+      a.out[idx] = f32_to_bf16_rne(o);
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dense_decode(const DenseArgs& a, hipStream_t stream, Launcher& launch) {
+  launch(dense_gateup_kernel, dim3(a.inter / kPairsPerItem), dim3(kThreads), stream, a);
+  launch(dense_down_kernel, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  return hipGetLastError();
+}
 
 template <bool kFp4>
 static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Launcher& launch) {

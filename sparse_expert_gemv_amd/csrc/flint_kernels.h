@@ -104,6 +104,30 @@ struct Launcher {
   }
 };
 
+// Dense SwiGLU MLP (Flint's layers 0 and 1): out = W2 (silu(W13[0:I] x) *
+// W13[I:2I] x) (+ r for the pre-norm block), bf16 weights.
+constexpr int kDenseChunk = 512;          // K columns of w2 per decode work item
+constexpr int kDenseMaxInter = 32768;     // I_d upper bound (multiple of kDenseChunk)
+struct DenseArgs {
+  const uint16_t* x;       // [T][H] the MLP's input (the block's normalised r)
+  uint16_t* out;           // [T][H]
+  const uint16_t* resid;   // r [T][H] for the pre-norm block, else nullptr
+  const uint16_t* w13;     // [2 I][H], rows [0, I) gate, [I, 2I) up
+  const uint16_t* w2;      // [H][I]
+  float* h;                // [T][I] fp32 (decode-sized T)
+  _Float16* h16;           // [T][I] fp16 (prefill-sized T)
+  int T, inter;
+};
+
+// RMSNorm of T rows of kHidden: n = bf16(r / sqrt(mean(r^2) + eps) * gamma),
+// one wave per row.
+void launch_rmsnorm(const uint16_t* r, const uint16_t* gamma, float eps, uint16_t* n, int T,
+                    hipStream_t stream, Launcher& launch);
+
+// The dense MLP for T <= kDecodeMaxT (GEMV kernels) and for larger T (MFMA).
+hipError_t launch_dense_decode(const DenseArgs& a, hipStream_t stream, Launcher& launch);
+hipError_t launch_dense_prefill(const DenseArgs& a, hipStream_t stream, Launcher& launch);
+
 // The decode path (T <= kDecodeMaxT) for bf16 or NVFP4 expert weights.
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, Launcher& launch);
 

@@ -20,6 +20,11 @@ struct flint_moe_ctx {
   std::string last_error;
 };
 
+struct flint_mlp_ctx {
+  flint_mlp_config cfg;
+  std::string last_error;
+};
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -333,5 +338,149 @@ FLINT_API const char* flint_moe_status_string(flint_status s) {
 }
 
 FLINT_API const char* flint_moe_last_error(const flint_moe_ctx* ctx) {
+  return ctx ? ctx->last_error.c_str() : "";
+}
+
+// ---------------------------------------------------------------- dense MLP
+
+namespace {
+
+void mlp_layout(const flint_mlp_config& c, int32_t T, flint_mlp_ws_layout* L) {
+  const size_t t = (size_t)T, H = (size_t)c.hidden, I = (size_t)c.inter;
+  const bool prefill = T > flint::kDecodeMaxT;
+  size_t o = 0;
+  L->normed = o; o = align_up(o + t * H * sizeof(uint16_t));
+  L->h = o;      o = align_up(o + t * I * (prefill ? sizeof(uint16_t) : sizeof(float)));
+  L->total_bytes = o;
+}
+
+flint_status mlp_fail(flint_mlp_ctx* ctx, flint_status s, const std::string& why) {
+  if (ctx) ctx->last_error = why;
+  return s;
+}
+
+flint_status mlp_forward_impl(flint_mlp_ctx* ctx, const uint16_t* w13, const uint16_t* w2,
+                              const uint16_t* gamma, float eps, const uint16_t* x, int32_t T,
+                              uint16_t* out, void* workspace, size_t workspace_bytes, void* stream,
+                              flint::Launcher& launch) {
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  ctx->last_error.clear();
+  const flint_mlp_config& c = ctx->cfg;
+  if (T < 0 || T > c.max_tokens) {
+    char buf[128];
+    std::snprintf(buf, sizeof buf, "T=%d outside [0, max_tokens=%d]", T, c.max_tokens);
+    return mlp_fail(ctx, FLINT_ERR_INVALID_ARG, buf);
+  }
+  if (T == 0) return FLINT_OK;
+  if (!w13 || !w2 || !x || !out || !workspace)
+    return mlp_fail(ctx, FLINT_ERR_INVALID_ARG, "w13, w2, x, out and workspace must be non-NULL");
+  const void* p16[] = {w13, w2, x, out};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return mlp_fail(ctx, FLINT_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (gamma && !aligned(gamma, 16))
+    return mlp_fail(ctx, FLINT_ERR_INVALID_ARG, "gamma must be 16-byte aligned");
+  if (gamma && !(std::isfinite(eps) && eps >= 0.f))
+    return mlp_fail(ctx, FLINT_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!aligned(workspace, kAlign))
+    return mlp_fail(ctx, FLINT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t act_bytes = (size_t)T * c.hidden * sizeof(uint16_t);
+  if (ranges_overlap(x, act_bytes, out, act_bytes))
+    return mlp_fail(ctx, FLINT_ERR_INVALID_ARG, "out overlaps x");
+  flint_mlp_ws_layout L;
+  mlp_layout(c, T, &L);
+  if (workspace_bytes < L.total_bytes) {
+    char buf[160];
+    std::snprintf(buf, sizeof buf, "workspace of %zu bytes, %zu needed for T=%d", workspace_bytes,
+                  L.total_bytes, T);
+    return mlp_fail(ctx, FLINT_ERR_WORKSPACE, buf);
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  flint::DenseArgs a{};
+  a.x = x;
+  a.out = out;
+  a.w13 = w13;
+  a.w2 = w2;
+  a.T = T;
+  a.inter = c.inter;
+  const bool prefill = T > flint::kDecodeMaxT;
+  if (prefill)
+    a.h16 = reinterpret_cast<_Float16*>(ws + L.h);
+  else
+    a.h = reinterpret_cast<float*>(ws + L.h);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (gamma) {
+    uint16_t* normed = reinterpret_cast<uint16_t*>(ws + L.normed);
+    flint::launch_rmsnorm(x, gamma, eps, normed, T, s, launch);
+    a.x = normed;
+    a.resid = x;
+  }
+  const hipError_t err = prefill ? flint::launch_dense_prefill(a, s, launch)
+                                 : flint::launch_dense_decode(a, s, launch);
+  if (err != hipSuccess) return mlp_fail(ctx, FLINT_ERR_HIP, hipGetErrorString(err));
+  return FLINT_OK;
+}
+
+}  // namespace
+
+FLINT_API flint_status flint_mlp_init(const flint_mlp_config* cfg, flint_mlp_ctx** ctx_out) {
+  if (!cfg || !ctx_out) return FLINT_ERR_INVALID_ARG;
+  if (cfg->hidden <= 0 || cfg->max_tokens <= 0 || cfg->inter <= 0) return FLINT_ERR_INVALID_ARG;
+  if (cfg->inter % flint::kDenseChunk != 0 || cfg->inter > flint::kDenseMaxInter)
+    return FLINT_ERR_INVALID_ARG;
+  if (cfg->hidden != flint::kHidden) return FLINT_ERR_UNSUPPORTED;
+  flint_mlp_ctx* ctx = new (std::nothrow) flint_mlp_ctx;
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  ctx->cfg = *cfg;
+  *ctx_out = ctx;
+  return FLINT_OK;
+}
+
+FLINT_API size_t flint_mlp_workspace_bytes(const flint_mlp_ctx* ctx, int32_t T) {
+  if (!ctx || T <= 0) return 0;
+  flint_mlp_ws_layout L;
+  mlp_layout(ctx->cfg, T, &L);
+  return L.total_bytes;
+}
+
+FLINT_API flint_status flint_mlp_workspace_layout(const flint_mlp_ctx* ctx, int32_t T,
+                                                  flint_mlp_ws_layout* layout) {
+  if (!ctx || !layout || T <= 0) return FLINT_ERR_INVALID_ARG;
+  mlp_layout(ctx->cfg, T, layout);
+  return FLINT_OK;
+}
+
+FLINT_API flint_status flint_mlp_forward(flint_mlp_ctx* ctx, const uint16_t* w13, const uint16_t* w2,
+                                         const uint16_t* gamma, float eps, const uint16_t* x,
+                                         int32_t T, uint16_t* out, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  flint::Launcher launch;
+  return mlp_forward_impl(ctx, w13, w2, gamma, eps, x, T, out, workspace, workspace_bytes, stream,
+                          launch);
+}
+
+FLINT_API flint_status flint_mlp_forward_timed(flint_mlp_ctx* ctx, const uint16_t* w13,
+                                               const uint16_t* w2, const uint16_t* gamma, float eps,
+                                               const uint16_t* x, int32_t T, uint16_t* out,
+                                               void* workspace, size_t workspace_bytes,
+                                               void* stream, void* const* events, int32_t n_events,
+                                               int32_t* n_kernels) {
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  if (!events || n_events < 16 || !n_kernels)
+    return mlp_fail(ctx, FLINT_ERR_INVALID_ARG, "events (>= 16) and n_kernels are required");
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return mlp_fail(ctx, FLINT_ERR_INVALID_ARG, "NULL event handle");
+  flint::Launcher launch;
+  launch.events = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  launch.n = n_events;
+  const flint_status st = mlp_forward_impl(ctx, w13, w2, gamma, eps, x, T, out, workspace,
+                                           workspace_bytes, stream, launch);
+  *n_kernels = launch.used;
+  return st;
+}
+
+FLINT_API void flint_mlp_destroy(flint_mlp_ctx* ctx) { delete ctx; }
+
+FLINT_API const char* flint_mlp_last_error(const flint_mlp_ctx* ctx) {
   return ctx ? ctx->last_error.c_str() : "";
 }

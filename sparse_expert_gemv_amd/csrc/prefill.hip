@@ -263,16 +263,19 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
 }
 
 using RouterGemm = BlockGemm<kMT, kMaxExperts, 1, 4, false, 3, 32>;
-// Pre-norm block: n = bf16(r / rms(r) * gamma), one wave per token; lane l
+// RMSNorm rows: n = bf16(r / rms(r) * gamma), one wave per token; lane l
 // owns the 16-byte vectors l, l + 64, l + 128, l + 192 of the row.
 constexpr int kNormVecPerLane = H / 8 / 64;   // 4
 
-__global__ __launch_bounds__(kThreads) void prefill_norm_kernel(LayerArgs a) {
+__global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const uint16_t* __restrict__ r,
+                                                          const uint16_t* __restrict__ gamma,
+                                                          float eps, uint16_t* __restrict__ n,
+                                                          int T) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kThreads / 64) + (int)(threadIdx.x / 64);
-  if (t >= a.T) return;
-  const u32x4* row = reinterpret_cast<const u32x4*>(a.resid + (size_t)t * H);
-  const u32x4* gam = reinterpret_cast<const u32x4*>(a.norm_w);
+  if (t >= T) return;
+  const u32x4* row = reinterpret_cast<const u32x4*>(r + (size_t)t * H);
+  const u32x4* gam = reinterpret_cast<const u32x4*>(gamma);
   u32x4 rv[kNormVecPerLane], gv[kNormVecPerLane];
   float ss = 0.f;
 #pragma unroll
@@ -284,8 +287,8 @@ __global__ __launch_bounds__(kThreads) void prefill_norm_kernel(LayerArgs a) {
   for (int i = 0; i < kNormVecPerLane; ++i) ss += sumsq_bf16x8(rv[i]);
   ss = wave_sum_lane63(ss);
   const float inv = rms_inv<H>(__builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                   __builtin_bit_cast(int, ss), 63)), a.eps);
-  u32x4* dst = reinterpret_cast<u32x4*>(a.normed + (size_t)t * H);
+                                   __builtin_bit_cast(int, ss), 63)), eps);
+  u32x4* dst = reinterpret_cast<u32x4*>(n + (size_t)t * H);
 #pragma unroll
   for (int i = 0; i < kNormVecPerLane; ++i) dst[lane + 64 * i] = rms_scale_bf16x8(rv[i], gv[i], inv);
 }
@@ -729,7 +732,115 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_shared_combine_kernel(Lay
   }
 }
 
+// ---------------------------------------------------------------- dense MLP
+
+// Gate/up GEMM of the dense MLP (layers 0 and 1): tile (128 tokens, 128 h
+// columns) with the gate and up rows of w13 [2 I_d][H] as B, SiLU-and-mul
+// epilogue, h fp16 [T][I_d].  Items run token-tile-major so that the column
+// blocks of one token tile share its x rows on one XCD.
+__global__ __launch_bounds__(kThreads, 2) void dense_gateup_gemm_kernel(DenseArgs a, int n_items) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GateUpGemm::kLds];
+  const int item = xcd_item(n_items);
+  if (item >= n_items) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / 2, wn = wave % 2;
+  const int n_cb = a.inter / 128;
+  const int q = item / n_cb, nb = item % n_cb;
+  const int start = q * kGM, count = min(kGM, a.T - start);
+  const uint16_t* ag[GateUpGemm::NA];
+  const uint16_t* bg[GateUpGemm::NB];
+#pragma unroll
+  for (int i = 0; i < GateUpGemm::NA; ++i) {
+    const int fr = GateUpGemm::fetch_row_a(i);
+    ag[i] = a.x + (size_t)(start + min(fr, count - 1)) * H + GateUpGemm::chunk_elems(fr);
+  }
+#pragma unroll
+  for (int i = 0; i < GateUpGemm::NB; ++i) {
+    const int n = GateUpGemm::fetch_row_b(i);
+    const int bw = n >> 7, ct = (n >> 5) & 3;
+    const int col = nb * 128 + bw * 64 + (ct & 1) * 32 + (n & 31);
+    bg[i] = a.w13 + (size_t)((ct >> 1) * a.inter + col) * H + GateUpGemm::chunk_elems(n);
+  }
+  const int rt_n = max(0, min(GateUpGemm::RT, (count - wm * GateUpGemm::TM + 31) / 32));
+  GateUpGemm g;
+  g.run(lds, ag, bg, H, rt_n);
+#pragma unroll
+  for (int rt = 0; rt < GateUpGemm::RT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * GateUpGemm::TM + rt * 32 + acc_row(r, lane);
+      if (row < count) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const int col = nb * 128 + wn * 64 + ct * 32 + (lane & 31);
+          const float gv = g.acc[rt][ct][r], uv = g.acc[rt][ct + 2][r];
+          a.h16[(size_t)(start + row) * a.inter + col] = (_Float16)(silu(gv) * uv);
+        }
+      }
+    }
+}
+
+// Down GEMM of the dense MLP: tile (128 tokens, 256 output columns), h fp16
+// times w2 (widened to fp16 into LDS), K = I_d; epilogue adds r for the
+// pre-norm block and rounds once to bf16.
+__global__ __launch_bounds__(kThreads, 2) void dense_down_gemm_kernel(DenseArgs a, int n_items) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemm::kLds];
+  const int item = xcd_item(n_items);
+  if (item >= n_items) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / 2, wn = wave % 2;
+  const int q = item / kDnColBlocks, nb = item % kDnColBlocks;
+  const int start = q * kGM, count = min(kGM, a.T - start);
+  const uint16_t* h16 = reinterpret_cast<const uint16_t*>(a.h16);
+  const uint16_t* ag[DownGemm::NA];
+  const uint16_t* bg[DownGemm::NB];
+#pragma unroll
+  for (int i = 0; i < DownGemm::NA; ++i) {
+    const int fr = DownGemm::fetch_row_a(i);
+    ag[i] = h16 + (size_t)(start + min(fr, count - 1)) * a.inter + DownGemm::chunk_elems(fr);
+  }
+#pragma unroll
+  for (int i = 0; i < DownGemm::NB; ++i) {
+    const int n = DownGemm::fetch_row_b(i);
+    bg[i] = a.w2 + (size_t)(nb * 256 + n) * a.inter + DownGemm::chunk_elems(n);
+  }
+  const int rt_n = max(0, min(DownGemm::RT, (count - wm * DownGemm::TM + 31) / 32));
+  DownGemm g;
+  g.run(lds, ag, bg, a.inter, rt_n);
+#pragma unroll
+  for (int rt = 0; rt < DownGemm::RT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * DownGemm::TM + rt * 32 + acc_row(r, lane);
+      if (row < count) {
+#pragma unroll
+        for (int ct = 0; ct < DownGemm::CT; ++ct) {
+          const int col = nb * 256 + wn * DownGemm::TN + ct * 32 + (lane & 31);
+          const size_t idx = (size_t)(start + row) * H + col;
+          float o = g.acc[rt][ct][r];
+          if (a.resid) o += bf16_lo(a.resid[idx]);
+          a.out[idx] = f32_to_bf16_rne(o);
+        }
+      }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_dense_prefill(const DenseArgs& a, hipStream_t stream, Launcher& launch) {
+  const int n_tiles = (a.T + kGM - 1) / kGM;
+  const int n_gu = n_tiles * (a.inter / 128);
+  launch(dense_gateup_gemm_kernel, dim3(round8(n_gu)), dim3(kThreads), stream, a, n_gu);
+  const int n_dn = n_tiles * kDnColBlocks;
+  launch(dense_down_gemm_kernel, dim3(round8(n_dn)), dim3(kThreads), stream, a, n_dn);
+  return hipGetLastError();
+}
+
+void launch_rmsnorm(const uint16_t* r, const uint16_t* gamma, float eps, uint16_t* n, int T,
+                    hipStream_t stream, Launcher& launch) {
+  launch(rmsnorm_kernel, dim3((T + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), stream, r,
+         gamma, eps, n, T);
+}
 
 int prefill_tiles_max(int T, int E, int k) {
   return (T * k + kGM - 1) / kGM + E;  // sum over experts of ceil(count / 128)
@@ -739,9 +850,7 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& laun
   const int nb = (a.T + kMT - 1) / kMT;
   const int n_routed_max = prefill_tiles_max(a.T, a.E, a.k);
   const int n_shared = (a.T + kGM - 1) / kGM;
-  if (a.norm_w)
-    launch(prefill_norm_kernel, dim3((a.T + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads),
-           stream, a);
+  if (a.norm_w) launch_rmsnorm(a.resid, a.norm_w, a.eps, a.normed, a.T, stream, launch);
   launch(prefill_router_kernel, dim3(nb), dim3(kThreads), stream, a);
   launch(prefill_scan_kernel, dim3(1), dim3(kScanThreads), stream, a, nb);
   launch(prefill_scatter_kernel, dim3(nb), dim3(kThreads), stream, a);

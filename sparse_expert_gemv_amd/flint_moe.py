@@ -40,6 +40,13 @@ ABI_SYMBOLS = (
     "flint_moe_destroy",
     "flint_moe_status_string",
     "flint_moe_last_error",
+    "flint_mlp_init",
+    "flint_mlp_workspace_bytes",
+    "flint_mlp_workspace_layout",
+    "flint_mlp_forward",
+    "flint_mlp_forward_timed",
+    "flint_mlp_destroy",
+    "flint_mlp_last_error",
 )
 
 
@@ -65,6 +72,15 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("total_bytes", "header", "logits", "topk_ids", "topk_w",
                  "route", "h", "extra", "normed")]
+
+
+class MlpConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32)]
+
+
+class MlpWsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("total_bytes", "normed", "h")]
 
 
 class FlintError(RuntimeError):
@@ -108,6 +124,23 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                   ctypes.POINTER(P), ctypes.c_int32,
                                                   ctypes.POINTER(ctypes.c_int32)]
     lib.flint_moe_block_forward_timed.restype = ctypes.c_int
+    lib.flint_mlp_init.argtypes = [ctypes.POINTER(MlpConfig), ctypes.POINTER(P)]
+    lib.flint_mlp_init.restype = ctypes.c_int
+    lib.flint_mlp_workspace_bytes.argtypes = [P, ctypes.c_int32]
+    lib.flint_mlp_workspace_bytes.restype = ctypes.c_size_t
+    lib.flint_mlp_workspace_layout.argtypes = [P, ctypes.c_int32, ctypes.POINTER(MlpWsLayout)]
+    lib.flint_mlp_workspace_layout.restype = ctypes.c_int
+    lib.flint_mlp_forward.argtypes = [P, P, P, P, ctypes.c_float, P, ctypes.c_int32, P, P,
+                                      ctypes.c_size_t, P]
+    lib.flint_mlp_forward.restype = ctypes.c_int
+    lib.flint_mlp_forward_timed.argtypes = [P, P, P, P, ctypes.c_float, P, ctypes.c_int32, P, P,
+                                            ctypes.c_size_t, P, ctypes.POINTER(P), ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int32)]
+    lib.flint_mlp_forward_timed.restype = ctypes.c_int
+    lib.flint_mlp_destroy.argtypes = [P]
+    lib.flint_mlp_destroy.restype = None
+    lib.flint_mlp_last_error.argtypes = [P]
+    lib.flint_mlp_last_error.restype = ctypes.c_char_p
     lib.flint_moe_destroy.argtypes = [P]
     lib.flint_moe_destroy.restype = None
     lib.flint_moe_status_string.argtypes = [ctypes.c_int]
@@ -270,6 +303,76 @@ class FlintMoE:
         import torch
         n = max(self.workspace_bytes(T), HEADER_BYTES)
         return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+class FlintMLP:
+    """The dense SwiGLU MLP of Flint's layers 0 and 1 (a ``flint_mlp_ctx``)."""
+
+    def __init__(self, inter=14336, hidden=2048, max_tokens=64):
+        self.lib = load_library()
+        self.cfg = MlpConfig(hidden, inter, max_tokens)
+        h = ctypes.c_void_p()
+        st = self.lib.flint_mlp_init(ctypes.byref(self.cfg), ctypes.byref(h))
+        if st != FLINT_OK:
+            raise FlintError(st, f"flint_mlp_init: {status_string(st)}")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.flint_mlp_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, T: int) -> int:
+        return int(self.lib.flint_mlp_workspace_bytes(self.handle, T))
+
+    def workspace_layout(self, T: int) -> dict:
+        L = MlpWsLayout()
+        st = self.lib.flint_mlp_workspace_layout(self.handle, T, ctypes.byref(L))
+        if st != FLINT_OK:
+            raise FlintError(st, f"flint_mlp_workspace_layout: {status_string(st)}")
+        return {n: getattr(L, n) for n, _ in MlpWsLayout._fields_}
+
+    def last_error(self) -> str:
+        return self.lib.flint_mlp_last_error(self.handle).decode()
+
+    def new_workspace(self, T: int, device):
+        import torch
+        return torch.empty(max(self.workspace_bytes(T), 256), dtype=torch.uint8, device=device)
+
+    def forward_raw(self, w13_ptr, w2_ptr, gamma_ptr, eps, x_ptr, T, out_ptr, ws_ptr, ws_bytes,
+                    stream_ptr) -> int:
+        return self.lib.flint_mlp_forward(self.handle, w13_ptr, w2_ptr, gamma_ptr, float(eps), x_ptr,
+                                          T, out_ptr, ws_ptr, ws_bytes, stream_ptr)
+
+    def forward_timed_raw(self, w13_ptr, w2_ptr, gamma_ptr, eps, x_ptr, T, out_ptr, ws_ptr,
+                          ws_bytes, stream_ptr, event_handles) -> tuple:
+        n = len(event_handles)
+        arr = (ctypes.c_void_p * n)(*event_handles)
+        nk = ctypes.c_int32(0)
+        st = self.lib.flint_mlp_forward_timed(self.handle, w13_ptr, w2_ptr, gamma_ptr, float(eps),
+                                              x_ptr, T, out_ptr, ws_ptr, ws_bytes, stream_ptr, arr,
+                                              n, ctypes.byref(nk))
+        return st, nk.value
+
+    def forward(self, w13, w2, x, out, gamma=None, eps=1e-6, workspace=None, stream=None) -> None:
+        """out = MLP(x), or x + MLP(RMSNorm(x) * gamma) when gamma is given.  Raises on error."""
+        import torch
+        T = int(x.shape[0])
+        if workspace is None:
+            workspace = self.new_workspace(T, x.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        st = self.forward_raw(_ptr(w13), _ptr(w2), _ptr(gamma), eps, _ptr(x), T, _ptr(out),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              stream.cuda_stream)
+        if st != FLINT_OK:
+            raise FlintError(st, f"flint_mlp_forward: {status_string(st)}: {self.last_error()}")
 
 
 def bf16_tensor(bits, device):

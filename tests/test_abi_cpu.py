@@ -18,7 +18,7 @@ def declared_symbols():
     for fn in os.listdir(os.path.join(ROOT, "include")):
         if fn.endswith(".h"):
             src = open(os.path.join(ROOT, "include", fn)).read()
-            names |= set(re.findall(r"\b(flint_moe_\w+)\s*\(", src))
+            names |= set(re.findall(r"\b(flint_(?:moe|mlp)_\w+)\s*\(", src))
     return names
 
 
@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = sg.load_library()
     decl = declared_symbols()
     assert decl, "no declarations found"
-    assert decl == set(sg.ABI_SYMBOLS) | (decl - set(sg.ABI_SYMBOLS))
+    assert decl == set(sg.ABI_SYMBOLS)
     for name in decl:
         assert hasattr(lib, name), name
 
@@ -143,3 +143,46 @@ def test_workspace_has_a_normed_region():
         assert lay["normed"] >= lay["route"] + (2 + 2 * 256 + T * 6) * 4
         assert lay["normed"] + T * 2048 * 2 <= min(v for k, v in lay.items()
                                                     if v > lay["normed"] or k == "total_bytes")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(inter=0), sg.FLINT_ERR_INVALID_ARG),
+    (dict(inter=700), sg.FLINT_ERR_INVALID_ARG),
+    (dict(inter=32768 + 512), sg.FLINT_ERR_INVALID_ARG),
+    (dict(max_tokens=0), sg.FLINT_ERR_INVALID_ARG),
+    (dict(hidden=1024), sg.FLINT_ERR_UNSUPPORTED),
+])
+def test_mlp_init_rejects(kw, status):
+    with pytest.raises(sg.FlintError) as e:
+        sg.FlintMLP(**kw)
+    assert e.value.status == status
+
+
+def test_mlp_workspace_and_host_validation_without_gpu():
+    m = sg.FlintMLP(inter=1024, max_tokens=128)
+    assert m.workspace_bytes(0) == 0
+    lay = m.workspace_layout(8)
+    assert lay["normed"] == 0 and lay["h"] >= 8 * 2048 * 2 and lay["h"] % 256 == 0
+    assert lay["total_bytes"] >= lay["h"] + 8 * 1024 * 4          # fp32 h for T <= 64
+    lay = m.workspace_layout(100)
+    assert lay["total_bytes"] >= lay["h"] + 100 * 1024 * 2        # fp16 h above
+    w13, w2, g, x, out, ws = 1 << 28, 1 << 29, 1 << 27, 1 << 30, 1 << 31, 1 << 32
+    need = m.workspace_bytes(4)
+    f = lambda **k: m.forward_raw(k.get("w13", w13), k.get("w2", w2), k.get("g", g),
+                                  k.get("eps", 1e-6), k.get("x", x), k.get("T", 4),
+                                  k.get("out", out), k.get("ws", ws), k.get("nbytes", need), None)
+    assert f(T=-1) == sg.FLINT_ERR_INVALID_ARG
+    assert f(T=129) == sg.FLINT_ERR_INVALID_ARG and "max_tokens" in m.last_error()
+    assert f(w13=None) == sg.FLINT_ERR_INVALID_ARG
+    assert f(w2=w2 + 8) == sg.FLINT_ERR_INVALID_ARG and "aligned" in m.last_error()
+    assert f(g=g + 2) == sg.FLINT_ERR_INVALID_ARG and "gamma" in m.last_error()
+    assert f(eps=-1.0) == sg.FLINT_ERR_INVALID_ARG and "eps" in m.last_error()
+    assert f(out=x + 4096) == sg.FLINT_ERR_INVALID_ARG and "overlaps" in m.last_error()
+    assert f(ws=ws + 64) == sg.FLINT_ERR_INVALID_ARG
+    assert f(nbytes=need - 1) == sg.FLINT_ERR_WORKSPACE
+    assert f(T=0, x=None) == sg.FLINT_OK
+    assert m.forward_timed_raw(w13, w2, g, 1e-6, x, 4, out, ws, need, None, [None] * 3)[0] == \
+        sg.FLINT_ERR_INVALID_ARG
+    lib = sg.load_library()
+    assert lib.flint_mlp_init(None, None) == sg.FLINT_ERR_INVALID_ARG
+    lib.flint_mlp_destroy(None)
