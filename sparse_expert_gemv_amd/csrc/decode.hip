@@ -177,7 +177,7 @@ struct GateUpRows<true> {
 // [p0, p0 + 8) of one expert, for `count` tokens, with the wave's rows
 // already loaded (in flight while the token list was fetched); the tokens'
 // x vectors stream through LDS.
-template <bool kFp4>
+template <bool kFp4, int kChunk = kXChunk>
 __device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int count,
                                                const TokenList& list, const uint16_t* __restrict__ x,
                                                float* h, u32x4* xs, int hstride = I) {
@@ -186,12 +186,12 @@ __device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int
   // The first chunk's x rows are requested while the weights are still in
   // flight; the barrier at the top of the loop waits for both.
   auto stage = [&](int c0) {
-    const int n = min(kXChunk, count - c0);
+    const int n = min(kChunk, count - c0);
     for (int j = 0; j < n; ++j) stage_x_row(xs + j * kVecH, x + (size_t)list.tok(c0 + j) * H);
   };
   if (count > 0) stage(0);
-  for (int c0 = 0; c0 < count; c0 += kXChunk) {
-    const int n = min(kXChunk, count - c0);
+  for (int c0 = 0; c0 < count; c0 += kChunk) {
+    const int n = min(kChunk, count - c0);
     wait_vmem_all();
     __syncthreads();
     for (int j = 0; j < n; ++j) {
@@ -211,9 +211,9 @@ __device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int
         hr[1] = silu(acc[1]) * acc[3];
       }
     }
-    if (c0 + kXChunk < count) {
+    if (c0 + kChunk < count) {
       lds_barrier();   // every wave is done with this chunk's x
-      stage(c0 + kXChunk);
+      stage(c0 + kChunk);
     }
   }
 }
@@ -804,14 +804,16 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
 
 // Gate/up of the dense MLP: block u computes gate rows [8u, 8u + 8) and the
 // matching up rows of w13 [2 I_d][H] for all T tokens (the routed gate/up
-// scheme with the whole MLP as one group of tokens), h fp32 [T][I_d].
+// scheme with the whole MLP as one group of tokens, x rows staged 8 at a
+// time since every block sees all T tokens), h fp32 [T][I_d].
+constexpr int kDenseXChunk = 8;   // 32 KiB of x rows in LDS
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void dense_gateup_kernel(DenseArgs a) {
-  __shared__ u32x4 xs[kXChunk * kVecH];
+  __shared__ u32x4 xs[kDenseXChunk * kVecH];
   const int p0 = blockIdx.x * kPairsPerItem;
   GateUpRows<false> wv;
   wv.load_rows(a.w13, a.inter, p0);
-  gateup_compute(wv, p0, a.T, TokenList{nullptr, 1, 0}, a.x, a.h, xs, a.inter);
+  gateup_compute<false, kDenseXChunk>(wv, p0, a.T, TokenList{nullptr, 1, 0}, a.x, a.h, xs, a.inter);
 }
 
 // Down of the dense MLP: block b owns output rows [8b, 8b + 8) for every
