@@ -113,3 +113,78 @@ def test_graph_replays_match_eager(flint_bf16, T):
             moe.forward(W, x, out, ids, None, ws)
             torch.cuda.synchronize()
             assert torch.equal(out, ref[r][0])
+
+
+def _replay_check(call_eager, call_raw, set_input, outs, n_inputs=3):
+    """Eager results for n inputs, then a captured graph of one call replayed
+    twice per input with eager work in between: every replay bit-equal."""
+    ref = []
+    for r in range(n_inputs):
+        set_input(r)
+        call_eager()
+        torch.cuda.synchronize()
+        ref.append([o.clone() for o in outs])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call_eager()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        assert call_raw(torch.cuda.current_stream().cuda_stream) == 0
+    for rep in range(2):
+        for r in range(n_inputs):
+            set_input(r)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for o, e in zip(outs, ref[r]):
+                assert torch.equal(o, e), f"replay {rep}/{r} differs from eager"
+            call_eager()
+            torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [8, 100])
+def test_block_graph_replays_match_eager(flint_bf16, T):
+    """The pre-norm block (norm fused into the router launch for T <= 64, its
+    own launch above) under graph capture."""
+    from synth import make_residual
+    sg = flint_bf16["sg"]
+    say(f"pre-norm block graph replays T={T}")
+    moe = sg.FlintMoE(max_tokens=T)
+    W = flint_bf16["W"]
+    gamma = sg.bf16_tensor(flint_bf16["syn"].norm_weight(), "cuda")
+    r = sg.bf16_tensor(make_residual(T, seed=0, x_seed=0), "cuda")
+    rs = [sg.bf16_tensor(make_residual(T, seed=0, x_seed=30 + i), "cuda") for i in range(3)]
+    out = torch.empty_like(r)
+    ids = torch.empty((T, 6), dtype=torch.int32, device="cuda")
+    ws = moe.new_workspace(T, "cuda")
+    Ws = W.struct()
+    _replay_check(
+        lambda: moe.block_forward(W, gamma, r, out, eps=1e-6, topk_ids=ids, workspace=ws),
+        lambda s: moe.block_forward_raw(Ws, int(gamma.data_ptr()), 1e-6, int(r.data_ptr()), T,
+                                        int(out.data_ptr()), int(ids.data_ptr()), 0,
+                                        int(ws.data_ptr()), ws.numel(), s),
+        lambda i: r.copy_(rs[i]), [out, ids])
+
+
+@pytest.mark.parametrize("T,block", [(8, False), (8, True), (100, True)])
+def test_dense_mlp_graph_replays_match_eager(T, block):
+    from synth import SyntheticDenseMLP
+    import sparse_expert_gemv_amd as sg
+    say(f"dense MLP graph replays T={T} block={block}")
+    S = SyntheticDenseMLP(seed=1, inter=1024)
+    w13, w2 = sg.bf16_tensor(S.w13(), "cuda"), sg.bf16_tensor(S.w2(), "cuda")
+    gamma = sg.bf16_tensor(S.norm_weight(), "cuda") if block else None
+    m = sg.FlintMLP(inter=1024, max_tokens=T)
+    x = sg.bf16_tensor(make_x(T, seed=0, x_seed=0), "cuda")
+    xs = [sg.bf16_tensor(make_x(T, seed=0, x_seed=40 + i), "cuda") for i in range(3)]
+    out = torch.empty_like(x)
+    ws = m.new_workspace(T, "cuda")
+    gp = int(gamma.data_ptr()) if block else None
+    _replay_check(
+        lambda: m.forward(w13, w2, x, out, gamma=gamma, workspace=ws),
+        lambda s: m.forward_raw(int(w13.data_ptr()), int(w2.data_ptr()), gp, 1e-6, int(x.data_ptr()),
+                                T, int(out.data_ptr()), int(ws.data_ptr()), ws.numel(), s),
+        lambda i: x.copy_(xs[i]), [out])
