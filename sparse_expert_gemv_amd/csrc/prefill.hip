@@ -700,17 +700,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_shared_combine_kernel(Lay
       const f32x4 s0 = *reinterpret_cast<const f32x4*>(park + row * kCbRow + c8);
       const f32x4 s1 = *reinterpret_cast<const f32x4*>(park + row * kCbRow + c8 + 4);
       float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      for (int j = 0; j < k; ++j) {
-        const float w = a.ws.wts[t * k + j];
-        const u32x4 y = *reinterpret_cast<const u32x4*>(p.y16 + (size_t)p.pos[t * k + j] * H + nb * 256 + c8);
-        o[0] = fmaf(w, f16_lo(y.x), o[0]);
-        o[1] = fmaf(w, f16_hi(y.x), o[1]);
-        o[2] = fmaf(w, f16_lo(y.y), o[2]);
-        o[3] = fmaf(w, f16_hi(y.y), o[3]);
-        o[4] = fmaf(w, f16_lo(y.z), o[4]);
-        o[5] = fmaf(w, f16_hi(y.z), o[5]);
-        o[6] = fmaf(w, f16_lo(y.w), o[6]);
-        o[7] = fmaf(w, f16_hi(y.w), o[7]);
+      // Every rank's y and weight requested before the first is used (the
+      // loads are independent); then added in rank order.
+      u32x4 yv[kMaxTopK];
+      float wj[kMaxTopK];
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+          wj[j] = a.ws.wts[t * k + j];
+          yv[j] = *reinterpret_cast<const u32x4*>(p.y16 + (size_t)p.pos[t * k + j] * H + nb * 256 + c8);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+          const float w = wj[j];
+          const u32x4 y = yv[j];
+          o[0] = fmaf(w, f16_lo(y.x), o[0]);
+          o[1] = fmaf(w, f16_hi(y.x), o[1]);
+          o[2] = fmaf(w, f16_lo(y.y), o[2]);
+          o[3] = fmaf(w, f16_hi(y.y), o[3]);
+          o[4] = fmaf(w, f16_lo(y.z), o[4]);
+          o[5] = fmaf(w, f16_hi(y.z), o[5]);
+          o[6] = fmaf(w, f16_lo(y.w), o[6]);
+          o[7] = fmaf(w, f16_hi(y.w), o[7]);
+        }
       }
       if (a.resid) {
         const u32x4 rr = *reinterpret_cast<const u32x4*>(a.resid + (size_t)t * H + nb * 256 + c8);
