@@ -734,6 +734,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   __shared__ int16_t s_active[kMaxExperts];
   __shared__ int16_t s_off[kMaxExperts + 1];
   __shared__ int16_t s_slots[kDecodeMaxT * kMaxTopK];
+  __shared__ float s_wts[kDecodeMaxT * kMaxTopK];
   __shared__ int16_t s_work[kMaxDownWork];
   __shared__ int s_scan[kDownWaves];
   __shared__ float part[(kMaxTopK + 1) * kDecodeMaxT * kDownRowsPerBlock];
@@ -745,7 +746,10 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   // The routing table in one round trip (whole arrays, no dependence on |U|).
   for (int q = threadIdx.x; q < E; q += kDownThreads) s_active[q] = (int16_t)route[1 + q];
   for (int q = threadIdx.x; q <= E; q += kDownThreads) s_off[q] = (int16_t)route[1 + E + q];
-  for (int q = threadIdx.x; q < T * k; q += kDownThreads) s_slots[q] = (int16_t)route[2 + 2 * E + q];
+  for (int q = threadIdx.x; q < T * k; q += kDownThreads) {
+    s_slots[q] = (int16_t)route[2 + 2 * E + q];
+    s_wts[q] = a.ws.wts[q];   // for the combine, fetched with the table
+  }
   const int n = route[0];
   __syncthreads();
 
@@ -794,7 +798,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
     const int r = q - t * kDownRowsPerBlock;
     float o = part[(T * k + t) * kDownRowsPerBlock + r];
     for (int j = 0; j < k; ++j)
-      o = fmaf(a.ws.wts[t * k + j], part[(t * k + j) * kDownRowsPerBlock + r], o);
+      o = fmaf(s_wts[t * k + j], part[(t * k + j) * kDownRowsPerBlock + r], o);
     if (a.resid) o += bf16_lo(a.resid[(size_t)t * H + r0 + r]);
     a.out[(size_t)t * H + r0 + r] = f32_to_bf16_rne(o);
   }
