@@ -264,7 +264,10 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-using RouterGemm = BlockGemm<kMT, kMaxExperts, 1, 4, false, 3, 32>;
+// 32 tokens per block (256 blocks at T = 8192, one per CU) with 128-byte K
+// chunks: the router matrix is small and shared by every block, so the
+// GEMM is bound by each block's latency per K step, not by bytes.
+using RouterGemm = BlockGemm<kMT, kMaxExperts, 1, 4, false, 3, 64>;
 // RMSNorm rows: n = bf16(r / rms(r) * gamma), one wave per token; lane l
 // owns the 16-byte vectors l, l + 64, l + 128, l + 192 of the row.
 constexpr int kNormVecPerLane = H / 8 / 64;   // 4
@@ -341,7 +344,8 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
   // preserving bits of the logit) << 32 | ~expert, so equal logits rank the
   // lower expert index first, and sigmoid's monotonicity makes the ranking by
   // logit the ranking by score.
-  {
+  static_assert(4 * kMT <= kThreads, "four threads per token");
+  if (tid < 4 * kMT) {
     const int i = tid >> 2, quarter = tid & 3;
     uint64_t top[kMaxTopK];
 #pragma unroll
