@@ -585,10 +585,14 @@ void gateup_kernel(LayerArgs a) {
 constexpr int kDownRowsPerBlock = 8;
 constexpr int kDownThreads = 512;
 constexpr int kDownWaves = kDownThreads / kWave;
-constexpr int kDnSlots = 4;       // slots per work entry (their h rows prefetched together)
-constexpr int kMaxDownWork = 512; // >= T*k/4 + (E + 1) + T/4 for T <= 64, k <= 8
-// Work entry code: item << 4 | sub-entry (int16: item <= 256, sub-entry < 16).
-static_assert(kDecodeMaxT / kDnSlots <= 16 && (kMaxExperts << 4) + 15 <= 32767, "work entry code");
+constexpr int kDnSlots = 2;       // slots per work entry (their h rows prefetched together)
+constexpr int kMaxDownWork = 640; // >= T*k/2 + (E + 1) + T/2 for T <= 64, k <= 8
+// Work entry code: item << 5 | sub-entry (int16: item <= 256, sub-entry < 32).
+constexpr int kDnSubBits = 5;
+static_assert(kDecodeMaxT / kDnSlots <= (1 << kDnSubBits) &&
+              (kMaxExperts << kDnSubBits) + (1 << kDnSubBits) - 1 <= 32767, "work entry code");
+static_assert(kDecodeMaxT * kMaxTopK / kDnSlots + kMaxExperts + 1 + kDecodeMaxT / kDnSlots <= kMaxDownWork,
+              "work list size");
 
 // A work entry: slots [j0, j0 + nj) of one item (an active expert, or the
 // shared expert whose slots are the T tokens).
@@ -601,7 +605,7 @@ struct DownItem {
 
 __device__ __forceinline__ DownItem down_entry(const LayerArgs& a, int entry, int n,
                                                const int16_t* s_active, const int16_t* s_off) {
-  const int item = entry >> 4, q = entry & 15;
+  const int item = entry >> kDnSubBits, q = entry & ((1 << kDnSubBits) - 1);
   DownItem d;
   d.shared = item >= n;
   const int cnt = d.shared ? a.T : s_off[item + 1] - s_off[item];
@@ -724,8 +728,9 @@ __device__ __forceinline__ void down_entry_rows(const LayerArgs& a, const DownIt
 // Down + combine.  Block b owns output rows [8b, 8b + 8) of every token.
 // Its work: every active expert and the shared expert, cut into entries of
 // up to kDnSlots slots (an expert hit by many tokens spreads over several
-// waves); wave w takes entries w, w + 8, ... and keeps the next entry's w2
-// rows and h rows in flight while it reduces the current one.  Lane l holds
+// waves); wave w takes entries w, w + 8, ... and keeps the next two
+// entries' w2 rows and h rows in flight while it reduces the current one
+// (two-slot entries keep three buffers within the register budget).  Lane l holds
 // columns [8l, 8l + 8) of each row.  Per (h row, output row) the 64-lane
 // partial dot products are summed in a fixed tree and parked in LDS; the
 // block then combines out = shared + sum_j w_j * routed_j in a fixed order.
@@ -766,31 +771,43 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
     if (w < wave) base += s_scan[w];
     total += s_scan[w];
   }
-  for (int q = 0; q < nsub; ++q) s_work[base + q] = (int16_t)((it << 4) | q);
+  for (int q = 0; q < nsub; ++q) s_work[base + q] = (int16_t)((it << kDnSubBits) | q);
   __syncthreads();
 
-  DownRows<kFp4> pa, pb;
-  DownItem da{}, db{};
+  // Three entries per wave in flight: the one being reduced and the next
+  // two (rows and h), rotated through pa, pb, pc.
+  DownRows<kFp4> pa, pb, pc;
+  DownItem da{}, db{}, dc{};
   int w = wave;
   if (w < total) {
     da = down_entry(a, s_work[w], n, s_active, s_off);
     prefetch_entry(pa, a, da, r0, s_slots);
   }
+  if (w + kDownWaves < total) {
+    db = down_entry(a, s_work[w + kDownWaves], n, s_active, s_off);
+    prefetch_entry(pb, a, db, r0, s_slots);
+  }
   while (w < total) {
-    const int nx = w + kDownWaves;
-    if (nx < total) {
-      db = down_entry(a, s_work[nx], n, s_active, s_off);
-      prefetch_entry(pb, a, db, r0, s_slots);
+    if (w + 2 * kDownWaves < total) {
+      dc = down_entry(a, s_work[w + 2 * kDownWaves], n, s_active, s_off);
+      prefetch_entry(pc, a, dc, r0, s_slots);
     }
     down_entry_rows(a, da, pa, s_slots, part);
-    if (nx >= total) break;
-    const int nx2 = nx + kDownWaves;
-    if (nx2 < total) {
-      da = down_entry(a, s_work[nx2], n, s_active, s_off);
+    w += kDownWaves;
+    if (w >= total) break;
+    if (w + 2 * kDownWaves < total) {
+      da = down_entry(a, s_work[w + 2 * kDownWaves], n, s_active, s_off);
       prefetch_entry(pa, a, da, r0, s_slots);
     }
     down_entry_rows(a, db, pb, s_slots, part);
-    w = nx2;
+    w += kDownWaves;
+    if (w >= total) break;
+    if (w + 2 * kDownWaves < total) {
+      db = down_entry(a, s_work[w + 2 * kDownWaves], n, s_active, s_off);
+      prefetch_entry(pb, a, db, r0, s_slots);
+    }
+    down_entry_rows(a, dc, pc, s_slots, part);
+    w += kDownWaves;
   }
   __syncthreads();
   for (int q = threadIdx.x; q < T * kDownRowsPerBlock; q += kDownThreads) {
