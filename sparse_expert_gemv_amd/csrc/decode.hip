@@ -4,11 +4,12 @@
 // Three launches on the caller's stream:
 //   1. route   : router GEMV, one expert row per wave for all T tokens (64
 //                blocks of 4 waves; for the pre-norm block each block
-//                normalises the rows it stages, and block 0 stores them).  The last block to finish picks every
-//                token's top-k by sigmoid score (a wave per token), computes
-//                the routing weights and buckets every (token, rank) slot by
-//                expert into the routing table (U ascending, slots grouped
-//                by expert in ascending slot order).
+//                normalises the rows it stages, and block 0 stores them).
+//                The last block to finish picks every token's top-k by
+//                sigmoid score (a wave per token), computes the routing
+//                weights and buckets every (token, rank) slot by expert into
+//                the routing table (U ascending, slots grouped by expert in
+//                ascending slot order).
 //   2. gate/up : 64 blocks for the shared expert (first, so that they stream
 //                from the start: they need no routing), then (active expert
 //                a, 8 gate/up row pairs) per block; the rows are streamed
@@ -59,10 +60,6 @@ static_assert(kDecodeMaxT * kMaxTopK <= 32767 && kMaxExperts <= 32767, "int16 ro
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// One x row (H bf16 = kVecH 16-byte vectors, one per thread) into LDS with
-// an LDS-direct load: no registers, and a thread's loads for several rows
-// are all in flight before the barrier that waits for them.  Lane l of a
-// wave writes the 16 bytes at the wave's LDS base + 16 l.
 // Barrier for LDS hand-offs only: waits for this wave's LDS operations, not
 // for its outstanding global loads (which __syncthreads also waits for), so
 // weight loads issued earlier stay in flight across it.  Also a compiler
@@ -80,6 +77,10 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt: no wait
 }
 
+// One x row (H bf16 = kVecH 16-byte vectors, one per thread) into LDS with
+// an LDS-direct load: no registers, and a thread's loads for several rows
+// are all in flight before the barrier that waits for them.  Lane l of a
+// wave writes the 16 bytes at the wave's LDS base + 16 l.
 __device__ __forceinline__ void stage_x_row(u32x4* dst, const uint16_t* row) {
   const int wave_base = threadIdx.x & ~(kWave - 1);
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(row) + threadIdx.x,
