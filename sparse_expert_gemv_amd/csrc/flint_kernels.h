@@ -14,7 +14,7 @@ constexpr int kMaxExperts = 256;   // E upper bound (four router scores per lane
 constexpr int kMaxTopK = 8;
 constexpr int kDecodeMaxT = 64;    // largest T taken by the GEMV (decode) kernels
 constexpr int kPrefillTile = 32;   // tokens per router / scatter block (prefill-sized T)
-constexpr int kGroupTile = 128;    // slots per grouped-GEMM M-tile (prefill-sized T)
+constexpr int kGroupTile = 256;    // slots per grouped-GEMM M-tile (prefill-sized T)
 // Workspace header: uint32 completion counters, each on its own 256-byte
 // line so that tickets on one never queue behind atomics on another.  All
 // are zero before a forward starts and zero after it ends.

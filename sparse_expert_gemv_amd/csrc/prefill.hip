@@ -114,8 +114,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Block GEMM C[BM x BN] = A[BM x K] B[BN x K]^T with both operands K-
 // contiguous in global memory, fed through an S-stage LDS ring of KC-wide K
-// chunks (KC * 2 bytes per row and stage).  KC = 32 keeps two blocks per CU;
-// KC = 64 moves whole 128-byte lines but its ring needs the LDS of a CU.
+// chunks (KC * 2 bytes per row and stage).  With KC = 32 the three-stage
+// ring of a 256 x 256 tile takes 96 KiB; KC = 64 moves whole 128-byte lines
+// but doubles the ring.
 // Global -> LDS moves are LDS-direct loads (global_load_lds, 16 bytes per
 // lane): one instruction of a wave fills 1 KiB of LDS, i.e. RPI consecutive
 // rows, lane i writing 16-byte chunk i % CPR of row i / CPR.  Within a row
@@ -131,18 +132,20 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // both are bf16.
 template <int BM, int BN, int WM, int WN, bool kF16, int S, int KC>
 struct BlockGemm {
+  static constexpr int kWM = WM, kWN = WN;
+  static constexpr int NW = WM * WN;                  // waves per block
+  static constexpr int kBlockThreads = 64 * NW;       // the launch's block size
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int RT = TM / 32, CT = TN / 32;
   static constexpr int kRow = KC * 2;                 // LDS bytes per row
   static constexpr int CPR = kRow / 16;               // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;                // rows per LDS-direct instruction
-  static constexpr int NA = BM / (4 * RPI), NB = BN / (4 * RPI);   // instructions per thread per stage
+  static constexpr int NA = BM / (NW * RPI), NB = BN / (NW * RPI);   // instructions per thread per stage
   static constexpr int NL = NA + NB;
   static constexpr int kStage = (BM + BN) * kRow;
   static constexpr int kLds = S * kStage;
-  static_assert(WM * WN == kThreads / 64, "one wave per tile");
   static_assert(KC == 32 || KC == 64, "K chunk");
-  static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile shape");
+  static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "tile shape");
   static_assert(S >= 2 && (S - 2) * NL < 64, "pipeline depth");
 
   f32x16 acc[RT][CT];
@@ -204,7 +207,6 @@ struct BlockGemm {
       if (kc + S - 2 < nk) wait_vmem<(S - 2) * NL>();
       else wait_vmem<0>();
       stage_barrier();   // stage kc is in LDS for every wave; stage kc-1 is free
-      if (kc + S - 1 < nk) issue(kc + S - 1);
       const uint8_t* st = lds + (kc % S) * kStage;
       // All fragments of the stage first, then its MFMAs.
       constexpr int KS = KC / 16;
@@ -218,6 +220,9 @@ struct BlockGemm {
         for (int j = 0; j < CT; ++j)
           bfr[ks][j] = *reinterpret_cast<const u32x4*>(st + b_rd + j * 32 * kRow + koff[ks]);
       }
+      // The next stage's loads go out while the fragment reads are in flight
+      // (its buffer was last read in step kc - 1, before the barrier).
+      if (kc + S - 1 < nk) issue(kc + S - 1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if constexpr (kF16) {
@@ -242,12 +247,16 @@ struct BlockGemm {
 // Block -> work item, XCD-aware: the hardware deals blocks to the 8 XCDs
 // round-robin; item w is given to XCD w / ceil(n/8) so that consecutive items
 // (the M-tiles and column blocks of one expert, which read the same weight
-// and activation rows) share an XCD's L2.  The grid is n rounded up to a
-// multiple of 8, so every item below n has exactly one block; blocks past n
-// return.
+// and activation rows) share an XCD's L2.  n is the live item count: the
+// grouped GEMMs' grids are sized for the longest possible tile list and
+// their kernels read the real length on the device, so that the live items,
+// not the grid, are spread over the XCDs.  The grid holds at least
+// 8 ceil(n/8) blocks; every item below n gets exactly one, and the caller
+// returns for the rest (item >= n).
 __device__ __forceinline__ int xcd_item(int n) {
   const int per = (n + 7) / 8;
   const int b = blockIdx.x;
+  if (b >= 8 * per) return n;
   return (b % 8) * per + b / 8;
 }
 
@@ -519,24 +528,27 @@ __global__ __launch_bounds__(kThreads) void prefill_scatter_kernel(LayerArgs a) 
 
 // ---------------------------------------------------------------- 4. gate/up
 
-// Block tile: 128 slots x 256 rows of w13 = the gate and up rows of 128 h
-// columns.  Wave (wm, wn) owns slots [64 wm, +64) and h columns
+// Block tile: 256 slots x 256 rows of w13 = the gate and up rows of 128 h
+// columns, eight waves.  Wave (wm, wn) owns slots [64 wm, +64) and h columns
 // [64 wn, +64) of the block's 128: its B tiles ct = 0, 1 are gate rows and
 // ct = 2, 3 the up rows of the same columns, so SiLU-and-mul pairs
-// acc[.][ct] with acc[.][ct + 2] in registers.
-using GateUpGemm = BlockGemm<kGM, 256, 2, 2, false, 3, 32>;
+// acc[.][ct] with acc[.][ct + 2] in registers.  The 256-slot M-tile stages a
+// third fewer operand bytes per MFMA than a 128-slot one at the same waves
+// per SIMD (one 96 KiB block per CU).
+using GateUpGemm = BlockGemm<kGM, 256, 4, 2, false, 3, 32>;
 constexpr int kGuColBlocks = I / 128;   // 4
 
-__global__ __launch_bounds__(kThreads, 2) void prefill_gateup_kernel(LayerArgs a, int n_shared_tiles,
-                                                                     int n_items) {
+__global__ __launch_bounds__(GateUpGemm::kBlockThreads, 1) void prefill_gateup_kernel(LayerArgs a,
+                                                                                    int n_shared_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[GateUpGemm::kLds];
+  const PrefillWs& p = a.ws.pre;
+  const int n_items = (n_shared_tiles + p.tiles[0]) * kGuColBlocks;
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / 2, wn = wave % 2;
   const int T = a.T, k = a.k, E = a.E;
   const int q = item / kGuColBlocks, nb = item % kGuColBlocks;   // column blocks of a tile adjacent
-  const PrefillWs& p = a.ws.pre;
   const int32_t* slots = a.ws.route + 2 + 2 * E;
 
   const uint8_t* w13;
@@ -549,7 +561,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gateup_kernel(LayerArgs a
     w13 = a.shared.w13;
   } else {
     const int rq = q - n_shared_tiles;
-    if (rq >= p.tiles[0]) return;
     const int32_t* tl = p.tiles + 1 + 3 * rq;
     w13 = a.routed.w13 + (size_t)tl[0] * 2 * I * H * 2;
     start = tl[1];
@@ -596,20 +607,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gateup_kernel(LayerArgs a
 
 // ---------------------------------------------------------------- 5. down (routed)
 
-// Block tile: 128 slots x 256 output columns; wave (wm, wn) owns slots
-// [64 wm, +64) x columns [128 wn, +128).
-using DownGemm = BlockGemm<kGM, 256, 2, 2, true, 3, 32>;
+// Block tile: 256 slots x 256 output columns, eight waves; wave (wm, wn)
+// owns slots [64 wm, +64) x columns [128 wn, +128).
+using DownGemm = BlockGemm<kGM, 256, 4, 2, true, 3, 32>;
 constexpr int kDnColBlocks = H / 256;   // 8
+// Epilogue: each half of the fp16 y tile (128 slots x 256 columns) is
+// parked row-major in LDS and stored as 16-byte vectors.
+constexpr int kYRow = 256 + 8;          // halves per LDS row of the parked tile
+static_assert(kGM * kYRow <= DownGemm::kLds, "half a y tile fits the GEMM's LDS");
 
-__global__ __launch_bounds__(kThreads, 2) void prefill_down_kernel(LayerArgs a, int n_items) {
+__global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_down_kernel(LayerArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemm::kLds];
+  const PrefillWs& p = a.ws.pre;
+  const int n_items = p.tiles[0] * kDnColBlocks;
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / 2, wn = wave % 2;
   const int q = item / kDnColBlocks, nb = item % kDnColBlocks;
-  const PrefillWs& p = a.ws.pre;
-  if (q >= p.tiles[0]) return;
   const int32_t* tl = p.tiles + 1 + 3 * q;
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)tl[0] * H * I;
   const int start = tl[1], count = tl[2];
@@ -628,33 +643,43 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_down_kernel(LayerArgs a, 
   }
   const int rt_n = max(0, min(DownGemm::RT, (count - wm * DownGemm::TM + 31) / 32));
   DownGemm g;
-  g.run(lds, ag, bg, I, rt_n);
+  g.run(lds, ag, bg, I, rt_n);   // LDS is free afterwards
+  _Float16* ys = reinterpret_cast<_Float16*>(lds);
+  constexpr int kHalf = kGM / 2;
+  for (int half = 0; half < 2; ++half) {
+    if (wm / (DownGemm::kWM / 2) == half) {
 #pragma unroll
-  for (int rt = 0; rt < DownGemm::RT; ++rt)
+      for (int rt = 0; rt < DownGemm::RT; ++rt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * DownGemm::TM + rt * 32 + acc_row(r, lane);
-      if (row < count) {
+        for (int ct = 0; ct < DownGemm::CT; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < DownGemm::CT; ++ct) {
-          const int col = nb * 256 + wn * DownGemm::TN + ct * 32 + (lane & 31);
-          p.y16[(size_t)(start + row) * H + col] = (_Float16)g.acc[rt][ct][r];
-        }
-      }
+          for (int r = 0; r < 16; ++r)
+            ys[(wm * DownGemm::TM - half * kHalf + rt * 32 + acc_row(r, lane)) * kYRow + wn * DownGemm::TN +
+               ct * 32 + (lane & 31)] = (_Float16)g.acc[rt][ct][r];
     }
+    __syncthreads();
+    for (int u = tid; u < kHalf * 32; u += DownGemm::kBlockThreads) {
+      const int row = half * kHalf + (u >> 5), c8 = (u & 31) * 8;
+      if (row < count)
+        *reinterpret_cast<u32x4*>(p.y16 + (size_t)(start + row) * H + nb * 256 + c8) =
+            *reinterpret_cast<const u32x4*>(ys + (row - half * kHalf) * kYRow + c8);
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------- 6. shared down + combine
 
-// Block tile: 128 tokens x 256 output columns of the shared expert's down
-// GEMM.  Epilogue in two halves of 64 tokens: the owning waves park their
+// Block tile: 256 tokens x 256 output columns of the shared expert's down
+// GEMM.  Epilogue in four parts of 64 tokens: the owning waves park their
 // accumulators in LDS, then every thread finishes 8 consecutive columns of a
 // token at a time: out = shared + sum_j w_j y_j in rank order, one bf16
 // rounding, 16-byte loads of y and stores of out.
 constexpr int kCbRow = 256 + 4;   // floats per LDS row of the parked tile
-constexpr int kCbLds = cmax(DownGemm::kLds, 64 * kCbRow * 4);
+constexpr int kCbLds = cmax(DownGemm::kLds, DownGemm::TM * kCbRow * 4);
 
-__global__ __launch_bounds__(kThreads, 2) void prefill_shared_combine_kernel(LayerArgs a, int n_items) {
+__global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_combine_kernel(LayerArgs a,
+                                                                                         int n_items) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kCbLds];
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
@@ -683,8 +708,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_shared_combine_kernel(Lay
   g.run(lds, ag, bg, I, rt_n);   // LDS is free afterwards
 
   float* park = reinterpret_cast<float*>(lds);
-  for (int half = 0; half < 2; ++half) {
-    if (wm == half) {
+  for (int part = 0; part < DownGemm::kWM; ++part) {
+    if (wm == part) {
 #pragma unroll
       for (int rt = 0; rt < DownGemm::RT; ++rt)
 #pragma unroll
@@ -696,9 +721,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_shared_combine_kernel(Lay
     }
     __syncthreads();
     // 64 tokens x 32 groups of 8 columns = 2048 units, 8 per thread.
-    for (int u = tid; u < 64 * 32; u += kThreads) {
+    for (int u = tid; u < DownGemm::TM * 32; u += DownGemm::kBlockThreads) {
       const int row = u >> 5, c8 = (u & 31) * 8;
-      const int lrow = half * 64 + row;
+      const int lrow = part * DownGemm::TM + row;
       if (lrow >= count) continue;
       const int t = t0 + lrow;
       const f32x4 s0 = *reinterpret_cast<const f32x4*>(park + row * kCbRow + c8);
@@ -758,7 +783,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_shared_combine_kernel(Lay
 // columns) with the gate and up rows of w13 [2 I_d][H] as B, SiLU-and-mul
 // epilogue, h fp16 [T][I_d].  Items run token-tile-major so that the column
 // blocks of one token tile share its x rows on one XCD.
-__global__ __launch_bounds__(kThreads, 2) void dense_gateup_gemm_kernel(DenseArgs a, int n_items) {
+__global__ __launch_bounds__(GateUpGemm::kBlockThreads, 1) void dense_gateup_gemm_kernel(DenseArgs a,
+                                                                                      int n_items) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[GateUpGemm::kLds];
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
@@ -803,7 +829,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gateup_gemm_kernel(DenseArg
 // Down GEMM of the dense MLP: tile (128 tokens, 256 output columns), h fp16
 // times w2 (widened to fp16 into LDS), K = I_d; epilogue adds r for the
 // pre-norm block and rounds once to bf16.
-__global__ __launch_bounds__(kThreads, 2) void dense_down_gemm_kernel(DenseArgs a, int n_items) {
+__global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void dense_down_gemm_kernel(DenseArgs a, int n_items) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemm::kLds];
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
@@ -850,9 +876,9 @@ __global__ __launch_bounds__(kThreads, 2) void dense_down_gemm_kernel(DenseArgs 
 hipError_t launch_dense_prefill(const DenseArgs& a, hipStream_t stream, Launcher& launch) {
   const int n_tiles = (a.T + kGM - 1) / kGM;
   const int n_gu = n_tiles * (a.inter / 128);
-  launch(dense_gateup_gemm_kernel, dim3(round8(n_gu)), dim3(kThreads), stream, a, n_gu);
+  launch(dense_gateup_gemm_kernel, dim3(round8(n_gu)), dim3(GateUpGemm::kBlockThreads), stream, a, n_gu);
   const int n_dn = n_tiles * kDnColBlocks;
-  launch(dense_down_gemm_kernel, dim3(round8(n_dn)), dim3(kThreads), stream, a, n_dn);
+  launch(dense_down_gemm_kernel, dim3(round8(n_dn)), dim3(DownGemm::kBlockThreads), stream, a, n_dn);
   return hipGetLastError();
 }
 
@@ -863,7 +889,7 @@ void launch_rmsnorm(const uint16_t* r, const uint16_t* gamma, float eps, uint16_
 }
 
 int prefill_tiles_max(int T, int E, int k) {
-  return (T * k + kGM - 1) / kGM + E;  // sum over experts of ceil(count / 128)
+  return (T * k + kGM - 1) / kGM + E;  // bounds the sum over experts of ceil(count / kGM)
 }
 
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
@@ -874,12 +900,14 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& laun
   launch(prefill_router_kernel, dim3(nb), dim3(kThreads), stream, a);
   launch(prefill_scan_kernel, dim3(1), dim3(kScanThreads), stream, a, nb);
   launch(prefill_scatter_kernel, dim3(nb), dim3(kThreads), stream, a);
+  // The grouped GEMMs' grids cover the longest possible tile list; the
+  // kernels read the real one.
   const int n_gu = (n_shared + n_routed_max) * kGuColBlocks;
-  launch(prefill_gateup_kernel, dim3(round8(n_gu)), dim3(kThreads), stream, a, n_shared, n_gu);
+  launch(prefill_gateup_kernel, dim3(round8(n_gu)), dim3(GateUpGemm::kBlockThreads), stream, a, n_shared);
   const int n_dn = n_routed_max * kDnColBlocks;
-  launch(prefill_down_kernel, dim3(round8(n_dn)), dim3(kThreads), stream, a, n_dn);
+  launch(prefill_down_kernel, dim3(round8(n_dn)), dim3(DownGemm::kBlockThreads), stream, a);
   const int n_sc = n_shared * kDnColBlocks;
-  launch(prefill_shared_combine_kernel, dim3(round8(n_sc)), dim3(kThreads), stream, a, n_sc);
+  launch(prefill_shared_combine_kernel, dim3(round8(n_sc)), dim3(DownGemm::kBlockThreads), stream, a, n_sc);
   return hipGetLastError();
 }
 

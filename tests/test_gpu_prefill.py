@@ -81,6 +81,31 @@ def test_prefill_t8192_sampled(flint_bf16):
     assert g.ok, str(g)
 
 
+def test_prefill_multi_tile_groups(flint_bf16):
+    """Skewed routing (the router bias): slot groups that span several
+    256-slot M-tiles (the largest has over 1300 slots).  Tokens on both sides
+    of every tile edge of the four largest groups, their last tokens and a
+    random sample against the oracle."""
+    T = 2048
+    say("prefill T=2048 with router bias: multi-tile expert groups")
+    xb = make_x(T, seed=0, x_seed=1)
+    r = run(flint_bf16, xb, bias=True)
+    counts = np.bincount(r["ids"].ravel(), minlength=256)
+    big = np.argsort(counts)[::-1][:4]
+    assert counts[big[0]] > 3 * 256, counts[big[0]]
+    sample = set(np.random.default_rng(1).choice(T, 24, replace=False).tolist())
+    for e in big:
+        toks = np.nonzero((r["ids"] == e).any(axis=1))[0]   # the group's slot order
+        for edge in range(256, len(toks), 256):
+            sample.update((int(toks[edge - 1]), int(toks[edge])))
+        sample.add(int(toks[-1]))
+    sample = sorted(sample)
+    res = moe_forward(flint_bf16["Lb"], xb, tokens=sample)
+    g = grade(r["out"], r["ids"], res, tokens=sample, tol=TOL_BF16)
+    print(f"{len(sample)} tokens: {g}")
+    assert g.ok, str(g)
+
+
 def test_prefill_deterministic(flint_bf16):
     say("prefill determinism T=1000")
     xb = make_x(1000, seed=0, x_seed=3)
