@@ -157,8 +157,8 @@ def kernel_names(nk: int, mlp: bool):
         return {2: ["gateup", "down"], 3: ["norm", "gateup", "down"]}.get(
             nk, [f"kernel{i}" for i in range(nk)])
     return {3: ["route", "gateup", "down"],
-            6: ["router", "scan", "scatter", "gateup", "down", "shared_down_combine"],
-            7: ["norm", "router", "scan", "scatter", "gateup", "down", "shared_down_combine"]}.get(
+            5: ["router", "bucket", "gateup", "down", "shared_down_combine"],
+            6: ["norm", "router", "bucket", "gateup", "down", "shared_down_combine"]}.get(
                 nk, [f"kernel{i}" for i in range(nk)])
 
 

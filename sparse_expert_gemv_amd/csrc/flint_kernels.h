@@ -34,9 +34,8 @@ __host__ __device__ constexpr int route_table_ints(int E, int T, int k) { return
 
 // Regions used only by the prefill-sized path.
 struct PrefillWs {
-  int32_t* counts;    // [nb][E]: slots per (64-token block, expert)
-  int32_t* base;      // [nb][E]: first sorted position of each (block, expert)
-  int32_t* tiles;     // [0] = routed tiles; then (expert, start, count) per 128-slot tile
+  int32_t* counts;    // [nb][E]: slots per (router block of kPrefillTile tokens, expert)
+  int32_t* tiles;     // [0] = routed tiles; then (expert, start, count) per kGroupTile-slot tile
   int32_t* pos;       // [T*k]: sorted position of slot s
   _Float16* h16;      // [T*k + T][I]: h in sorted slot order, then the shared expert's
   _Float16* y16;      // [T*k][H]: unweighted down projection per sorted slot

@@ -42,14 +42,12 @@ size_t prefill_extra_bytes(const flint_moe_config& c, int32_t T, flint::PrefillW
   const size_t tiles = (size_t)flint::prefill_tiles_max(T, c.n_experts, c.top_k);
   size_t o = 0;
   const size_t counts = o; o = align_up(o + nb * E * sizeof(int32_t));
-  const size_t basep = o;  o = align_up(o + nb * E * sizeof(int32_t));
   const size_t tl = o;     o = align_up(o + (1 + 3 * tiles) * sizeof(int32_t));
   const size_t pos = o;    o = align_up(o + t * k * sizeof(int32_t));
   const size_t h16 = o;    o = align_up(o + (t * k + t) * I * sizeof(uint16_t));
   const size_t y16 = o;    o = align_up(o + t * k * H * sizeof(uint16_t));
   if (p) {
     p->counts = reinterpret_cast<int32_t*>(base + counts);
-    p->base = reinterpret_cast<int32_t*>(base + basep);
     p->tiles = reinterpret_cast<int32_t*>(base + tl);
     p->pos = reinterpret_cast<int32_t*>(base + pos);
     p->h16 = reinterpret_cast<_Float16*>(base + h16);

@@ -406,11 +406,21 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
   for (int e = tid; e < E; e += kThreads) a.ws.pre.counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// ---------------------------------------------------------------- 2. scan
+// ---------------------------------------------------------------- 2. bucketing
 
-constexpr int kScanThreads = 1024;             // 4 threads per expert
-constexpr int kScanParts = kScanThreads / kMaxExperts;
-constexpr int kScanBatch = 16;                 // counts loaded per round trip
+// Stable counting sort of the T*k slots by expert, one launch of nb blocks
+// (one per router block).  Block b sums the router's per-block expert counts
+// itself, four threads per expert each over a quarter of the blocks,
+// kBucketBatch counts per round trip: before[e] over the blocks ahead of b
+// and total[e] over all.  The totals' exclusive scan over experts gives the
+// group offsets; the block places each of its slots at offset + before +
+// its rank among the block's slots of the same expert (read from per-expert
+// occupancy bitmaps), so slots ascend within every group.  Block 0 also
+// writes the routing table's header (U and the group offsets) and the
+// M-tile list.
+constexpr int kBucketThreads = 1024;
+constexpr int kBucketParts = kBucketThreads / kMaxExperts;   // 4
+constexpr int kBucketBatch = 16;
 
 // Exclusive prefix sum of v over threads [0, 256) (one value per expert).
 // Every thread of the block calls it; threads >= 256 pass 0 and get 0.
@@ -425,104 +435,91 @@ __device__ __forceinline__ int expert_excl_scan(int v, int* s_wave) {
   return threadIdx.x < kMaxExperts ? base + incl - v : 0;
 }
 
-__global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(LayerArgs a, int nb) {
+__global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(LayerArgs a, int nb) {
+  constexpr int kWords = kMT * kMaxTopK / 32;        // bitmap words per expert
+  __shared__ uint32_t occ[kMaxExperts * kWords];
+  __shared__ int s_part[2][kBucketParts][kMaxExperts];
+  __shared__ int s_base[kMaxExperts];
   __shared__ int s_wave[4];
   __shared__ int s_tot[2];
-  __shared__ int s_part[kScanParts][kMaxExperts];
-  __shared__ int s_off[kMaxExperts];
-  const int e = threadIdx.x % kMaxExperts, part = threadIdx.x / kMaxExperts;
+  const int tid = threadIdx.x;
+  const int e = tid % kMaxExperts, part = tid / kMaxExperts;
   const bool lead = part == 0;
-  const int E = a.E, T = a.T, k = a.k;
-  const PrefillWs& p = a.ws.pre;
-  // Part `part` owns blocks [b0, b1); counts are loaded kScanBatch at a time
-  // so that each thread has one round trip to memory in flight per batch.
-  const int per = (nb + kScanParts - 1) / kScanParts;
-  const int b0 = min(nb, part * per), b1 = min(nb, b0 + per);
-  int psum = 0;
-  if (e < E)
-    for (int b = b0; b < b1; b += kScanBatch) {
-      int c[kScanBatch];
-#pragma unroll
-      for (int q = 0; q < kScanBatch; ++q) c[q] = b + q < b1 ? p.counts[(size_t)(b + q) * E + e] : 0;
-#pragma unroll
-      for (int q = 0; q < kScanBatch; ++q) psum += c[q];
-    }
-  s_part[part][e] = psum;
-  __syncthreads();
-  int cnt = 0;
-  if (lead && e < E)
-    for (int q = 0; q < kScanParts; ++q) cnt += s_part[q][e];
-  const int off = expert_excl_scan(cnt, s_wave);
-  const int active = cnt > 0;
-  const int aidx = expert_excl_scan(active, s_wave);
-  const int ntile = (cnt + kGM - 1) / kGM;
-  const int tile0 = expert_excl_scan(ntile, s_wave);
-  if (threadIdx.x == kMaxExperts - 1) {
-    s_tot[0] = aidx + active;
-    s_tot[1] = tile0 + ntile;
-  }
-  if (lead) s_off[e] = off;
-  __syncthreads();
-  // Per (block, expert) base = expert offset + counts of earlier blocks.
-  if (e < E) {
-    int run = s_off[e];
-    for (int q = 0; q < part; ++q) run += s_part[q][e];
-    for (int b = b0; b < b1; b += kScanBatch) {
-      int c[kScanBatch];
-#pragma unroll
-      for (int q = 0; q < kScanBatch; ++q) c[q] = b + q < b1 ? p.counts[(size_t)(b + q) * E + e] : 0;
-#pragma unroll
-      for (int q = 0; q < kScanBatch; ++q)
-        if (b + q < b1) {
-          p.base[(size_t)(b + q) * E + e] = run;
-          run += c[q];
-        }
-    }
-  }
-  int32_t* route = a.ws.route;
-  if (lead && active) {
-    route[1 + aidx] = e;
-    route[1 + E + aidx] = off;
-    for (int q = 0; q < ntile; ++q) {
-      int32_t* tl = p.tiles + 1 + 3 * (tile0 + q);
-      tl[0] = e;
-      tl[1] = off + q * kGM;
-      tl[2] = min(kGM, cnt - q * kGM);
-    }
-  }
-  if (threadIdx.x == 0) {
-    route[0] = s_tot[0];
-    route[1 + E + s_tot[0]] = T * k;
-    p.tiles[0] = s_tot[1];
-  }
-}
-
-// ---------------------------------------------------------------- 3. scatter
-
-__global__ __launch_bounds__(kThreads) void prefill_scatter_kernel(LayerArgs a) {
-  constexpr int kSlotsMax = kMT * kMaxTopK;        // 512
-  constexpr int kWords = kSlotsMax / 32;           // 16
-  __shared__ uint32_t occ[kMaxExperts * kWords];  // 16 KiB
   const int T = a.T, E = a.E, k = a.k;
-  const int s0 = blockIdx.x * kMT * k;
-  const int ns = min(kMT, T - blockIdx.x * kMT) * k;
+  const int b = blockIdx.x;
+  const int s0 = b * kMT * k;
+  const int ns = min(kMT, T - b * kMT) * k;
   const PrefillWs& p = a.ws.pre;
-  for (int i = threadIdx.x; i < kMaxExperts * kWords; i += kThreads) occ[i] = 0;
-  __syncthreads();
-  for (int q = threadIdx.x; q < ns; q += kThreads) {
-    const int e = a.ws.ids[s0 + q];
-    atomicOr(&occ[e * kWords + (q >> 5)], 1u << (q & 31));
+  for (int q = tid; q < kMaxExperts * kWords; q += kBucketThreads) occ[q] = 0;
+
+  const int per = (nb + kBucketParts - 1) / kBucketParts;
+  const int b0 = min(nb, part * per), b1 = min(nb, b0 + per);
+  int before = 0, total = 0;
+  if (e < E)
+    for (int c0 = b0; c0 < b1; c0 += kBucketBatch) {
+      int c[kBucketBatch];
+#pragma unroll
+      for (int q = 0; q < kBucketBatch; ++q) c[q] = c0 + q < b1 ? p.counts[(size_t)(c0 + q) * E + e] : 0;
+#pragma unroll
+      for (int q = 0; q < kBucketBatch; ++q) {
+        total += c[q];
+        before += c0 + q < b ? c[q] : 0;
+      }
+    }
+  s_part[0][part][e] = before;
+  s_part[1][part][e] = total;
+  __syncthreads();   // the partials and the cleared bitmaps
+  for (int q = tid; q < ns; q += kBucketThreads) {
+    const int ex = a.ws.ids[s0 + q];
+    atomicOr(&occ[ex * kWords + (q >> 5)], 1u << (q & 31));
   }
+  int cnt = 0, bef = 0;
+  if (lead && e < E)
+    for (int q = 0; q < kBucketParts; ++q) {
+      cnt += s_part[1][q][e];
+      bef += s_part[0][q][e];
+    }
+  const int off = expert_excl_scan(cnt, s_wave);   // its barriers also publish the bitmaps
+  if (lead) s_base[e] = off + bef;
   __syncthreads();
-  int32_t* slots = a.ws.route + 2 + 2 * E;
-  for (int q = threadIdx.x; q < ns; q += kThreads) {
-    const int e = a.ws.ids[s0 + q];
-    const uint32_t* m = occ + e * kWords;
+
+  int32_t* route = a.ws.route;
+  int32_t* slots = route + 2 + 2 * E;
+  for (int q = tid; q < ns; q += kBucketThreads) {
+    const int ex = a.ws.ids[s0 + q];
+    const uint32_t* m = occ + ex * kWords;
     int rank = __popc(m[q >> 5] & ((1u << (q & 31)) - 1u));
     for (int w = 0; w < (q >> 5); ++w) rank += __popc(m[w]);
-    const int pos = p.base[(size_t)blockIdx.x * E + e] + rank;
+    const int pos = s_base[ex] + rank;
     slots[pos] = s0 + q;
     p.pos[s0 + q] = pos;
+  }
+
+  if (b == 0) {   // block-uniform: the scans below synchronise the block
+    const int active = cnt > 0;
+    const int aidx = expert_excl_scan(active, s_wave);
+    const int ntile = (cnt + kGM - 1) / kGM;
+    const int tile0 = expert_excl_scan(ntile, s_wave);
+    if (tid == kMaxExperts - 1) {
+      s_tot[0] = aidx + active;
+      s_tot[1] = tile0 + ntile;
+    }
+    if (active) {
+      route[1 + aidx] = e;
+      route[1 + E + aidx] = off;
+      for (int q = 0; q < ntile; ++q) {
+        int32_t* tl = p.tiles + 1 + 3 * (tile0 + q);
+        tl[0] = e;
+        tl[1] = off + q * kGM;
+        tl[2] = min(kGM, cnt - q * kGM);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      route[0] = s_tot[0];
+      route[1 + E + s_tot[0]] = T * k;
+      p.tiles[0] = s_tot[1];
+    }
   }
 }
 
@@ -615,6 +612,7 @@ constexpr int kDnColBlocks = H / 256;   // 8
 // parked row-major in LDS and stored as 16-byte vectors.
 constexpr int kYRow = 256 + 8;          // halves per LDS row of the parked tile
 static_assert(kGM * kYRow <= DownGemm::kLds, "half a y tile fits the GEMM's LDS");
+static_assert(kGM * kMaxTopK % DownGemm::kBlockThreads == 0, "slot positions per thread");
 
 __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_down_kernel(LayerArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemm::kLds];
@@ -681,6 +679,8 @@ constexpr int kCbLds = cmax(DownGemm::kLds, DownGemm::TM * kCbRow * 4);
 __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_combine_kernel(LayerArgs a,
                                                                                          int n_items) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kCbLds];
+  __shared__ int s_pos[kGM * kMaxTopK];     // y row and weight of each (token, rank) of the tile
+  __shared__ float s_w[kGM * kMaxTopK];
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -689,6 +689,20 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_com
   const int q = item / kDnColBlocks, nb = item % kDnColBlocks;
   const PrefillWs& p = a.ws.pre;
   const int t0 = q * kGM, count = min(kGM, T - t0);
+  // The tile's slot positions and weights are requested before the GEMM and
+  // parked in LDS after it, so that the combine's y loads depend on no
+  // global round trip of their own.
+  constexpr int kPw = kGM * kMaxTopK / DownGemm::kBlockThreads;
+  int pos_r[kPw];
+  float w_r[kPw];
+#pragma unroll
+  for (int i = 0; i < kPw; ++i) {
+    const int e = tid + i * DownGemm::kBlockThreads;
+    if (e < count * k) {
+      pos_r[i] = p.pos[t0 * k + e];
+      w_r[i] = a.ws.wts[t0 * k + e];
+    }
+  }
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.shared.w2);
   const uint16_t* h16 = reinterpret_cast<const uint16_t*>(p.h16);
   const uint16_t* ag[DownGemm::NA];
@@ -706,6 +720,14 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_com
   const int rt_n = max(0, min(DownGemm::RT, (count - wm * DownGemm::TM + 31) / 32));
   DownGemm g;
   g.run(lds, ag, bg, I, rt_n);   // LDS is free afterwards
+#pragma unroll
+  for (int i = 0; i < kPw; ++i) {
+    const int e = tid + i * DownGemm::kBlockThreads;
+    if (e < count * k) {
+      s_pos[e] = pos_r[i];
+      s_w[e] = w_r[i];
+    }
+  }
 
   float* park = reinterpret_cast<float*>(lds);
   for (int part = 0; part < DownGemm::kWM; ++part) {
@@ -720,7 +742,7 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_com
                 g.acc[rt][ct][r];
     }
     __syncthreads();
-    // 64 tokens x 32 groups of 8 columns = 2048 units, 8 per thread.
+    // 64 tokens x 32 groups of 8 columns = 2048 units, four per thread.
     for (int u = tid; u < DownGemm::TM * 32; u += DownGemm::kBlockThreads) {
       const int row = u >> 5, c8 = (u & 31) * 8;
       const int lrow = part * DownGemm::TM + row;
@@ -736,8 +758,8 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_com
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j) {
         if (j < k) {
-          wj[j] = a.ws.wts[t * k + j];
-          yv[j] = *reinterpret_cast<const u32x4*>(p.y16 + (size_t)p.pos[t * k + j] * H + nb * 256 + c8);
+          wj[j] = s_w[lrow * k + j];
+          yv[j] = *reinterpret_cast<const u32x4*>(p.y16 + (size_t)s_pos[lrow * k + j] * H + nb * 256 + c8);
         }
       }
 #pragma unroll
@@ -898,8 +920,7 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& laun
   const int n_shared = (a.T + kGM - 1) / kGM;
   if (a.norm_w) launch_rmsnorm(a.resid, a.norm_w, a.eps, a.normed, a.T, stream, launch);
   launch(prefill_router_kernel, dim3(nb), dim3(kThreads), stream, a);
-  launch(prefill_scan_kernel, dim3(1), dim3(kScanThreads), stream, a, nb);
-  launch(prefill_scatter_kernel, dim3(nb), dim3(kThreads), stream, a);
+  launch(prefill_bucket_kernel, dim3(nb), dim3(kBucketThreads), stream, a, nb);
   // The grouped GEMMs' grids cover the longest possible tile list; the
   // kernels read the real one.
   const int n_gu = (n_shared + n_routed_max) * kGuColBlocks;
