@@ -238,8 +238,12 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
 // experts whose key equals M, the lowest index (first set bit of a ballot
 // per column); lane j keeps the j-th pick, computes its sigmoid score and
 // writes its slot.  The selected experts also go to s_ids[t * k + j] (LDS).
-template <int G>
-__device__ void route_tokens(const LayerArgs& a, int t0, int dt, int n, int* s_ids) {
+// kCoherent: the logits were stored by other blocks of the same launch;
+// otherwise by an earlier launch.  to_global: also store ids and weights to
+// the workspace and the caller's copies (one block per forward does).
+template <int G, bool kCoherent = true>
+__device__ void route_tokens(const LayerArgs& a, int t0, int dt, int n, int* s_ids,
+                             bool to_global = true) {
   const int lane = threadIdx.x & (kWave - 1);
   const int E = a.E, k = a.k;
   uint32_t key[G][4];
@@ -249,7 +253,10 @@ __device__ void route_tokens(const LayerArgs& a, int t0, int dt, int n, int* s_i
   for (int g = 0; g < G; ++g) {
     const int t = min(t0 + min(g, n - 1) * dt, a.T - 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) z[g][q] = load_coherent(a.ws.logits + (size_t)t * E + min(lane * 4 + q, E - 1));
+    for (int q = 0; q < 4; ++q) {
+      const float* zp = a.ws.logits + (size_t)t * E + min(lane * 4 + q, E - 1);
+      z[g][q] = kCoherent ? load_coherent(zp) : *zp;
+    }
   }
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -293,12 +300,14 @@ __device__ void route_tokens(const LayerArgs& a, int t0, int dt, int n, int* s_i
     const float sc = lane < k ? sigmoid(unord_f32(my_key[g])) : 0.f;
     const float sum = __shfl(wave_sum_lane63(sc), kWave - 1);
     if (lane < k) {
-      const float w = (a.renormalize ? sc / sum : sc) * a.routed_scale;
-      a.ws.ids[t * k + lane] = my_e[g];
-      a.ws.wts[t * k + lane] = w;
       s_ids[t * k + lane] = my_e[g];
-      if (a.ids_out) a.ids_out[t * k + lane] = my_e[g];
-      if (a.wts_out) a.wts_out[t * k + lane] = w;
+      if (to_global) {
+        const float w = (a.renormalize ? sc / sum : sc) * a.routed_scale;
+        a.ws.ids[t * k + lane] = my_e[g];
+        a.ws.wts[t * k + lane] = w;
+        if (a.ids_out) a.ids_out[t * k + lane] = my_e[g];
+        if (a.wts_out) a.wts_out[t * k + lane] = w;
+      }
     }
   }
 }
@@ -465,8 +474,10 @@ __device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, in
 // Router: wave w of block b computes the logits of expert 4b + w for all T
 // tokens; the tokens' x vectors stream through LDS kRouteXChunk at a time
 // (for the pre-norm block, normalised from r on the way in).  The last
-// block to finish routes every token and builds the routing table.
-template <bool kNorm>
+// block to finish routes every token and builds the routing table; with
+// kFused (small batches, fused_routing_applies) the launch ends with the
+// logits and the gate/up launch routes instead.
+template <bool kNorm, bool kFused>
 __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   __shared__ u32x4 xs[kRouteXChunk * kVecH];
   __shared__ RouteLds L;
@@ -476,8 +487,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   const int wave = threadIdx.x / kWave;
   const int e = blockIdx.x * kRouterRows + wave;
   const int er = min(e, a.E - 1);
-  for (int i = threadIdx.x; i < kMaxExperts; i += kThreads) L.cnt[i] = 0;
-  for (int i = threadIdx.x; i < kMaxExperts * kMaskWords; i += kThreads) L.occ[i] = 0;
+  if (!kFused) {
+    for (int i = threadIdx.x; i < kMaxExperts; i += kThreads) L.cnt[i] = 0;
+    for (int i = threadIdx.x; i < kMaxExperts * kMaskWords; i += kThreads) L.occ[i] = 0;
+  }
   u32x4 wv[kVecPerLaneH];
   const u32x4* row = reinterpret_cast<const u32x4*>(a.router_w + (size_t)er * H);
 #pragma unroll
@@ -511,7 +524,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
     for (int j = 0; j < kRouteXChunk; ++j) {
       if (j < n) {
         const float z = wave_sum_lane63(acc[j]);
-        if (lane == kWave - 1 && e < a.E) store_coherent(a.ws.logits + (size_t)(c0 + j) * a.E + e, z + bias);
+        if (lane == kWave - 1 && e < a.E) {
+          float* zp = a.ws.logits + (size_t)(c0 + j) * a.E + e;
+          if (kFused) *zp = z + bias;
+          else store_coherent(zp, z + bias);
+        }
       }
     }
     if (c0 + kRouteXChunk < a.T) {
@@ -519,6 +536,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
       stage(c0 + kRouteXChunk);
     }
   }
+  if (kFused) return;
   // The last router block sees every logit.
   if (!last_block_ticket(a.ws.header + kHdrRouterDone, gridDim.x, &s_flag)) return;
   // Wave w routes tokens w, w + 4, ...: up to 4 at a time, interleaved.
@@ -535,14 +553,89 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   build_route_table(a, L);
 }
 
+// Routing of a small batch inside one block, from the logits of the router
+// launch: every routed gate/up block repeats it, which costs less than a
+// completion ticket and a one-block routing step between the two launches
+// as long as every wave ranks at most one token and the whole grid is
+// resident at once (fused_routing_applies).  Wave w ranks token w; wave 0
+// then sorts the slots by (expert, slot) — slot s
+// lands at the number of slots with a smaller expert plus the earlier
+// slots of its own — and marks where each expert's run starts, which gives
+// U in ascending order.  Item `ai` (the ai-th expert of U) is returned in
+// meta = {|U|, expert, first sorted position, slot count}; its slots are
+// sorted_s[pos .. pos + count).  The writer block also stores the ids,
+// the weights and the routing table for the down launch.
+constexpr int kFusedMaxSlots = 16;   // (1 + 16) x 64 gate/up blocks: resident at 5 per CU
+__host__ __device__ constexpr bool fused_routing_applies(int T, int k) {
+  return T <= kRouteWaves && T * k <= kFusedMaxSlots;
+}
+
+struct FusedRouteLds {
+  int ids[kWave];
+  int sorted_e[kWave];
+  int16_t sorted_s[kWave];
+  int meta[4];
+};
+
+__device__ void fused_route(const LayerArgs& a, int ai, bool writer, FusedRouteLds& L) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int T = a.T, E = a.E, nslots = a.T * a.k;
+  if (wave < T) route_tokens<1, false>(a, wave, kRouteWaves, 1, L.ids, writer);
+  __syncthreads();
+  if (wave == 0 && lane < nslots) {
+    const int e = L.ids[lane];
+    int less = 0, before = 0;
+    for (int j = 0; j < nslots; ++j) {
+      const int ej = L.ids[j];
+      less += ej < e;
+      before += (ej == e) & (j < lane);
+    }
+    L.sorted_e[less + before] = e;
+    L.sorted_s[less + before] = (int16_t)lane;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int p = lane;
+    const int e = p < nslots ? L.sorted_e[p] : -1;
+    const bool first = p < nslots && (p == 0 || e != L.sorted_e[p > 0 ? p - 1 : 0]);
+    const uint64_t fm = __ballot(first);
+    const int n = __popcll(fm);
+    const int uidx = __popcll(fm & ((1ull << p) - 1ull));
+    const uint64_t above = p < kWave - 1 ? fm >> (p + 1) : 0ull;
+    const int next = above ? p + 1 + (int)__builtin_ctzll(above) : nslots;
+    if (first && uidx == ai) {
+      L.meta[1] = e;
+      L.meta[2] = p;
+      L.meta[3] = next - p;
+    }
+    if (lane == 0) L.meta[0] = n;
+    if (writer) {
+      int32_t* route = a.ws.route;
+      if (first) {
+        route[1 + uidx] = e;
+        route[1 + E + uidx] = p;
+      }
+      if (p < nslots) route[2 + 2 * E + p] = L.sorted_s[p];
+      if (lane == 0) {
+        route[0] = n;
+        route[1 + E + n] = nslots;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // Blocks [0, kUnitsPerExpert): the shared expert for all T tokens (h rows
-// T*k + t); then routed items.
-template <bool kFp4>
+// T*k + t); then routed items.  kFused: the routed blocks route the batch
+// themselves (fused_route) instead of reading the routing table.
+template <bool kFp4, bool kFused>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void gateup_kernel(LayerArgs a) {
   __shared__ u32x4 xs[kXChunk * kVecH];
   __shared__ int16_t s_slots[kDecodeMaxT];
   __shared__ int s_meta[4];
+  __shared__ FusedRouteLds FL;
   if ((int)blockIdx.x < kUnitsPerExpert) {
     const int unit = blockIdx.x;
     GateUpRows<kFp4> wv;
@@ -553,6 +646,15 @@ void gateup_kernel(LayerArgs a) {
   const int b = blockIdx.x - kUnitsPerExpert;
   const int ai = b / kUnitsPerExpert;
   const int unit = b - ai * kUnitsPerExpert;
+  if (kFused) {
+    fused_route(a, ai, b == 0, FL);
+    if (ai >= FL.meta[0]) return;
+    const int e = FL.meta[1], off = FL.meta[2], cnt = FL.meta[3];
+    GateUpRows<kFp4> wv;
+    wv.load(a.routed, e, unit * kPairsPerItem);
+    gateup_compute(wv, unit * kPairsPerItem, cnt, TokenList{FL.sorted_s + off, a.k, 0}, a.x, a.ws.h, xs);
+    return;
+  }
   const int32_t* route = a.ws.route;
   const int E = a.E;
   // |U|, U[ai] and its slot range in one round trip (all in bounds: ai < E).
@@ -943,11 +1045,20 @@ template <bool kFp4>
 static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
   const int n_router = (a.E + kRouterRows - 1) / kRouterRows;
   const int n_routed = min(a.E, a.T * a.k) * kUnitsPerExpert;
-  if (a.norm_w)
-    launch(route_kernel<true>, dim3(n_router), dim3(kThreads), stream, a);
-  else
-    launch(route_kernel<false>, dim3(n_router), dim3(kThreads), stream, a);
-  launch(gateup_kernel<kFp4>, dim3(kUnitsPerExpert + n_routed), dim3(kThreads), stream, a);
+  const dim3 g_route(n_router), g_gateup(kUnitsPerExpert + n_routed);
+  if (fused_routing_applies(a.T, a.k)) {
+    if (a.norm_w)
+      launch(route_kernel<true, true>, g_route, dim3(kThreads), stream, a);
+    else
+      launch(route_kernel<false, true>, g_route, dim3(kThreads), stream, a);
+    launch(gateup_kernel<kFp4, true>, g_gateup, dim3(kThreads), stream, a);
+  } else {
+    if (a.norm_w)
+      launch(route_kernel<true, false>, g_route, dim3(kThreads), stream, a);
+    else
+      launch(route_kernel<false, false>, g_route, dim3(kThreads), stream, a);
+    launch(gateup_kernel<kFp4, false>, g_gateup, dim3(kThreads), stream, a);
+  }
   launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
   return hipGetLastError();
 }

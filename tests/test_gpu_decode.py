@@ -49,7 +49,8 @@ def ws_region(r, name, T, dtype, count):
 
 @pytest.mark.parametrize("T,bias,x_seed", [(1, False, 0), (8, False, 0), (32, True, 0),
                                            (2, False, 1), (3, True, 2), (13, False, 3),
-                                           (47, True, 4), (64, False, 5), (64, True, 6)])
+                                           (47, True, 4), (64, False, 5), (64, True, 6),
+                                           (10, True, 8), (11, False, 9)])
 def test_decode_matches_oracle(dev, T, bias, x_seed):
     say(f"decode parity T={T} bias={bias} x_seed={x_seed}")
     xb = make_x(T, seed=SEED, x_seed=x_seed)
