@@ -117,7 +117,7 @@ struct GateUpRows<false> {
     for (int i = 0; i < kVecPerLaneH; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        w[r][i] = reinterpret_cast<const u32x4*>(w13 + (size_t)row[r] * H)[lane + i * kWave];
+        w[r][i] = load_stream(reinterpret_cast<const u32x4*>(w13 + (size_t)row[r] * H) + lane + i * kWave);
     g = 1.0f;
   }
   __device__ __forceinline__ void load(const Bank& bank, int e, int p0) {
@@ -148,8 +148,8 @@ struct GateUpRows<true> {
     for (int i = 0; i < kVecPerLaneH; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        q[r][i] = reinterpret_cast<const uint32_t*>(w13 + (size_t)row[r] * (H / 2))[lane + i * kWave];
-        sc[r][i] = s13[(size_t)row[r] * (H / 16) + (lane * 8 + i * 512) / 16];
+        q[r][i] = load_stream(reinterpret_cast<const uint32_t*>(w13 + (size_t)row[r] * (H / 2)) + lane + i * kWave);
+        sc[r][i] = load_stream(s13 + (size_t)row[r] * (H / 16) + (lane * 8 + i * 512) / 16);
       }
     g = bank.w13_gscale[e];
   }
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   u32x4 wv[kVecPerLaneH];
   const u32x4* row = reinterpret_cast<const u32x4*>(a.router_w + (size_t)er * H);
 #pragma unroll
-  for (int i = 0; i < kVecPerLaneH; ++i) wv[i] = row[lane + i * kWave];
+  for (int i = 0; i < kVecPerLaneH; ++i) wv[i] = load_stream(row + lane + i * kWave);
   const float bias = a.router_b ? a.router_b[er] : 0.f;
   u32x4 gv{};
   if (kNorm) gv = reinterpret_cast<const u32x4*>(a.norm_w)[threadIdx.x];
@@ -738,7 +738,7 @@ struct DownRows<false> {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int r = 0; r < kDownRowsPerBlock; ++r)
-      w[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I)[lane];
+      w[r] = load_stream(reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I) + lane);
   }
   __device__ __forceinline__ float scale() const { return 1.0f; }
   // Lane partial of row r: its 8 columns of w2 . h.
@@ -772,8 +772,8 @@ struct DownRows<true> {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int r = 0; r < kDownRowsPerBlock; ++r) {
-      q[r] = reinterpret_cast<const uint32_t*>(w2 + (size_t)(r0 + r) * (I / 2))[lane];
-      sc[r] = s2[(size_t)(r0 + r) * (I / 16) + lane / 2];
+      q[r] = load_stream(reinterpret_cast<const uint32_t*>(w2 + (size_t)(r0 + r) * (I / 2)) + lane);
+      sc[r] = load_stream(s2 + (size_t)(r0 + r) * (I / 16) + lane / 2);
     }
     g = bank.w2_gscale[d.e];
   }
@@ -956,7 +956,7 @@ struct DenseW2Rows {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int r = 0; r < kDownRowsPerBlock; ++r)
-      w[r] = reinterpret_cast<const u32x4*>(a.w2 + (size_t)(r0 + r) * a.inter + c * kDenseChunk)[lane];
+      w[r] = load_stream(reinterpret_cast<const u32x4*>(a.w2 + (size_t)(r0 + r) * a.inter + c * kDenseChunk) + lane);
   }
   __device__ __forceinline__ void widen(float (&f)[kDownRowsPerBlock][8]) const {
 #pragma unroll

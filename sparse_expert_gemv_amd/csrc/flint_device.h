@@ -102,6 +102,12 @@ __device__ __forceinline__ float dpp(float v) {
       0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xF, true));
 }
 
+// Weight loads: every weight byte is read once per forward, so the loads
+// carry the non-temporal hint and do not displace the small data that is
+// read many times (x, h, routing tables) from L2 and the Infinity Cache.
+template <typename V>
+__device__ __forceinline__ V load_stream(const V* p) { return __builtin_nontemporal_load(p); }
+
 // Sum over the 64 lanes of a wave; the total is valid in lane 63.
 __device__ __forceinline__ float wave_sum_lane63(float v) {
   v += dpp<0xB1>(v);        // quad_perm [1,0,3,2]
