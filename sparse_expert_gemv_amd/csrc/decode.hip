@@ -697,8 +697,8 @@ static_assert(kDecodeMaxT / kDnSlots <= (1 << kDnSubBits) &&
 static_assert(kDecodeMaxT * kMaxTopK / kDnSlots + kMaxExperts + 1 + kDecodeMaxT / kDnSlots <= kMaxDownWork,
               "work list size");
 
-// A work entry: slots [j0, j0 + nj) of one item (an active expert, or the
-// shared expert whose slots are the T tokens).
+// A work entry: slots [j0, j0 + nj) of one item (item 0: the shared
+// expert, whose slots are the T tokens; item i > 0: active expert i - 1).
 struct DownItem {
   int e;            // expert index in its bank
   bool shared;
@@ -706,16 +706,26 @@ struct DownItem {
   int j0, nj;
 };
 
-__device__ __forceinline__ DownItem down_entry(const LayerArgs& a, int entry, int n,
+__device__ __forceinline__ DownItem shared_entry(const LayerArgs& a, int q) {
+  DownItem d;
+  d.shared = true;
+  d.e = 0;
+  d.off = 0;
+  d.j0 = q * kDnSlots;
+  d.nj = min(kDnSlots, a.T - d.j0);
+  return d;
+}
+
+__device__ __forceinline__ DownItem down_entry(const LayerArgs& a, int entry,
                                                const int16_t* s_active, const int16_t* s_off) {
   const int item = entry >> kDnSubBits, q = entry & ((1 << kDnSubBits) - 1);
+  if (item == 0) return shared_entry(a, q);
   DownItem d;
-  d.shared = item >= n;
-  const int cnt = d.shared ? a.T : s_off[item + 1] - s_off[item];
-  d.e = d.shared ? 0 : s_active[item];
-  d.off = d.shared ? 0 : s_off[item];
+  d.shared = false;
+  d.e = s_active[item - 1];
+  d.off = s_off[item - 1];
   d.j0 = q * kDnSlots;
-  d.nj = min(kDnSlots, cnt - d.j0);
+  d.nj = min(kDnSlots, s_off[item] - d.off - d.j0);
   return d;
 }
 
@@ -829,9 +839,11 @@ __device__ __forceinline__ void down_entry_rows(const LayerArgs& a, const DownIt
 }
 
 // Down + combine.  Block b owns output rows [8b, 8b + 8) of every token.
-// Its work: every active expert and the shared expert, cut into entries of
+// Its work: the shared expert and every active expert, cut into entries of
 // up to kDnSlots slots (an expert hit by many tokens spreads over several
-// waves); wave w takes entries w, w + 8, ... and keeps the next two
+// waves), the shared expert's first: they need no routing table, so their
+// rows and h are requested while the table is still on its way.  Wave w
+// takes entries w, w + 8, ... and keeps the next two
 // entries' w2 rows and h rows in flight while it reduces the current one
 // (two-slot entries keep three buffers within the register budget).  Lane l holds
 // columns [8l, 8l + 8) of each row.  Per (h row, output row) the 64-lane
@@ -851,62 +863,98 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   const int r0 = blockIdx.x * kDownRowsPerBlock;
   const int T = a.T, k = a.k, E = a.E;
   const int32_t* route = a.ws.route;
-  // The routing table in one round trip (whole arrays, no dependence on |U|).
-  for (int q = threadIdx.x; q < E; q += kDownThreads) s_active[q] = (int16_t)route[1 + q];
-  for (int q = threadIdx.x; q <= E; q += kDownThreads) s_off[q] = (int16_t)route[1 + E + q];
-  for (int q = threadIdx.x; q < T * k; q += kDownThreads) {
-    s_slots[q] = (int16_t)route[2 + 2 * E + q];
-    s_wts[q] = a.ws.wts[q];   // for the combine, fetched with the table
+  // The routing table in one round trip (whole arrays, no dependence on |U|;
+  // one element of each per thread), requested before the shared expert's
+  // entries so that waiting for it leaves those in flight.
+  const int q = threadIdx.x;
+  int v_act = 0, v_off = 0, v_slot = 0;
+  float v_wt = 0.f;
+  if (q < E) v_act = route[1 + q];
+  if (q <= E) v_off = route[1 + E + q];
+  if (q < T * k) {
+    v_slot = route[2 + 2 * E + q];
+    v_wt = a.ws.wts[q];   // for the combine, fetched with the table
   }
   const int n = route[0];
-  __syncthreads();
 
-  // Work list: item i (i < n: active expert i; i == n: shared) contributes
-  // ceil(cnt_i / kDnSlots) entries, laid out by an exclusive scan.
+  // Three entries per wave in flight: the one being reduced and the next
+  // two (rows and h), rotated through pa, pb, pc.  The shared expert's
+  // entries are the first n_sh of the work list.
+  const int n_sh = (T + kDnSlots - 1) / kDnSlots;
+  DownRows<kFp4> pa, pb, pc;
+  DownItem da{}, db{}, dc{};
+  int w = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform: scalar branches below
+  // Each path stores the table on its own, so that the wait for the table
+  // leaves exactly that path's entry loads in flight (at a join, the wait
+  // would have to assume none were issued and wait for all); the distinct
+  // asm markers keep the copies from being merged.
+  auto store_table = [&]() __attribute__((always_inline)) {
+    if (q < E) s_active[q] = (int16_t)v_act;
+    if (q <= E) s_off[q] = (int16_t)v_off;
+    if (q < T * k) {
+      s_slots[q] = (int16_t)v_slot;
+      s_wts[q] = v_wt;
+    }
+  };
+  if (w + kDownWaves < n_sh) {
+    da = shared_entry(a, w);
+    prefetch_entry(pa, a, da, r0, s_slots);
+    db = shared_entry(a, w + kDownWaves);
+    prefetch_entry(pb, a, db, r0, s_slots);
+    store_table();
+    asm volatile("; down: two shared entries in flight" ::: "memory");
+  } else if (w < n_sh) {
+    da = shared_entry(a, w);
+    prefetch_entry(pa, a, da, r0, s_slots);
+    store_table();
+    asm volatile("; down: one shared entry in flight" ::: "memory");
+  } else {
+    store_table();
+  }
+  lds_barrier();
+
+  // Work list: item 0 (the shared expert, T slots) and items 1..n (active
+  // expert i - 1) contribute ceil(cnt / kDnSlots) entries each, laid out by
+  // an exclusive scan.
   const int it = threadIdx.x;
-  const int cnt = it < n ? s_off[it + 1] - s_off[it] : (it == n ? T : 0);
+  const int cnt = it == 0 ? T : (it <= n ? s_off[it] - s_off[it - 1] : 0);
   const int nsub = (cnt + kDnSlots - 1) / kDnSlots;
   const int incl = wave_incl_scan(nsub);
   if (lane == kWave - 1) s_scan[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int base = incl - nsub, total = 0;
-  for (int w = 0; w < kDownWaves; ++w) {
-    if (w < wave) base += s_scan[w];
-    total += s_scan[w];
+  for (int v = 0; v < kDownWaves; ++v) {
+    if (v < wave) base += s_scan[v];
+    total += s_scan[v];
   }
-  for (int q = 0; q < nsub; ++q) s_work[base + q] = (int16_t)((it << kDnSubBits) | q);
-  __syncthreads();
+  for (int j = 0; j < nsub; ++j) s_work[base + j] = (int16_t)((it << kDnSubBits) | j);
+  lds_barrier();
 
-  // Three entries per wave in flight: the one being reduced and the next
-  // two (rows and h), rotated through pa, pb, pc.
-  DownRows<kFp4> pa, pb, pc;
-  DownItem da{}, db{}, dc{};
-  int w = wave;
-  if (w < total) {
-    da = down_entry(a, s_work[w], n, s_active, s_off);
+  if (w >= n_sh && w < total) {
+    da = down_entry(a, s_work[w], s_active, s_off);
     prefetch_entry(pa, a, da, r0, s_slots);
   }
-  if (w + kDownWaves < total) {
-    db = down_entry(a, s_work[w + kDownWaves], n, s_active, s_off);
+  if (w + kDownWaves >= n_sh && w + kDownWaves < total) {
+    db = down_entry(a, s_work[w + kDownWaves], s_active, s_off);
     prefetch_entry(pb, a, db, r0, s_slots);
   }
   while (w < total) {
     if (w + 2 * kDownWaves < total) {
-      dc = down_entry(a, s_work[w + 2 * kDownWaves], n, s_active, s_off);
+      dc = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
       prefetch_entry(pc, a, dc, r0, s_slots);
     }
     down_entry_rows(a, da, pa, s_slots, part);
     w += kDownWaves;
     if (w >= total) break;
     if (w + 2 * kDownWaves < total) {
-      da = down_entry(a, s_work[w + 2 * kDownWaves], n, s_active, s_off);
+      da = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
       prefetch_entry(pa, a, da, r0, s_slots);
     }
     down_entry_rows(a, db, pb, s_slots, part);
     w += kDownWaves;
     if (w >= total) break;
     if (w + 2 * kDownWaves < total) {
-      db = down_entry(a, s_work[w + 2 * kDownWaves], n, s_active, s_off);
+      db = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
       prefetch_entry(pb, a, db, r0, s_slots);
     }
     down_entry_rows(a, dc, pc, s_slots, part);
