@@ -2,24 +2,28 @@
 // NVFP4 (W4A16) expert weights.
 //
 // Three launches on the caller's stream:
-//   1. route   : router GEMV, one expert row per wave for all T tokens (64
-//                blocks of 4 waves; for the pre-norm block each block
-//                normalises the rows it stages, and block 0 stores them).
+//   1. route   : router GEMV over 64 blocks of four expert rows each (4
+//                waves, one row each; for the pre-norm block every block
+//                normalises the rows it stages, block 0 storing them; bare
+//                layer with T > 8: 16 waves, each all four rows for its
+//                tokens).
 //                The last block to finish picks every token's top-k by
 //                sigmoid score (a wave per token), computes the routing
 //                weights and buckets every (token, rank) slot by expert into
 //                the routing table (U ascending, slots grouped by expert in
-//                ascending slot order).
+//                ascending slot order).  For small batches (T <= 4,
+//                T * k <= 16) the launch ends with the logits and every
+//                routed gate/up block routes the batch itself.
 //   2. gate/up : 64 blocks for the shared expert (first, so that they stream
 //                from the start: they need no routing), then (active expert
 //                a, 8 gate/up row pairs) per block; the rows are streamed
 //                once for all of the expert's tokens; SiLU-and-mul in
 //                registers; h stays fp32.
-//   3. down    : 8 output rows of every token per block, over the |U| active
-//                experts and the shared expert, each expert's w2 rows read
-//                once; the partial dot products meet in LDS and combine as
-//                out = shared + sum_j w_j * routed_j (+ r for the pre-norm
-//                block) in a fixed order, rounded once to bf16.
+//   3. down    : 8 output rows of every token per block, over the shared
+//                expert and the |U| active experts, each expert's w2 rows
+//                read once; the partial dot products meet in LDS and combine
+//                as out = shared + sum_j w_j * routed_j (+ r for the
+//                pre-norm block) in a fixed order, rounded once to bf16.
 // The one hand-off inside a launch (router blocks -> routing block) uses a
 // completion ticket in the workspace header and coherent (write-through)
 // stores/loads, never whole-cache flushes; between launches the stream
@@ -44,7 +48,11 @@ constexpr int kVecH = H / 8;                  // 16-byte vectors per H row (256)
 constexpr int kVecPerLaneH = kVecH / kWave;   // 4
 constexpr int kRouteWaves = kThreads / kWave;
 constexpr int kRouterRows = kRouteWaves;      // router: one expert row per wave
-constexpr int kRouteXChunk = 8;               // tokens staged in LDS at a time (32 KiB)
+constexpr int kRouteXChunk = 8;               // tokens staged in LDS at a time (32 KiB), pre-norm block
+constexpr int kRouteBareMinT = 8;            // larger bare-layer batches: the 16-wave router
+constexpr int kRouteBareThreads = 1024;       // bare-layer router: 16 waves per block
+constexpr int kRouteBareWaves = kRouteBareThreads / kWave;
+constexpr int kRouteBareXChunk = 32;          // tokens staged in LDS at a time (128 KiB), bare layer
 constexpr int kPairsPerItem = 8;              // gate/up item: 8 (gate, up) row pairs
 constexpr int kUnitsPerExpert = I / kPairsPerItem;  // 64
 constexpr int kXChunk = 4;                    // tokens staged in LDS at a time (16 KiB)
@@ -234,10 +242,13 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
 // the G selections interleaved round by round.  Ranks on the logit (the
 // sigmoid is strictly increasing), ties to the lower expert index.  Lane l
 // holds the order-preserving keys of experts 4l .. 4l + 3 (0 = empty: no
-// finite logit maps to 0); round j takes the wave maximum M and, among the
-// experts whose key equals M, the lowest index (first set bit of a ballot
-// per column); lane j keeps the j-th pick, computes its sigmoid score and
-// writes its slot.  The selected experts also go to s_ids[t * k + j] (LDS).
+// finite logit maps to 0), sorted by (key descending, expert ascending), so
+// the lane's head is its best candidate; round j takes the wave maximum M
+// of the heads, the lowest lane whose head equals M wins (lower lanes hold
+// lower experts, and a lane's equal keys are ordered by expert), and the
+// winner pops its head.  Lane j keeps the j-th pick, computes its sigmoid
+// score and writes its slot.  The selected experts also go to
+// s_ids[t * k + j] (LDS).
 // kCoherent: the logits were stored by other blocks of the same launch;
 // otherwise by an earlier launch.  to_global: also store ids and weights to
 // the workspace and the caller's copies (one block per forward does).
@@ -247,6 +258,7 @@ __device__ void route_tokens(const LayerArgs& a, int t0, int dt, int n, int* s_i
   const int lane = threadIdx.x & (kWave - 1);
   const int E = a.E, k = a.k;
   uint32_t key[G][4];
+  int ex[G][4];
   float z[G][4];
   // Unconditional (clamped) loads: all of them in flight at once.
 #pragma unroll
@@ -259,9 +271,28 @@ __device__ void route_tokens(const LayerArgs& a, int t0, int dt, int n, int* s_i
     }
   }
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) key[g][q] = lane * 4 + q < E ? ord_f32(z[g][q]) : 0u;
+    for (int q = 0; q < 4; ++q) {
+      key[g][q] = lane * 4 + q < E ? ord_f32(z[g][q]) : 0u;
+      ex[g][q] = lane * 4 + q;
+    }
+    // Five compare-exchanges sort the four (key desc, expert asc).
+    auto cx = [&](int i, int j) __attribute__((always_inline)) {
+      const bool sw = key[g][j] > key[g][i] || (key[g][j] == key[g][i] && ex[g][j] < ex[g][i]);
+      const uint32_t ki = key[g][i], kj = key[g][j];
+      const int ei = ex[g][i], ej = ex[g][j];
+      key[g][i] = sw ? kj : ki;
+      key[g][j] = sw ? ki : kj;
+      ex[g][i] = sw ? ej : ei;
+      ex[g][j] = sw ? ei : ej;
+    };
+    cx(0, 1);
+    cx(2, 3);
+    cx(0, 2);
+    cx(1, 3);
+    cx(1, 2);
+  }
   int my_e[G];
   uint32_t my_key[G];
 #pragma unroll
@@ -273,20 +304,22 @@ __device__ void route_tokens(const LayerArgs& a, int t0, int dt, int n, int* s_i
   for (int j = 0; j < k; ++j) {
     uint32_t m[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) m[g] = max(max(key[g][0], key[g][1]), max(key[g][2], key[g][3]));
+    for (int g = 0; g < G; ++g) m[g] = key[g][0];
     wave_max_u32_lane63_multi<G>(m);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const uint32_t M = (uint32_t)__builtin_amdgcn_readlane((int)m[g], 63);
-      int best = 4 * kWave;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint64_t hit = __ballot(key[g][q] == M);
-        if (hit) best = min(best, 4 * (int)__builtin_ctzll(hit) + q);
+      const int win = (int)__builtin_ctzll(__ballot(key[g][0] == M));
+      const int best = __builtin_amdgcn_readlane(ex[g][0], win);
+      if (lane == win) {
+        key[g][0] = key[g][1];
+        key[g][1] = key[g][2];
+        key[g][2] = key[g][3];
+        key[g][3] = 0u;
+        ex[g][0] = ex[g][1];
+        ex[g][1] = ex[g][2];
+        ex[g][2] = ex[g][3];
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (lane * 4 + q == best) key[g][q] = 0u;
       if (lane == j) {
         my_e[g] = best;
         my_key[g] = M;
@@ -375,6 +408,26 @@ __device__ void build_route_table(const LayerArgs& a, RouteLds& L) {
     for (int w = 0; w < (s >> 5); ++w) rank += __popc(m[w]);
     r_slots[L.aoff[e] + rank] = s;
   }
+}
+
+// The end of a router launch: the last block to finish (it sees every
+// logit) routes every token — wave w takes tokens w, w + kWaves, ..., up to
+// 4 at a time, interleaved — and builds the routing table.
+template <int kWaves>
+__device__ __forceinline__ void route_tail(const LayerArgs& a, RouteLds& L, int* s_flag) {
+  const int wave = threadIdx.x / kWave;
+  if (!last_block_ticket(a.ws.header + kHdrRouterDone, gridDim.x, s_flag)) return;
+  const int mine = (a.T - wave + kWaves - 1) / kWaves;
+  if (mine == 1) {
+    route_tokens<1>(a, wave, kWaves, 1, L.ids);
+  } else if (mine == 2) {
+    route_tokens<2>(a, wave, kWaves, 2, L.ids);
+  } else {
+    for (int g0 = 0; g0 < mine; g0 += 4)
+      route_tokens<4>(a, wave + g0 * kWaves, kWaves, min(4, mine - g0), L.ids);
+  }
+  lds_barrier();   // the selections are in LDS; their global stores need not land yet
+  build_route_table(a, L);
 }
 
 // Lane exchange for the transposed reduction: lane l reads lane l ^ 4 (or
@@ -471,15 +524,17 @@ __device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, in
   }
 }
 
-// Router: wave w of block b computes the logits of expert 4b + w for all T
-// tokens; the tokens' x vectors stream through LDS kRouteXChunk at a time
-// (for the pre-norm block, normalised from r on the way in).  The last
-// block to finish routes every token and builds the routing table; with
-// kFused (small batches, fused_routing_applies) the launch ends with the
-// logits and the gate/up launch routes instead.
+// Router of the pre-norm block and of small bare-layer batches: wave w of
+// block b computes the logits of expert 4b + w for all T tokens; the
+// tokens' rows stream through LDS kRouteXChunk at a time (for the pre-norm
+// block, normalised from r on the way in).  The last block to finish routes
+// every token and builds the routing table; with kFused (small batches,
+// fused_routing_applies) the launch ends with the logits and the gate/up
+// launch routes instead.
 template <bool kNorm, bool kFused>
 __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
-  __shared__ u32x4 xs[kRouteXChunk * kVecH];
+  constexpr int XC = kRouteXChunk;
+  __shared__ u32x4 xs[XC * kVecH];
   __shared__ RouteLds L;
   __shared__ int s_flag;
   __shared__ float s_ss[kRouteWaves * kRouteXChunk];
@@ -499,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   u32x4 gv{};
   if (kNorm) gv = reinterpret_cast<const u32x4*>(a.norm_w)[threadIdx.x];
   auto stage = [&](int c0) __attribute__((always_inline)) {
-    const int n = min(kRouteXChunk, a.T - c0);
+    const int n = min(XC, a.T - c0);
     if (kNorm) {
       stage_normed_rows(a, c0, n, xs, gv, s_ss);
     } else {
@@ -507,13 +562,13 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
     }
   };
   stage(0);   // in flight together with the router rows
-  for (int c0 = 0; c0 < a.T; c0 += kRouteXChunk) {
-    const int n = min(kRouteXChunk, a.T - c0);
+  for (int c0 = 0; c0 < a.T; c0 += XC) {
+    const int n = min(XC, a.T - c0);
     wait_vmem_all();
     __syncthreads();
-    float acc[kRouteXChunk];
+    float acc[XC];
 #pragma unroll
-    for (int j = 0; j < kRouteXChunk; ++j) {
+    for (int j = 0; j < XC; ++j) {
       acc[j] = 0.f;
       if (j < n) {
 #pragma unroll
@@ -521,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < kRouteXChunk; ++j) {
+    for (int j = 0; j < XC; ++j) {
       if (j < n) {
         const float z = wave_sum_lane63(acc[j]);
         if (lane == kWave - 1 && e < a.E) {
@@ -531,26 +586,85 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
         }
       }
     }
-    if (c0 + kRouteXChunk < a.T) {
+    if (c0 + XC < a.T) {
       lds_barrier();   // every wave is done with this chunk's x
-      stage(c0 + kRouteXChunk);
+      stage(c0 + XC);
     }
   }
   if (kFused) return;
-  // The last router block sees every logit.
-  if (!last_block_ticket(a.ws.header + kHdrRouterDone, gridDim.x, &s_flag)) return;
-  // Wave w routes tokens w, w + 4, ...: up to 4 at a time, interleaved.
-  const int mine = (a.T - wave + kRouteWaves - 1) / kRouteWaves;
-  if (mine == 1) {
-    route_tokens<1>(a, wave, kRouteWaves, 1, L.ids);
-  } else if (mine == 2) {
-    route_tokens<2>(a, wave, kRouteWaves, 2, L.ids);
-  } else {
-    for (int g0 = 0; g0 < mine; g0 += 4)
-      route_tokens<4>(a, wave + g0 * kRouteWaves, kRouteWaves, min(4, mine - g0), L.ids);
+  route_tail<kRouteWaves>(a, L, &s_flag);
+}
+
+// Router of larger bare-layer batches (T > kRouteBareMinT): 16 waves per
+// block, and every wave holds all four of the block's router rows (experts
+// 4b .. 4b + 3) and computes them for its tokens (wave w: tokens w, w + 16
+// of each chunk of kRouteBareXChunk staged in LDS), so each x vector is
+// read from LDS once per block rather than once per row; the 8 (row, token)
+// sums of a wave meet in one transposed 8-value reduction.  The routing
+// tail then has 16 waves for the top-k.  Every wave reading all four rows
+// (64 KiB per wave from L2) does not pay off for small batches.
+__global__ __launch_bounds__(kRouteBareThreads) void route_bare_kernel(LayerArgs a) {
+  static_assert(kRouteBareXChunk == 2 * kRouteBareWaves, "two tokens per wave and chunk");
+  __shared__ u32x4 xs[kRouteBareXChunk * kVecH];
+  __shared__ RouteLds L;
+  __shared__ int s_flag;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int e0 = blockIdx.x * kRouterRows;
+  for (int i = threadIdx.x; i < kMaxExperts; i += kRouteBareThreads) L.cnt[i] = 0;
+  for (int i = threadIdx.x; i < kMaxExperts * kMaskWords; i += kRouteBareThreads) L.occ[i] = 0;
+  u32x4 wv[kRouterRows][kVecPerLaneH];
+#pragma unroll
+  for (int r = 0; r < kRouterRows; ++r) {
+    const u32x4* row = reinterpret_cast<const u32x4*>(a.router_w + (size_t)min(e0 + r, a.E - 1) * H);
+#pragma unroll
+    for (int i = 0; i < kVecPerLaneH; ++i) wv[r][i] = load_stream(row + lane + i * kWave);
   }
-  lds_barrier();   // the selections are in LDS; their global stores need not land yet
-  build_route_table(a, L);
+  // Lane l < 8 stores the sum for row bitrev3(l) / 2 of token bitrev3(l) % 2.
+  const int my_r = bitrev3(lane & 7) >> 1, my_g = bitrev3(lane & 7) & 1;
+  const int my_e = e0 + my_r;
+  const float bias = a.router_b && lane < 8 ? a.router_b[min(my_e, a.E - 1)] : 0.f;
+  // Thread i stages 16-byte vector i % 256 of rows 4p + i / 256 (p = 0, 1, ...).
+  auto stage = [&](int c0) __attribute__((always_inline)) {
+    const int n = min(kRouteBareXChunk, a.T - c0);
+    const int v = threadIdx.x & (kVecH - 1);
+    for (int j = threadIdx.x / kVecH; j < n; j += kRouteBareThreads / kVecH)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(a.x + (size_t)(c0 + j) * H) + v,
+                                       (lds_ptr_t)(xs + j * kVecH + (v & ~(kWave - 1))), 16, 0, 0);
+  };
+  stage(0);   // in flight together with the router rows
+  for (int c0 = 0; c0 < a.T; c0 += kRouteBareXChunk) {
+    const int n = min(kRouteBareXChunk, a.T - c0);
+    wait_vmem_all();
+    __syncthreads();
+    if (wave < n) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int j = wave + g * kRouteBareWaves;
+        if (j < n) {
+#pragma unroll
+          for (int i = 0; i < kVecPerLaneH; ++i) {
+            const u32x4 xv = xs[j * kVecH + lane + i * kWave];
+#pragma unroll
+            for (int r = 0; r < kRouterRows; ++r) acc[r * 2 + g] = dot8_bf16(wv[r][i], xv, acc[r * 2 + g]);
+          }
+        }
+      }
+      const float z = wave_sum8_transposed(acc);
+      const int j = wave + my_g * kRouteBareWaves;
+      if (lane < 8 && j < n && my_e < a.E) {
+        store_coherent(a.ws.logits + (size_t)(c0 + j) * a.E + my_e, z + bias);
+      }
+    }
+    if (c0 + kRouteBareXChunk < a.T) {
+      lds_barrier();   // every wave is done with this chunk's x
+      stage(c0 + kRouteBareXChunk);
+    }
+  }
+  route_tail<kRouteBareWaves>(a, L, &s_flag);
 }
 
 // Routing of a small batch inside one block, from the logits of the router
@@ -1103,6 +1217,8 @@ static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Lau
   } else {
     if (a.norm_w)
       launch(route_kernel<true, false>, g_route, dim3(kThreads), stream, a);
+    else if (a.T > kRouteBareMinT)
+      launch(route_bare_kernel, g_route, dim3(kRouteBareThreads), stream, a);
     else
       launch(route_kernel<false, false>, g_route, dim3(kThreads), stream, a);
     launch(gateup_kernel<kFp4, false>, g_gateup, dim3(kThreads), stream, a);
