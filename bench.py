@@ -17,7 +17,8 @@ The roofline's
 "traffic" (HBM bytes per launch of the dominant kernel) is read from the
 counter table in profiles/hbm_traffic.md when its row was measured on the
 kernel sources as they are now (SHA-256 of the path's .hip file and the two
-shared headers); otherwise it is null.
+shared headers); otherwise it is null.  "traffic_GBps" is that byte count over
+the launch's measured average duration (the counter-measured HBM rate).
 
 With --block, one step is the pre-norm block around the layer instead
 (flint_moe_block_forward: RMSNorm of the residual stream r, the layer, and
@@ -88,6 +89,14 @@ def measured_traffic(workload: str, kernel: str, sha: str):
     except OSError:
         pass
     return None
+
+
+def with_traffic_rate(roof: dict) -> dict:
+    """Adds the counter-measured HBM rate of the dominant launch: its
+    FETCH_SIZE + WRITE_SIZE bytes per launch over its average launch time."""
+    t = roof.get("traffic")
+    roof["traffic_GBps"] = round(t / (roof["avg_launch_us"] * 1e-6) / 1e9, 1) if t else None
+    return roof
 
 
 def log(msg):
@@ -340,7 +349,7 @@ def run_mlp(args, rank):
         "kernel_timing": "start/stop timestamps of each kernel's execution (hipExtLaunchKernelGGL "
                          "events), averaged over K eager steps",
         "eager_wall_us_per_step": round(eager_us, 2),
-        "roofline": roof,
+        "roofline": with_traffic_rate(roof),
     })
     if rank == 0 and args.cpu_baseline_seconds > 0:
         log("timing the oracle on the host")
@@ -516,7 +525,7 @@ def main():
         "kernel_timing": "start/stop timestamps of each kernel's execution (hipExtLaunchKernelGGL "
                          "events), averaged over K eager steps",
         "eager_wall_us_per_step": round(eager_us, 2),
-        "roofline": roof,
+        "roofline": with_traffic_rate(roof),
     })
     if rank == 0 and args.cpu_baseline_seconds > 0:
         log("timing the oracle on the host")
