@@ -71,7 +71,7 @@ def test_prefill_flags(flint_bf16):
     assert g.ok, str(g)
 
 
-@pytest.mark.parametrize("T", [8, 300])
+@pytest.mark.parametrize("T", [1, 8, 32, 300])   # routing in gate/up; 4-wave; 16-wave router; prefill
 def test_graph_replays_match_eager(flint_bf16, T):
     sg = flint_bf16["sg"]
     say(f"graph replays T={T}")
