@@ -524,6 +524,14 @@ __device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, in
   }
 }
 
+// Threads of a route_kernel block: 4 waves (one router row each); the bare
+// layer's ticketed routing adds 4 waves that only rank tokens in the
+// routing block (one token per wave at T = 8).  The pre-norm block's row
+// staging maps one thread to each 16-byte vector of a row.
+__host__ __device__ constexpr int route_threads(bool norm, bool fused) {
+  return norm || fused ? kThreads : 2 * kThreads;
+}
+
 // Router of the pre-norm block and of small bare-layer batches: wave w of
 // block b computes the logits of expert 4b + w for all T tokens; the
 // tokens' rows stream through LDS kRouteXChunk at a time (for the pre-norm
@@ -532,24 +540,29 @@ __device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, in
 // fused_routing_applies) the launch ends with the logits and the gate/up
 // launch routes instead.
 template <bool kNorm, bool kFused>
-__global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
+__global__ __launch_bounds__(route_threads(kNorm, kFused)) void route_kernel(LayerArgs a) {
   constexpr int XC = kRouteXChunk;
+  constexpr int kNT = route_threads(kNorm, kFused);
   __shared__ u32x4 xs[XC * kVecH];
   __shared__ RouteLds L;
   __shared__ int s_flag;
   __shared__ float s_ss[kRouteWaves * kRouteXChunk];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
+  // Waves kRouterRows and up (bare layer, ticketed routing) only rank tokens.
+  const bool gemv = wave < kRouterRows;
   const int e = blockIdx.x * kRouterRows + wave;
   const int er = min(e, a.E - 1);
   if (!kFused) {
-    for (int i = threadIdx.x; i < kMaxExperts; i += kThreads) L.cnt[i] = 0;
-    for (int i = threadIdx.x; i < kMaxExperts * kMaskWords; i += kThreads) L.occ[i] = 0;
+    for (int i = threadIdx.x; i < kMaxExperts; i += kNT) L.cnt[i] = 0;
+    for (int i = threadIdx.x; i < kMaxExperts * kMaskWords; i += kNT) L.occ[i] = 0;
   }
   u32x4 wv[kVecPerLaneH];
   const u32x4* row = reinterpret_cast<const u32x4*>(a.router_w + (size_t)er * H);
+  if (gemv) {
 #pragma unroll
-  for (int i = 0; i < kVecPerLaneH; ++i) wv[i] = load_stream(row + lane + i * kWave);
+    for (int i = 0; i < kVecPerLaneH; ++i) wv[i] = load_stream(row + lane + i * kWave);
+  }
   const float bias = a.router_b ? a.router_b[er] : 0.f;
   u32x4 gv{};
   if (kNorm) gv = reinterpret_cast<const u32x4*>(a.norm_w)[threadIdx.x];
@@ -557,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
     const int n = min(XC, a.T - c0);
     if (kNorm) {
       stage_normed_rows(a, c0, n, xs, gv, s_ss);
-    } else {
+    } else if (threadIdx.x < kVecH) {
       for (int j = 0; j < n; ++j) stage_x_row(xs + j * kVecH, a.x + (size_t)(c0 + j) * H);
     }
   };
@@ -570,14 +583,14 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
 #pragma unroll
     for (int j = 0; j < XC; ++j) {
       acc[j] = 0.f;
-      if (j < n) {
+      if (gemv && j < n) {
 #pragma unroll
         for (int i = 0; i < kVecPerLaneH; ++i) acc[j] = dot8_bf16(wv[i], xs[j * kVecH + lane + i * kWave], acc[j]);
       }
     }
 #pragma unroll
     for (int j = 0; j < XC; ++j) {
-      if (j < n) {
+      if (gemv && j < n) {
         const float z = wave_sum_lane63(acc[j]);
         if (lane == kWave - 1 && e < a.E) {
           float* zp = a.ws.logits + (size_t)(c0 + j) * a.E + e;
@@ -592,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
     }
   }
   if (kFused) return;
-  route_tail<kRouteWaves>(a, L, &s_flag);
+  route_tail<kNT / kWave>(a, L, &s_flag);
 }
 
 // Router of larger bare-layer batches (T > kRouteBareMinT): 16 waves per
@@ -1220,7 +1233,7 @@ static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Lau
     else if (a.T > kRouteBareMinT)
       launch(route_bare_kernel, g_route, dim3(kRouteBareThreads), stream, a);
     else
-      launch(route_kernel<false, false>, g_route, dim3(kThreads), stream, a);
+      launch(route_kernel<false, false>, g_route, dim3(route_threads(false, false)), stream, a);
     launch(gateup_kernel<kFp4, false>, g_gateup, dim3(kThreads), stream, a);
   }
   launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
