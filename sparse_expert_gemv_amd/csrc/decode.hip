@@ -3,10 +3,11 @@
 //
 // Three launches on the caller's stream:
 //   1. route   : router GEMV over 64 blocks of four expert rows each (4
-//                waves, one row each; for the pre-norm block every block
-//                normalises the rows it stages, block 0 storing them; bare
-//                layer with T > 8: 16 waves, each all four rows for its
-//                tokens).
+//                waves, one row each, plus 4 waves that only rank tokens
+//                for the bare layer's ticketed routing at T <= 8; for the
+//                pre-norm block every block normalises the rows it stages,
+//                block 0 storing them; bare layer with T > 8: 16 waves,
+//                each all four rows for its tokens).
 //                The last block to finish picks every token's top-k by
 //                sigmoid score (a wave per token), computes the routing
 //                weights and buckets every (token, rank) slot by expert into
