@@ -383,8 +383,8 @@ def mlp_cpu_baseline(S, x_bits, block, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(expert parallelism is a design note, not code). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(expert parallelism across GPUs is not implemented). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     rank = int(os.environ.get("RANK", "0"))
     if args.mlp:

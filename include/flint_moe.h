@@ -60,7 +60,7 @@ typedef struct flint_moe_ctx flint_moe_ctx; /* opaque, host memory */
 typedef enum flint_status {
   FLINT_OK = 0,
   FLINT_ERR_INVALID_ARG = 1, /* NULL / misaligned / out-of-range argument */
-  FLINT_ERR_UNSUPPORTED = 2, /* shape or format this build has no kernels for */
+  FLINT_ERR_UNSUPPORTED = 2, /* shape or format the library has no kernels for */
   FLINT_ERR_WORKSPACE = 3,   /* workspace smaller than flint_moe_workspace_bytes() */
   FLINT_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } flint_status;
