@@ -309,6 +309,94 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const uint16_t* __res
 
 constexpr int kZRow = kMaxExperts + 1;   // logits row stride in LDS (floats)
 
+// Top-k of G tile rows i0, i0 + di, ... (tokens t0 + i) from the logits
+// parked in LDS, one wave, the G selections interleaved round by round.
+// Ranks on the logit (the sigmoid is strictly increasing), ties to the lower
+// expert index: lane l holds the order-preserving keys of experts 4l ..
+// 4l + 3 sorted by (key descending, expert ascending); round j takes the
+// wave maximum of the lanes' heads and the lowest lane holding it pops its
+// head (lower lanes hold lower experts).  Lane j keeps the j-th pick; the
+// routing weights are s_j / sum s (if renormalised) x routed_scale, and each
+// pick is counted in hist.  Rows past T are ranked on zero keys and dropped.
+template <int G>
+__device__ void rank_rows(const LayerArgs& a, const float* zs, int t0, int i0, int di, int* hist) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k, T = a.T;
+  uint32_t key[G][4];
+  int ex[G][4];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int i = i0 + g * di;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      key[g][q] = (e < E && t0 + i < T) ? ord_f32(zs[i * kZRow + e]) : 0u;
+      ex[g][q] = e;
+    }
+    auto cx = [&](int u, int v) __attribute__((always_inline)) {
+      const bool sw = key[g][v] > key[g][u] || (key[g][v] == key[g][u] && ex[g][v] < ex[g][u]);
+      const uint32_t ku = key[g][u], kv = key[g][v];
+      const int eu = ex[g][u], ev = ex[g][v];
+      key[g][u] = sw ? kv : ku;
+      key[g][v] = sw ? ku : kv;
+      ex[g][u] = sw ? ev : eu;
+      ex[g][v] = sw ? eu : ev;
+    };
+    cx(0, 1);
+    cx(2, 3);
+    cx(0, 2);
+    cx(1, 3);
+    cx(1, 2);
+  }
+  int my_e[G];
+  uint32_t my_key[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    my_e[g] = 0;
+    my_key[g] = 0;
+  }
+#pragma unroll 1
+  for (int j = 0; j < k; ++j) {
+    uint32_t m[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = key[g][0];
+    wave_max_u32_lane63_multi<G>(m);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t M = (uint32_t)__builtin_amdgcn_readlane((int)m[g], 63);
+      const int win = (int)__builtin_ctzll(__ballot(key[g][0] == M));
+      const int best = __builtin_amdgcn_readlane(ex[g][0], win);
+      if (lane == win) {
+        key[g][0] = key[g][1];
+        key[g][1] = key[g][2];
+        key[g][2] = key[g][3];
+        key[g][3] = 0u;
+        ex[g][0] = ex[g][1];
+        ex[g][1] = ex[g][2];
+        ex[g][2] = ex[g][3];
+      }
+      if (lane == j) {
+        my_e[g] = best;
+        my_key[g] = M;
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = t0 + i0 + g * di;
+    const float sc = lane < k ? sigmoid(unord_f32(my_key[g])) : 0.f;
+    const float sum = __shfl(wave_sum_lane63(sc), 63);
+    if (t < T && lane < k) {
+      const float w = (a.renormalize ? sc / sum : sc) * a.routed_scale;
+      a.ws.ids[t * k + lane] = my_e[g];
+      a.ws.wts[t * k + lane] = w;
+      if (a.ids_out) a.ids_out[t * k + lane] = my_e[g];
+      if (a.wts_out) a.wts_out[t * k + lane] = w;
+      atomicAdd(&hist[my_e[g]], 1);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[cmax(RouterGemm::kLds, kMT * kZRow * 4)];
   __shared__ int hist[kMaxExperts];
@@ -347,61 +435,11 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
   if (tid < E)
     for (int i = 0; i < kMT && t0 + i < T; ++i) a.ws.logits[(size_t)(t0 + i) * E + tid] = zs[i * kZRow + tid];
 
-  // Top-k: four threads per token, each keeping the k largest keys of its 64
-  // experts in a descending list (insertion by compare-exchange), then two
-  // exchange rounds within the quad merge the four lists.  Key = (order-
-  // preserving bits of the logit) << 32 | ~expert, so equal logits rank the
-  // lower expert index first, and sigmoid's monotonicity makes the ranking by
-  // logit the ranking by score.
-  static_assert(4 * kMT <= kThreads, "four threads per token");
-  if (tid < 4 * kMT) {
-    const int i = tid >> 2, quarter = tid & 3;
-    uint64_t top[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) top[j] = 0;
-    auto insert = [&](uint64_t c) {
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        const uint64_t hi = max_u64(top[j], c);
-        c = top[j] < c ? top[j] : c;
-        top[j] = hi;
-      }
-    };
-    for (int q = 0; q < 64; ++q) {
-      const int e = quarter * 64 + q;
-      if (e < E) insert(((uint64_t)ord_f32(zs[i * kZRow + e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e));
-    }
-    uint64_t other[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) other[j] = dpp64<0xB1, 0xF>(top[j]);   // lane ^ 1
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) insert(other[j]);
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) other[j] = dpp64<0x4E, 0xF>(top[j]);   // lane ^ 2
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) insert(other[j]);
-    const int t = t0 + i;
-    if (quarter == 0 && t < T) {
-      float sc[kMaxTopK], sum = 0.f;
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        sc[j] = sigmoid(unord_f32((uint32_t)(top[j] >> 32)));
-        if (j < k) sum += sc[j];
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k) {
-          const int id = (int)(0xFFFFFFFFu - (uint32_t)top[j]);
-          const float w = (a.renormalize ? sc[j] / sum : sc[j]) * a.routed_scale;
-          a.ws.ids[t * k + j] = id;
-          a.ws.wts[t * k + j] = w;
-          if (a.ids_out) a.ids_out[t * k + j] = id;
-          if (a.wts_out) a.wts_out[t * k + j] = w;
-          atomicAdd(&hist[id], 1);
-        }
-      }
-    }
-  }
+  // Top-k: wave w ranks tile rows w, w + 4, ..., four at a time (rank_rows).
+  static_assert(kMT % (4 * kThreads / 64) == 0, "whole groups of four rows per wave");
+#pragma unroll 1
+  for (int i0 = wave; i0 < kMT; i0 += 4 * (kThreads / 64))
+    rank_rows<4>(a, zs, t0, i0, kThreads / 64, hist);
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) a.ws.pre.counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
