@@ -774,6 +774,42 @@ void gateup_kernel(LayerArgs a) {
   const int b = blockIdx.x - kUnitsPerExpert;
   const int ai = b / kUnitsPerExpert;
   const int unit = b - ai * kUnitsPerExpert;
+  if (kFused && a.T == 1) {
+    // One token: every wave ranks it (the same picks in every wave), so no
+    // block barrier precedes the weight loads.  The k picks are distinct;
+    // the item's expert is the ai-th smallest, its one slot the pick's rank
+    // j (slot j of token 0).  Wave 0 of the first routed block stores the
+    // ids, the weights and the routing table.
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int k = a.k, E = a.E;
+    const bool writer = b == 0 && wave == 0;
+    int* ids = FL.ids + wave * kMaxTopK;   // this wave's picks (written and read by this wave)
+    route_tokens<1, false>(a, 0, 1, 1, ids, writer);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the picks are in LDS
+    const int ej = lane < k ? ids[lane] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int i = 0; i < k; ++i) rank += ids[i] < ej;
+    const uint64_t hit = __ballot(lane < k && rank == ai);
+    if (writer) {
+      int32_t* route = a.ws.route;
+      if (lane < k) {
+        route[1 + rank] = ej;
+        route[1 + E + rank] = rank;
+        route[2 + 2 * E + rank] = lane;
+      }
+      if (lane == 0) {
+        route[0] = k;
+        route[1 + E + k] = k;
+      }
+    }
+    const int slot = (int)__builtin_ctzll(hit);   // ai < k: exactly one lane
+    const int e = __builtin_amdgcn_readlane(ej, slot);
+    GateUpRows<kFp4> wv;
+    wv.load(a.routed, e, unit * kPairsPerItem);
+    gateup_compute<kFp4, kXChunk>(wv, unit * kPairsPerItem, 1, TokenList{nullptr, a.k, slot}, a.x, a.ws.h, xs);
+    return;
+  }
   if (kFused) {
     fused_route(a, ai, b == 0, FL);
     if (ai >= FL.meta[0]) return;
