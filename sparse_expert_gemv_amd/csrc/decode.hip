@@ -1027,102 +1027,127 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   const int r0 = blockIdx.x * kDownRowsPerBlock;
   const int T = a.T, k = a.k, E = a.E;
   const int32_t* route = a.ws.route;
-  // The routing table in one round trip (whole arrays, no dependence on |U|;
-  // one element of each per thread), requested before the shared expert's
-  // entries so that waiting for it leaves those in flight.
-  const int q = threadIdx.x;
-  int v_act = 0, v_off = 0, v_slot = 0;
-  float v_wt = 0.f;
-  if (q < E) v_act = route[1 + q];
-  if (q <= E) v_off = route[1 + E + q];
-  if (q < T * k) {
-    v_slot = route[2 + 2 * E + q];
-    v_wt = a.ws.wts[q];   // for the combine, fetched with the table
-  }
-  const int n = route[0];
-
-  // Three entries per wave in flight: the one being reduced and the next
-  // two (rows and h), rotated through pa, pb, pc.  The shared expert's
-  // entries are the first n_sh of the work list.
-  const int n_sh = (T + kDnSlots - 1) / kDnSlots;
-  DownRows<kFp4> pa, pb, pc;
-  DownItem da{}, db{}, dc{};
-  int w = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform: scalar branches below
-  // Each path stores the table on its own, so that the wait for the table
-  // leaves exactly that path's entry loads in flight (at a join, the wait
-  // would have to assume none were issued and wait for all); the distinct
-  // asm markers keep the copies from being merged.
-  auto store_table = [&]() __attribute__((always_inline)) {
-    if (q < E) s_active[q] = (int16_t)v_act;
-    if (q <= E) s_off[q] = (int16_t)v_off;
-    if (q < T * k) {
-      s_slots[q] = (int16_t)v_slot;
-      s_wts[q] = v_wt;
+  if (T == 1 && k < kDownWaves) {
+    // One token: k + 1 entries of one slot each and no work list.  Wave 0
+    // takes the shared expert (no table needed), wave w <= k the (w - 1)-th
+    // expert of U and its slot, read straight from the routing table.
+    const int w0 = __builtin_amdgcn_readfirstlane(wave);
+    if ((int)threadIdx.x < k) s_wts[threadIdx.x] = a.ws.wts[threadIdx.x];
+    if (w0 <= k) {
+      DownItem d;
+      if (w0 == 0) {
+        d = shared_entry(a, 0);
+      } else {
+        const int ai = w0 - 1;
+        d.shared = false;
+        d.e = route[1 + ai];
+        d.off = ai;
+        d.j0 = 0;
+        d.nj = 1;
+        if (lane == 0) s_slots[ai] = (int16_t)route[2 + 2 * E + ai];   // read back by this wave only
+      }
+      DownRows<kFp4> p;
+      prefetch_entry(p, a, d, r0, s_slots);
+      down_entry_rows(a, d, p, s_slots, part);
     }
-  };
-  if (w + kDownWaves < n_sh) {
-    da = shared_entry(a, w);
-    prefetch_entry(pa, a, da, r0, s_slots);
-    db = shared_entry(a, w + kDownWaves);
-    prefetch_entry(pb, a, db, r0, s_slots);
-    store_table();
-    asm volatile("; down: two shared entries in flight" ::: "memory");
-  } else if (w < n_sh) {
-    da = shared_entry(a, w);
-    prefetch_entry(pa, a, da, r0, s_slots);
-    store_table();
-    asm volatile("; down: one shared entry in flight" ::: "memory");
   } else {
-    store_table();
-  }
-  lds_barrier();
-
-  // Work list: item 0 (the shared expert, T slots) and items 1..n (active
-  // expert i - 1) contribute ceil(cnt / kDnSlots) entries each, laid out by
-  // an exclusive scan.
-  const int it = threadIdx.x;
-  const int cnt = it == 0 ? T : (it <= n ? s_off[it] - s_off[it - 1] : 0);
-  const int nsub = (cnt + kDnSlots - 1) / kDnSlots;
-  const int incl = wave_incl_scan(nsub);
-  if (lane == kWave - 1) s_scan[wave] = incl;
-  lds_barrier();
-  int base = incl - nsub, total = 0;
-  for (int v = 0; v < kDownWaves; ++v) {
-    if (v < wave) base += s_scan[v];
-    total += s_scan[v];
-  }
-  for (int j = 0; j < nsub; ++j) s_work[base + j] = (int16_t)((it << kDnSubBits) | j);
-  lds_barrier();
-
-  if (w >= n_sh && w < total) {
-    da = down_entry(a, s_work[w], s_active, s_off);
-    prefetch_entry(pa, a, da, r0, s_slots);
-  }
-  if (w + kDownWaves >= n_sh && w + kDownWaves < total) {
-    db = down_entry(a, s_work[w + kDownWaves], s_active, s_off);
-    prefetch_entry(pb, a, db, r0, s_slots);
-  }
-  while (w < total) {
-    if (w + 2 * kDownWaves < total) {
-      dc = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
-      prefetch_entry(pc, a, dc, r0, s_slots);
+    // The routing table in one round trip (whole arrays, no dependence on |U|;
+    // one element of each per thread), requested before the shared expert's
+    // entries so that waiting for it leaves those in flight.
+    const int q = threadIdx.x;
+    int v_act = 0, v_off = 0, v_slot = 0;
+    float v_wt = 0.f;
+    if (q < E) v_act = route[1 + q];
+    if (q <= E) v_off = route[1 + E + q];
+    if (q < T * k) {
+      v_slot = route[2 + 2 * E + q];
+      v_wt = a.ws.wts[q];   // for the combine, fetched with the table
     }
-    down_entry_rows(a, da, pa, s_slots, part);
-    w += kDownWaves;
-    if (w >= total) break;
-    if (w + 2 * kDownWaves < total) {
-      da = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
+    const int n = route[0];
+
+    // Three entries per wave in flight: the one being reduced and the next
+    // two (rows and h), rotated through pa, pb, pc.  The shared expert's
+    // entries are the first n_sh of the work list.
+    const int n_sh = (T + kDnSlots - 1) / kDnSlots;
+    DownRows<kFp4> pa, pb, pc;
+    DownItem da{}, db{}, dc{};
+    int w = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform: scalar branches below
+    // Each path stores the table on its own, so that the wait for the table
+    // leaves exactly that path's entry loads in flight (at a join, the wait
+    // would have to assume none were issued and wait for all); the distinct
+    // asm markers keep the copies from being merged.
+    auto store_table = [&]() __attribute__((always_inline)) {
+      if (q < E) s_active[q] = (int16_t)v_act;
+      if (q <= E) s_off[q] = (int16_t)v_off;
+      if (q < T * k) {
+        s_slots[q] = (int16_t)v_slot;
+        s_wts[q] = v_wt;
+      }
+    };
+    if (w + kDownWaves < n_sh) {
+      da = shared_entry(a, w);
+      prefetch_entry(pa, a, da, r0, s_slots);
+      db = shared_entry(a, w + kDownWaves);
+      prefetch_entry(pb, a, db, r0, s_slots);
+      store_table();
+      asm volatile("; down: two shared entries in flight" ::: "memory");
+    } else if (w < n_sh) {
+      da = shared_entry(a, w);
+      prefetch_entry(pa, a, da, r0, s_slots);
+      store_table();
+      asm volatile("; down: one shared entry in flight" ::: "memory");
+    } else {
+      store_table();
+    }
+    lds_barrier();
+
+    // Work list: item 0 (the shared expert, T slots) and items 1..n (active
+    // expert i - 1) contribute ceil(cnt / kDnSlots) entries each, laid out by
+    // an exclusive scan.
+    const int it = threadIdx.x;
+    const int cnt = it == 0 ? T : (it <= n ? s_off[it] - s_off[it - 1] : 0);
+    const int nsub = (cnt + kDnSlots - 1) / kDnSlots;
+    const int incl = wave_incl_scan(nsub);
+    if (lane == kWave - 1) s_scan[wave] = incl;
+    lds_barrier();
+    int base = incl - nsub, total = 0;
+    for (int v = 0; v < kDownWaves; ++v) {
+      if (v < wave) base += s_scan[v];
+      total += s_scan[v];
+    }
+    for (int j = 0; j < nsub; ++j) s_work[base + j] = (int16_t)((it << kDnSubBits) | j);
+    lds_barrier();
+
+    if (w >= n_sh && w < total) {
+      da = down_entry(a, s_work[w], s_active, s_off);
       prefetch_entry(pa, a, da, r0, s_slots);
     }
-    down_entry_rows(a, db, pb, s_slots, part);
-    w += kDownWaves;
-    if (w >= total) break;
-    if (w + 2 * kDownWaves < total) {
-      db = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
+    if (w + kDownWaves >= n_sh && w + kDownWaves < total) {
+      db = down_entry(a, s_work[w + kDownWaves], s_active, s_off);
       prefetch_entry(pb, a, db, r0, s_slots);
     }
-    down_entry_rows(a, dc, pc, s_slots, part);
-    w += kDownWaves;
+    while (w < total) {
+      if (w + 2 * kDownWaves < total) {
+        dc = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
+        prefetch_entry(pc, a, dc, r0, s_slots);
+      }
+      down_entry_rows(a, da, pa, s_slots, part);
+      w += kDownWaves;
+      if (w >= total) break;
+      if (w + 2 * kDownWaves < total) {
+        da = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
+        prefetch_entry(pa, a, da, r0, s_slots);
+      }
+      down_entry_rows(a, db, pb, s_slots, part);
+      w += kDownWaves;
+      if (w >= total) break;
+      if (w + 2 * kDownWaves < total) {
+        db = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
+        prefetch_entry(pb, a, db, r0, s_slots);
+      }
+      down_entry_rows(a, dc, pc, s_slots, part);
+      w += kDownWaves;
+    }
   }
   __syncthreads();
   for (int q = threadIdx.x; q < T * kDownRowsPerBlock; q += kDownThreads) {
