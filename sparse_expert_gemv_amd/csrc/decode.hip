@@ -565,6 +565,31 @@ __global__ __launch_bounds__(route_threads(kNorm, kFused)) void route_kernel(Lay
     for (int i = 0; i < kVecPerLaneH; ++i) wv[i] = load_stream(row + lane + i * kWave);
   }
   const float bias = a.router_b ? a.router_b[er] : 0.f;
+  if constexpr (!kNorm && kFused) {
+    // Small batch (T <= kRouteWaves): each wave reads the T x rows straight
+    // from memory with its router row; no LDS staging, no block barrier.
+    static_assert(kRouteWaves <= kRouteXChunk, "one chunk");
+    u32x4 xv[kRouteWaves][kVecPerLaneH];
+#pragma unroll
+    for (int j = 0; j < kRouteWaves; ++j) {
+      if (j < a.T) {
+#pragma unroll
+        for (int i = 0; i < kVecPerLaneH; ++i)
+          xv[j][i] = reinterpret_cast<const u32x4*>(a.x + (size_t)j * H)[lane + i * kWave];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRouteWaves; ++j) {
+      if (j < a.T) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < kVecPerLaneH; ++i) acc = dot8_bf16(wv[i], xv[j][i], acc);
+        const float z = wave_sum_lane63(acc);
+        if (lane == kWave - 1 && e < a.E) a.ws.logits[(size_t)j * a.E + e] = z + bias;
+      }
+    }
+    return;
+  }
   u32x4 gv{};
   if (kNorm) gv = reinterpret_cast<const u32x4*>(a.norm_w)[threadIdx.x];
   auto stage = [&](int c0) __attribute__((always_inline)) {
