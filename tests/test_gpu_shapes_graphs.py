@@ -50,7 +50,7 @@ def test_other_expert_counts(E, k):
                          sg.DeviceBank(t["sh_w13"], t["sh_w2"]))
     L = OracleLayer(2048, E, k, 512, syn.router_w(), None, syn.expert)
     moe = sg.FlintMoE(n_experts=E, top_k=k, max_tokens=100)
-    for T in (1, 5, 13, 64, 100):   # routing in gate/up; 8-wave router; 16-wave router; prefill
+    for T in (1, 4, 5, 13, 64, 100):   # routing in gate/up (T*k <= 16); 8-wave router; 16-wave router; prefill
         say(f"  E={E} k={k} T={T}")
         xb = make_x(T, seed=3, x_seed=T)
         out, ids = forward(sg, moe, W, xb, k)
