@@ -18,8 +18,9 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from oracle import bf16_to_f64  # noqa: E402
-from oracle.block import block_forward, block_token, f64_to_bf16_bits, rmsnorm  # noqa: E402
-from oracle.grading import TOL_BF16, grade_block  # noqa: E402
+from oracle.block import block_forward  # noqa: E402
+from oracle.grading import TOL_BF16, grade_block, grade_block_arrays  # noqa: E402
+from oracle.grouped import block_forward_grouped  # noqa: E402
 from synth import make_residual  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -105,24 +106,24 @@ def test_block_prefill_matches_oracle(flint_bf16, T, x_seed):
     check_all(r, res)
 
 
-def test_block_prefill_t8192_sampled(flint_bf16):
-    """The prefill workload's size: n of every token; out, ids and weights of
-    a spread sample of tokens, each computed by the oracle one by one."""
+def test_block_prefill_t8192_full(flint_bf16):
+    """The prefill workload's size: n, ids, weights and out of every token,
+    against the expert-grouped oracle."""
     T = 8192
-    say("block prefill T=8192: n of every token, output of a sample")
+    say("block prefill T=8192: every token")
     dev = flint_bf16
     gamma = dev["syn"].norm_weight()
     rb = make_residual(T, seed=0, x_seed=7)
     r = run_block(dev, rb, gamma, max_tokens=T)
-    n64 = rmsnorm(bf16_to_f64(rb).reshape(T, 2048), bf16_to_f64(gamma), EPS)
-    nbits = f64_to_bf16_bits(n64)
-    flips = sum(check_normed(r["normed"][t], nbits[t], n64[t]) for t in range(T))
-    assert flips <= T * 2048 // 1000, f"{flips} midpoint flips"
-    sample = sorted(set(np.linspace(0, T - 1, 24).astype(int).tolist()))
-    res = block_forward(dev["L"], rb, gamma, eps=EPS, tokens=sample)
-    g = grade_block(r["out"], r["ids"], res, tokens=sample, tol=TOL_BF16)
+    G = block_forward_grouped(dev["L"], rb, gamma, eps=EPS)
+    flips = [check_normed(r["normed"][t], G.normed_bits[t], G.normed_f64[t]) for t in range(T)]
+    assert sum(flips) <= T * 2048 // 1000, f"{sum(flips)} midpoint flips"
+    g = grade_block_arrays(r["out"], r["ids"], G.out, G.layer_out, G.ids, G.gaps, tol=TOL_BF16)
     print(g)
     assert g.ok, str(g)
+    keep = (G.gaps >= 1e-5) & (np.array(flips) == 0)
+    assert np.array_equal(r["ids"][keep], G.ids[keep])
+    np.testing.assert_allclose(r["w"][keep], G.weights[keep], rtol=2e-6, atol=1e-7)
 
 
 def test_block_zero_gamma_returns_r_exactly(flint_bf16):

@@ -14,6 +14,7 @@ torch = pytest.importorskip("torch")
 
 from oracle import bf16_to_f64  # noqa: E402
 from oracle.dense import DenseMLP, mlp_block_forward, mlp_forward  # noqa: E402
+from oracle.grouped import mlp_forward_batched  # noqa: E402
 from synth import SyntheticDenseMLP, make_residual, make_x  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -102,15 +103,30 @@ def test_dense_prefill_matches_oracle(T, block):
     check_out(out, refs, block)
 
 
-def test_dense_prefill_t8192_sampled():
+def check_out_arrays(out_bits, ref, mlp, block):
+    got = bf16_to_f64(out_bits).reshape(out_bits.shape)
+    rms = float(np.sqrt(np.mean(mlp ** 2)))
+    excess = np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) if block else 0.0)
+    ratio = float(max(0.0, np.max(excess))) / rms
+    print(f"max excess / RMS(MLP out) = {ratio:.5f} (tol {TOL}) over {got.shape[0]} tokens")
+    assert ratio <= TOL
+
+
+@pytest.mark.parametrize("block", [False, True])
+def test_dense_prefill_t8192_full(block):
+    """Every token of a prefill-sized batch against the batched oracle."""
     d = dense(FLINT_INTER_D)
     T = 8192
-    say("dense prefill T=8192, sampled tokens")
-    xb = make_x(T, seed=0, x_seed=6)
-    out, _, _ = run(d, xb, max_tokens=T)
-    sample = sorted(set(np.linspace(0, T - 1, 12).astype(int).tolist()))
-    refs = mlp_forward(d["M"], xb, tokens=sample)
-    check_out(out[sample], refs, block=False)
+    say(f"dense prefill T=8192 block={block}, every token")
+    xb = (make_residual if block else make_x)(T, seed=0, x_seed=6)
+    out, _, _ = run(d, xb, block=block, max_tokens=T)
+    S = d["S"]
+    if block:
+        ref, mlp = mlp_forward_batched(S.w13(), S.w2(), xb, 2048, FLINT_INTER_D,
+                                       gamma_bits=S.norm_weight(), eps=EPS)
+    else:
+        ref = mlp = mlp_forward_batched(S.w13(), S.w2(), xb, 2048, FLINT_INTER_D)
+    check_out_arrays(out, ref, mlp, block)
 
 
 @pytest.mark.parametrize("inter,T", [(512, 5), (1536, 3), (1536, 130)])

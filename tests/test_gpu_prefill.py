@@ -1,9 +1,10 @@
 """GPU parity of the prefill-sized (T > 64) MFMA path against the fp64 oracle.
 
-Small T: every token against the oracle.  T = 8192 (the prefill workload):
-the router output (ids, weights) and the routing table for every token, and
-the layer output on a spread sample of tokens computed one by one by the
-oracle.
+Small T: every token against the per-token oracle.  T = 8192 (the prefill
+workload, "RecursiveSI/flint — vLLM serving recipe", section "Benchmarking",
+prefill 8K): the router output (ids, weights), the routing table and the
+layer output of every token, against the expert-grouped oracle
+(``oracle.grouped``, pinned token by token against the per-token oracle).
 """
 
 import numpy as np
@@ -11,8 +12,9 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from oracle import bucket, moe_forward, route_all  # noqa: E402
-from oracle.grading import TOL_BF16, grade  # noqa: E402
+from oracle import bucket, moe_forward  # noqa: E402
+from oracle.grading import TOL_BF16, grade, grade_arrays  # noqa: E402
+from oracle.grouped import moe_forward_grouped  # noqa: E402
 from synth import make_x  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -51,16 +53,16 @@ def test_prefill_matches_oracle(flint_bf16, T, bias, x_seed):
             np.testing.assert_allclose(r["w"][t], rr.weights, rtol=2e-6, atol=1e-7)
 
 
-def test_prefill_t8192_sampled(flint_bf16):
+def test_prefill_t8192_full(flint_bf16):
     T = 8192
-    say("prefill T=8192: routing of every token, output of a sample")
+    say("prefill T=8192: routing, table and output of every token")
     xb = make_x(T, seed=0, x_seed=0)
     r = run(flint_bf16, xb)
-    ids_ref, w_ref, gaps, _ = route_all(flint_bf16["L"], xb)
-    keep = gaps >= 1e-5
+    G = moe_forward_grouped(flint_bf16["L"], xb)
+    keep = G.gaps >= 1e-5
     print(f"excluded tokens (gap < 1e-5): {int((~keep).sum())}")
-    assert np.array_equal(r["ids"][keep], ids_ref[keep])
-    np.testing.assert_allclose(r["w"][keep], w_ref[keep], rtol=2e-6, atol=1e-7)
+    assert np.array_equal(r["ids"][keep], G.ids[keep])
+    np.testing.assert_allclose(r["w"][keep], G.weights[keep], rtol=2e-6, atol=1e-7)
     # Routing table: the bucketing of the device's own ids, bit-exact.
     b = bucket(r["ids"], 256)
     lay = r["moe"].workspace_layout(T)
@@ -72,37 +74,26 @@ def test_prefill_t8192_sampled(flint_bf16):
     np.testing.assert_array_equal(route[1 + 256:1 + 256 + nU + 1],
                                   b["offsets"][b["active"].tolist() + [256]])
     np.testing.assert_array_equal(route[2 + 512:], b["slots"])
-    # Output of 48 tokens spread over the batch (first, last, tile edges).
-    sample = sorted(set([0, 1, 63, 64, 65, 127, 4095, 4096, 8127, 8128, 8190, 8191] +
-                        [int(v) for v in np.random.default_rng(0).choice(T, 36, replace=False)]))
-    res = moe_forward(flint_bf16["L"], xb, tokens=sample)
-    g = grade(r["out"], r["ids"], res, tokens=sample, tol=TOL_BF16)
+    # The output of every token.
+    g = grade_arrays(r["out"], r["ids"], G.out, G.ids, G.gaps, tol=TOL_BF16)
     print(g)
     assert g.ok, str(g)
+    assert g.n_graded == int(keep.sum())
 
 
 def test_prefill_multi_tile_groups(flint_bf16):
     """Skewed routing (the router bias): slot groups that span several
-    256-slot M-tiles (the largest has over 1300 slots).  Tokens on both sides
-    of every tile edge of the four largest groups, their last tokens and a
-    random sample against the oracle."""
+    256-slot M-tiles (the largest has over 1300 slots).  Every token against
+    the expert-grouped oracle."""
     T = 2048
     say("prefill T=2048 with router bias: multi-tile expert groups")
     xb = make_x(T, seed=0, x_seed=1)
     r = run(flint_bf16, xb, bias=True)
     counts = np.bincount(r["ids"].ravel(), minlength=256)
-    big = np.argsort(counts)[::-1][:4]
-    assert counts[big[0]] > 3 * 256, counts[big[0]]
-    sample = set(np.random.default_rng(1).choice(T, 24, replace=False).tolist())
-    for e in big:
-        toks = np.nonzero((r["ids"] == e).any(axis=1))[0]   # the group's slot order
-        for edge in range(256, len(toks), 256):
-            sample.update((int(toks[edge - 1]), int(toks[edge])))
-        sample.add(int(toks[-1]))
-    sample = sorted(sample)
-    res = moe_forward(flint_bf16["Lb"], xb, tokens=sample)
-    g = grade(r["out"], r["ids"], res, tokens=sample, tol=TOL_BF16)
-    print(f"{len(sample)} tokens: {g}")
+    assert counts.max() > 3 * 256, counts.max()
+    G = moe_forward_grouped(flint_bf16["Lb"], xb)
+    g = grade_arrays(r["out"], r["ids"], G.out, G.ids, G.gaps, tol=TOL_BF16)
+    print(g)
     assert g.ok, str(g)
 
 
