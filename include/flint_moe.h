@@ -267,6 +267,22 @@ flint_status flint_mlp_forward_timed(flint_mlp_ctx* ctx, const uint16_t* w13, co
 void flint_mlp_destroy(flint_mlp_ctx* ctx);                   /* NULL-safe */
 const char* flint_mlp_last_error(const flint_mlp_ctx* ctx);  /* "" if none */
 
+/* ------------------------------------------------------------------------
+ * Measurement probe (not part of the layer).  Reads `bytes` bytes at `src`
+ * once, as 16-byte non-temporal vector loads in a fully coalesced grid-stride
+ * stream (the access the layer's weight loads aim for), and writes the XOR of
+ * the 32-bit words each of its FLINT_MOE_CALIB_SINK_WORDS blocks read to
+ * sink[block] (blocks that read nothing write 0), so the XOR over the whole
+ * sink equals the XOR of every 32-bit word of the buffer.  Used to measure
+ * the HBM read rate a plain stream reaches, beside the nominal peak.
+ *   src   device, 16-byte aligned;  bytes: a positive multiple of 16
+ *   sink  device uint32 [FLINT_MOE_CALIB_SINK_WORDS]
+ * Asynchronous on `stream`.  INVALID_ARG for NULL / misaligned / bad sizes,
+ * FLINT_ERR_HIP if the launch fails. */
+#define FLINT_MOE_CALIB_SINK_WORDS 2048
+flint_status flint_moe_calib_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                                         void* stream);
+
 /* Static name of a status code. */
 const char* flint_moe_status_string(flint_status s);
 

@@ -11,5 +11,6 @@ SwiGLU MLP of Flint's first two layers.
 from .flint_moe import (  # noqa: F401
     FLINT_OK, FLINT_ERR_INVALID_ARG, FLINT_ERR_UNSUPPORTED, FLINT_ERR_WORKSPACE, FLINT_ERR_HIP,
     FLINT_W_BF16, FLINT_W_NVFP4, ABI_SYMBOLS, LIB_PATH, DeviceBank, DeviceWeights, FlintError,
-    FlintMoE, FlintMLP, bf16_bits, bf16_tensor, load_library, status_string,
+    FlintMoE, FlintMLP, CALIB_SINK_WORDS, bf16_bits, bf16_tensor, calib_stream_read, load_library,
+    status_string,
 )

@@ -47,7 +47,9 @@ ABI_SYMBOLS = (
     "flint_mlp_forward_timed",
     "flint_mlp_destroy",
     "flint_mlp_last_error",
+    "flint_moe_calib_stream_read",
 )
+CALIB_SINK_WORDS = 2048  # FLINT_MOE_CALIB_SINK_WORDS
 
 
 class Config(ctypes.Structure):
@@ -147,6 +149,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.flint_moe_status_string.restype = ctypes.c_char_p
     lib.flint_moe_last_error.argtypes = [P]
     lib.flint_moe_last_error.restype = ctypes.c_char_p
+    lib.flint_moe_calib_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.flint_moe_calib_stream_read.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -373,6 +377,13 @@ class FlintMLP:
                               stream.cuda_stream)
         if st != FLINT_OK:
             raise FlintError(st, f"flint_mlp_forward: {status_string(st)}: {self.last_error()}")
+
+
+def calib_stream_read(src_ptr: int, nbytes: int, sink_ptr: int, stream_ptr) -> None:
+    """The streaming-read probe on raw addresses (see flint_moe_calib_stream_read)."""
+    st = load_library().flint_moe_calib_stream_read(src_ptr, nbytes, sink_ptr, stream_ptr)
+    if st != FLINT_OK:
+        raise FlintError(st, f"flint_moe_calib_stream_read: {status_string(st)}")
 
 
 def bf16_tensor(bits, device):
