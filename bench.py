@@ -611,7 +611,7 @@ def hbm_calibration(args, dev, sizes):
     total = 4 * 2**30
     buf = torch.empty(total, dtype=torch.uint8, device=dev)
     buf.fill_(1)
-    sink = torch.empty(sg.CALIB_SINK_WORDS, dtype=torch.int32, device=dev)
+    sink = torch.zeros(sg.CALIB_SINK_WORDS, dtype=torch.int32, device=dev)
     base, sp = int(buf.data_ptr()), int(sink.data_ptr())
     out = {}
     for label, nbytes in sizes:

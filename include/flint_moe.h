@@ -269,14 +269,15 @@ const char* flint_mlp_last_error(const flint_mlp_ctx* ctx);  /* "" if none */
 
 /* ------------------------------------------------------------------------
  * Measurement probe (not part of the layer).  Reads `bytes` bytes at `src`
- * once, as 16-byte non-temporal vector loads in a fully coalesced grid-stride
- * stream (the access the layer's weight loads aim for), and writes the XOR of
- * the 32-bit words each of its FLINT_MOE_CALIB_SINK_WORDS blocks read to
- * sink[block] (blocks that read nothing write 0), so the XOR over the whole
- * sink equals the XOR of every 32-bit word of the buffer.  Used to measure
- * the HBM read rate a plain stream reaches, beside the nominal peak.
+ * once, as 16-byte non-temporal vector loads: one-shot blocks of 256 threads,
+ * each owning a contiguous 64 KiB chunk and issuing all of its loads before
+ * using any (the access the layer's gate/up weight loads make), and XORs the
+ * 32-bit words block b read into sink[b % FLINT_MOE_CALIB_SINK_WORDS] with
+ * atomic XORs.  With a zeroed sink, the XOR over the whole sink afterwards
+ * equals the XOR of every 32-bit word of the buffer.  Used to measure the HBM
+ * read rate a plain stream reaches, beside the nominal peak.
  *   src   device, 16-byte aligned;  bytes: a positive multiple of 16
- *   sink  device uint32 [FLINT_MOE_CALIB_SINK_WORDS]
+ *   sink  device uint32 [FLINT_MOE_CALIB_SINK_WORDS], updated (XOR) in place
  * Asynchronous on `stream`.  INVALID_ARG for NULL / misaligned / bad sizes,
  * FLINT_ERR_HIP if the launch fails. */
 #define FLINT_MOE_CALIB_SINK_WORDS 2048
