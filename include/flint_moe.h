@@ -207,6 +207,25 @@ flint_status flint_moe_block_forward_timed(flint_moe_ctx* ctx, const flint_moe_w
                                            void* stream, void* const* events, int32_t n_events,
                                            int32_t* n_kernels);
 
+/* flint_moe_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Its kernels, arguments, validation and
+ * results are those of flint_moe_forward; the workspace is instead a static
+ * device array of FLINT_MOE_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held until the process ends.  The call allocates nothing.
+ *   - T <= FLINT_MOE_NOALLOC_MAX_TOKENS (the decode-sized batches); larger T
+ *     returns FLINT_ERR_UNSUPPORTED (use flint_moe_forward).
+ *   - The first call on a device zeroes the array's completion counters on
+ *     `stream`; every completed forward leaves them zero again.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's intermediate results.  Calls that overlap on one GPU (several
+ *     streams or threads at once) race: serialise them. */
+#define FLINT_MOE_NOALLOC_SCRATCH_BYTES 2097152
+#define FLINT_MOE_NOALLOC_MAX_TOKENS 64
+flint_status flint_moe_forward_noalloc(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                       const uint16_t* x, int32_t T, uint16_t* out,
+                                       int32_t* topk_ids, float* topk_w, void* stream);
+
 /* Release a context.  NULL is allowed. */
 void flint_moe_destroy(flint_moe_ctx* ctx);
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -121,6 +122,12 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Clears n 32-bit words (a kernel rather than a memset, so that a caller may
+// capture it in a graph).
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
 }  // namespace
 
 FLINT_API flint_status flint_moe_init(const flint_moe_config* cfg, flint_moe_ctx** ctx_out) {
@@ -160,7 +167,8 @@ struct NormArgs {
 flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const uint16_t* x,
                           int32_t T, uint16_t* out, int32_t* topk_ids, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* stream,
-                          flint::Launcher& launch, const NormArgs& norm = NormArgs()) {
+                          flint::Launcher& launch, const NormArgs& norm = NormArgs(),
+                          bool zero_header_first = false) {
   if (!ctx) return FLINT_ERR_INVALID_ARG;
   ctx->last_error.clear();
   const flint_moe_config& c = ctx->cfg;
@@ -247,6 +255,12 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.nvfp4 = c.format == FLINT_W_NVFP4;
 
   (void)hipGetLastError();  // do not report an earlier, unrelated failure
+  if (zero_header_first) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(8), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       a.ws.header, (int)flint::kHeaderWords);
+    const hipError_t ez = hipGetLastError();
+    if (ez != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(ez));
+  }
   const hipError_t err = prefill ? flint::launch_prefill(a, static_cast<hipStream_t>(stream), launch)
                                  : flint::launch_decode(a, static_cast<hipStream_t>(stream), launch);
   if (err != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(err));
@@ -319,6 +333,82 @@ FLINT_API flint_status flint_moe_block_forward_timed(
   const flint_status s = forward_impl(ctx, w, r, T, out, topk_ids, topk_w, workspace,
                                       workspace_bytes, stream, launch, norm);
   *n_kernels = launch.used;
+  return s;
+}
+
+// ---------------------------------------------------------------- no-allocation forward
+
+namespace {
+
+// The no-allocation forward's workspace: a file-scope device array, one copy
+// per GPU the library runs on, kept until the process ends.  Host code never
+// passes `scratch` itself to a kernel (in host code the name is only a
+// stand-in); it takes the array's device address on each device once, with
+// hipGetSymbolAddress, and uses that address everywhere.
+constexpr size_t kScratchBytes = FLINT_MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct DeviceScratch {
+  void* ptr = nullptr;   // scratch's address on the device
+  bool zeroed = false;   // a forward has cleared its completion counters
+};
+std::mutex g_scratch_mu;
+DeviceScratch g_scratch[kMaxDevices];
+
+}  // namespace
+
+FLINT_API flint_status flint_moe_forward_noalloc(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                                 const uint16_t* x, int32_t T, uint16_t* out,
+                                                 int32_t* topk_ids, float* topk_w, void* stream) {
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  ctx->last_error.clear();
+  if (T < 0 || T > ctx->cfg.max_tokens) {
+    char buf[128];
+    std::snprintf(buf, sizeof buf, "T=%d outside [0, max_tokens=%d]", T, ctx->cfg.max_tokens);
+    return fail(ctx, FLINT_ERR_INVALID_ARG, buf);
+  }
+  if (T == 0) return FLINT_OK;
+  flint_moe_ws_layout L;
+  compute_layout(ctx->cfg, T, &L);
+  if (T > FLINT_MOE_NOALLOC_MAX_TOKENS || L.total_bytes > kScratchBytes) {
+    char buf[192];
+    std::snprintf(buf, sizeof buf,
+                  "the no-allocation forward takes T <= %d (a %zu-byte device scratch array); "
+                  "T=%d needs %zu bytes: use flint_moe_forward with a workspace",
+                  FLINT_MOE_NOALLOC_MAX_TOKENS, kScratchBytes, T, L.total_bytes);
+    return fail(ctx, FLINT_ERR_UNSUPPORTED, buf);
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ctx, FLINT_ERR_UNSUPPORTED, "device index beyond the library's per-device table");
+  void* ws = nullptr;
+  bool first = false;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    DeviceScratch& d = g_scratch[dev];
+    if (!d.ptr) {
+      e = hipGetSymbolAddress(&d.ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !d.ptr) {
+        d.ptr = nullptr;
+        return fail(ctx, FLINT_ERR_HIP, e != hipSuccess ? hipGetErrorString(e)
+                                                        : "scratch array has no device address");
+      }
+    }
+    ws = d.ptr;
+    first = !d.zeroed;
+  }
+  // The first forward on a device clears the counters on `stream`, after the
+  // arguments have been validated and before its kernels.
+  flint::Launcher launch;
+  const flint_status s = forward_impl(ctx, w, x, T, out, topk_ids, topk_w, ws, kScratchBytes,
+                                      stream, launch, NormArgs(), first);
+  if (s == FLINT_OK && first) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_scratch[dev].zeroed = true;
+  }
   return s;
 }
 

@@ -35,6 +35,7 @@ ABI_SYMBOLS = (
     "flint_moe_workspace_layout",
     "flint_moe_forward",
     "flint_moe_forward_timed",
+    "flint_moe_forward_noalloc",
     "flint_moe_block_forward",
     "flint_moe_block_forward_timed",
     "flint_moe_destroy",
@@ -118,6 +119,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             P, ctypes.c_size_t, P, ctypes.POINTER(P),
                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.flint_moe_forward_timed.restype = ctypes.c_int
+    lib.flint_moe_forward_noalloc.argtypes = [P, ctypes.POINTER(Weights), P, ctypes.c_int32, P, P,
+                                              P, P]
+    lib.flint_moe_forward_noalloc.restype = ctypes.c_int
     lib.flint_moe_block_forward.argtypes = [P, ctypes.POINTER(Weights), P, ctypes.c_float, P,
                                             ctypes.c_int32, P, P, P, P, ctypes.c_size_t, P]
     lib.flint_moe_block_forward.restype = ctypes.c_int
@@ -265,6 +269,20 @@ class FlintMoE:
                               stream.cuda_stream)
         if st != FLINT_OK:
             raise FlintError(st, f"flint_moe_forward: {status_string(st)}: {self.last_error()}")
+
+    def forward_noalloc(self, weights: DeviceWeights, x, out, topk_ids=None, topk_w=None,
+                        stream=None) -> None:
+        """The layer with the library's static scratch array as workspace (T <= 64)."""
+        import torch
+        T = int(x.shape[0])
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        st = self.lib.flint_moe_forward_noalloc(self.handle, ctypes.byref(weights.struct()), _ptr(x),
+                                                T, _ptr(out), _ptr(topk_ids), _ptr(topk_w),
+                                                stream.cuda_stream)
+        if st != FLINT_OK:
+            raise FlintError(st, f"flint_moe_forward_noalloc: {status_string(st)}: "
+                                 f"{self.last_error()}")
 
     def block_forward_raw(self, weights: Weights, gamma_ptr, eps, r_ptr, T, out_ptr, ids_ptr, w_ptr,
                           ws_ptr, ws_bytes, stream_ptr) -> int:

@@ -135,6 +135,28 @@ def test_block_forward_host_validation_without_gpu():
                                      [None] * 4)[0] == sg.FLINT_ERR_INVALID_ARG
 
 
+def test_noalloc_forward_host_validation_without_gpu():
+    """The no-allocation forward rejects what its static scratch cannot hold
+    before it touches the GPU."""
+    m = sg.FlintMoE(max_tokens=128)
+    W = _fake_weights()
+    x, out = 1 << 30, 1 << 31
+    lib = m.lib
+    call = lambda T: lib.flint_moe_forward_noalloc(m.handle, ctypes.byref(W), x, T, out, None,
+                                                   None, None)
+    assert call(65) == sg.FLINT_ERR_UNSUPPORTED and "T <= 64" in m.last_error()
+    assert call(129) == sg.FLINT_ERR_INVALID_ARG and "max_tokens" in m.last_error()
+    assert call(-1) == sg.FLINT_ERR_INVALID_ARG
+    assert call(0) == sg.FLINT_OK
+    assert lib.flint_moe_forward_noalloc(None, None, None, 1, None, None, None, None) == \
+        sg.FLINT_ERR_INVALID_ARG
+    hdr = open(os.path.join(ROOT, "include", "flint_moe.h")).read()
+    assert int(re.search(r"FLINT_MOE_NOALLOC_MAX_TOKENS\s+(\d+)", hdr).group(1)) == 64
+    # The largest batch it takes fits its scratch array.
+    scratch = int(re.search(r"FLINT_MOE_NOALLOC_SCRATCH_BYTES\s+(\d+)", hdr).group(1))
+    assert sg.FlintMoE(max_tokens=64, top_k=8).workspace_bytes(64) <= scratch
+
+
 def test_workspace_has_a_normed_region():
     m = sg.FlintMoE(max_tokens=8192)
     for T in (1, 8, 64, 65, 8192):
