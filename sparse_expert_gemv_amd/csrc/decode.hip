@@ -89,10 +89,16 @@ __device__ __forceinline__ void wait_vmem_all() {
 // One x row (H bf16 = kVecH 16-byte vectors, one per thread) into LDS with
 // an LDS-direct load: no registers, and a thread's loads for several rows
 // are all in flight before the barrier that waits for them.  Lane l of a
-// wave writes the 16 bytes at the wave's LDS base + 16 l.
+// wave writes the 16 bytes at the wave's LDS base + 16 l, so LDS position t
+// (t < kVecH) receives the vector thread t loads: vector t, or with kPermute
+// vector 4 (t % 64) + t / 64, the order in which the NVFP4 gate/up rows read
+// x (lane l's i-th vector covers columns [32 l + 8 i, +8)), so that their
+// reads of position l + 64 i stay free of bank conflicts.
+template <bool kPermute = false>
 __device__ __forceinline__ void stage_x_row(u32x4* dst, const uint16_t* row) {
   const int wave_base = threadIdx.x & ~(kWave - 1);
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(row) + threadIdx.x,
+  const int src = kPermute ? 4 * (threadIdx.x & (kWave - 1)) + threadIdx.x / kWave : threadIdx.x;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(row) + src,
                                    (lds_ptr_t)(dst + wave_base), 16, 0, 0);
 }
 
@@ -138,14 +144,16 @@ struct GateUpRows<false> {
   __device__ __forceinline__ void pin() {}
 };
 
-// NVFP4: 8 E2M1 codes (one 32-bit word) and their E4M3 block scale per row
-// per i; the codes convert exactly to bf16 and meet x in bf16 dot products,
-// the block scale multiplies each 8-element partial sum, the tensor scale
-// the row total.
+// NVFP4: lane l holds columns [32 l, 32 l + 32) of each of its 4 rows as one
+// 16-byte load of E2M1 codes (words i = 0..3: columns [32 l + 8 i, +8)) and
+// the two E4M3 scales of those columns' 16-element blocks as one 2-byte load;
+// the x vectors arrive in the matching order (stage_x_row<true>).  The codes
+// convert exactly to bf16 and meet x in bf16 dot products; the block scale
+// multiplies each 8-element partial sum, the tensor scale the row total.
 template <>
 struct GateUpRows<true> {
-  uint32_t q[4][kVecPerLaneH];
-  uint32_t sc[4][kVecPerLaneH];  // E4M3 byte
+  uint32_t q[4][kVecPerLaneH];   // codes: [row][word]
+  uint32_t sc[4];                // two E4M3 bytes (blocks 2l, 2l + 1) per row
   float g;
   __device__ __forceinline__ void load(const Bank& bank, int e, int p0) {
     const uint8_t* w13 = bank.w13 + (size_t)e * 2 * I * (H / 2);
@@ -153,13 +161,18 @@ struct GateUpRows<true> {
     const int lane = threadIdx.x & (kWave - 1);
     const int p = p0 + 2 * (threadIdx.x / kWave);
     const int row[4] = {p, p + 1, I + p, I + p + 1};
+    static_assert(H / 2 == 16 * kWave && H / 16 == 2 * kWave, "one 16-byte code vector per lane");
 #pragma unroll
-    for (int i = 0; i < kVecPerLaneH; ++i)
+    for (int r = 0; r < 4; ++r) {
+      const u32x4 v = load_stream(reinterpret_cast<const u32x4*>(w13 + (size_t)row[r] * (H / 2)) + lane);
+      q[r][0] = v.x;
+      q[r][1] = v.y;
+      q[r][2] = v.z;
+      q[r][3] = v.w;
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        q[r][i] = load_stream(reinterpret_cast<const uint32_t*>(w13 + (size_t)row[r] * (H / 2)) + lane + i * kWave);
-        sc[r][i] = load_stream(s13 + (size_t)row[r] * (H / 16) + (lane * 8 + i * 512) / 16);
-      }
+    for (int r = 0; r < 4; ++r)
+      sc[r] = load_stream(reinterpret_cast<const uint16_t*>(s13 + (size_t)row[r] * (H / 16)) + lane);
     g = bank.w13_gscale[e];
   }
   __device__ __forceinline__ float dot(int r, int i, const u32x4& xv, float acc) const {
@@ -171,15 +184,19 @@ struct GateUpRows<true> {
     p = dot2_bf16(fp4x2_to_bf16x2<1>(c), xv.y, p);
     p = dot2_bf16(fp4x2_to_bf16x2<2>(c), xv.z, p);
     p = dot2_bf16(fp4x2_to_bf16x2<3>(c), xv.w, p);
-    return fmaf(p, __builtin_amdgcn_cvt_f32_fp8((int)sc[r][i], 0), acc);
+    const float s = i < 2 ? __builtin_amdgcn_cvt_f32_fp8((int)sc[r], 0)
+                          : __builtin_amdgcn_cvt_f32_fp8((int)sc[r], 1);
+    return fmaf(p, s, acc);
   }
   // Keep the codes packed across tokens: widening every word once, outside
   // the token loop, would need four times the registers.
   __device__ __forceinline__ void pin() {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int i = 0; i < kVecPerLaneH; ++i) asm volatile("" : "+v"(q[r][i]), "+v"(sc[r][i]));
+      for (int i = 0; i < kVecPerLaneH; ++i) asm volatile("" : "+v"(q[r][i]));
+      asm volatile("" : "+v"(sc[r]));
+    }
   }
 };
 
@@ -197,7 +214,7 @@ __device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int
   // flight; the barrier at the top of the loop waits for both.
   auto stage = [&](int c0) {
     const int n = min(kChunk, count - c0);
-    for (int j = 0; j < n; ++j) stage_x_row(xs + j * kVecH, x + (size_t)list.tok(c0 + j) * H);
+    for (int j = 0; j < n; ++j) stage_x_row<kFp4>(xs + j * kVecH, x + (size_t)list.tok(c0 + j) * H);
   };
   if (count > 0) stage(0);
   for (int c0 = 0; c0 < count; c0 += kChunk) {
