@@ -18,7 +18,13 @@ pre-norm block (``block``) is pinned by a worked example, closed forms of the
 norm, every bf16 rounding midpoint, and reductions to the residual alone and to
 the bare layer.  The dense MLP of layers 0 and 1 (``dense``) is pinned by a
 worked example, structured rows with a closed form, additivity over
-intermediate channels, and its reduction to the layer's shared expert.
+intermediate channels, and its reduction to the layer's shared expert.  The
+low-latency decode path around the layer (``decoder``: attention output
+projection, rounded residual adds, the next layer's norm) is pinned by a
+brute-force projection, hand-worked residual roundings, closed forms of the
+next norm, and its reduction to the block oracle when the projection is
+zero.  The expert-grouped evaluation (``grouped``) is pinned token by token
+against the per-token oracle.
 
 Parity unpinned: agreement with Recursive's own runtime at the real Flint
 shape cannot be checked here (neither that runtime nor trained weights are
@@ -42,4 +48,5 @@ from .moe import (  # noqa: F401
 )
 from .block import BlockResult, block_forward, block_token, f64_to_bf16_bits, rmsnorm  # noqa: F401
 from .dense import DenseMLP, mlp_block_forward, mlp_forward, mlp_token  # noqa: F401
+from .decoder import DecoderResult, decoder_forward, decoder_token, o_proj  # noqa: F401
 from .nvfp4 import e2m1_to_f64, e4m3fn_to_f64, nvfp4_dequant  # noqa: F401
