@@ -23,8 +23,14 @@
  *   s_e   = 1 / (1 + exp(-z_e))
  *   S_t   = the top_k experts by s_e, ties to the lower index
  *   w_j   = s_{S_j} / sum_i s_{S_i}   (renormalize = 1)  else s_{S_j};  times routed_scale
- *   h_e   = silu(W13_e[0:I] x_t) * (W13_e[I:2I] x_t)       (fp32, never rounded)
+ *   h_e   = silu(W13_e[0:I] x_t) * (W13_e[I:2I] x_t)       (fp32 accumulate)
  *   out_t = W2_sh h_sh + sum_j w_j W2_{S_j} h_{S_j}          (fp32, rounded once to bf16, RNE)
+ * Intermediate precision: for T <= 64 (the decode kernels) h is kept in fp32
+ * and never rounded.  For T > 64 (the MFMA GEMMs) h and each slot's
+ * unweighted W2 h cross between launches as fp16 carrying a 2^-8 bias (the
+ * stored value is fp16(v * 2^-8)): 11 significant bits, finite for
+ * |h|, |W2 h| < 65504 * 2^8 = 1.68e7, values below 2^-6 kept to an absolute
+ * 2^-17; w2 enters those GEMMs as fp16 (exact for 2^-14 <= |w| <= 65504).
  *
  * Conventions for every call:
  *   - bf16 values are passed as uint16_t bit patterns.
@@ -241,7 +247,8 @@ void flint_moe_destroy(flint_moe_ctx* ctx);
  * and with a norm gain (the pre-norm block, as for flint_moe_block_forward):
  *   out_t = bf16_rne( r_t + W2 h(n_t) ),  n_t = bf16_rne(RMSNorm(r_t) * gamma)
  * T <= 64 runs GEMV kernels; larger T runs MFMA GEMMs that keep h in fp16
- * between the two products.  Same conventions as the layer above (caller-owned
+ * between the two products, with the 2^-8 bias of the layer's prefill path
+ * (finite for |h| < 1.68e7).  Same conventions as the layer above (caller-owned
  * memory, asynchronous on `stream`, host-side validation). */
 typedef struct flint_mlp_ctx flint_mlp_ctx; /* opaque, host memory */
 

@@ -3,40 +3,47 @@
 // batch sizes each expert sees ~T*6/256 tokens and the work is a dense
 // contraction per expert.
 //
-// Six launches on the caller's stream:
-//   1. router  : logits[64 tokens x 256] = X Wr^T per block (bf16 MFMA, fp32
-//                accumulate, + bias), top-k per token by sigmoid score, the
-//                routing weights, and the block's per-expert slot counts.
-//   2. scan    : one block turns the counts into expert offsets, the routing
-//                table (U ascending) and the grouped-GEMM tile list (128 slots
-//                per tile, no padding stored).
-//   3. scatter : stable counting sort of the (token, rank) slots by expert,
-//                ascending slot order within an expert; the inverse
-//                permutation is kept for the combine.
-//   4. gate/up : grouped GEMM per (expert tile, 128 h columns): gathered x
+// Five launches on the caller's stream (six for the pre-norm block, whose
+// RMSNorm of r into the workspace buffer `normed` comes first, one wave per
+// token):
+//   1. router  : logits[32 tokens x 256] = X Wr^T per block (bf16 MFMA, fp32
+//                accumulate, + bias), then in the epilogue the top-k of each
+//                token by sigmoid score (a wave ranks four tokens at a time
+//                from the logits parked in LDS), the routing weights, and the
+//                block's per-expert slot counts.
+//   2. bucket  : every block sums the router blocks' counts, scans them into
+//                expert offsets and places its own (token, rank) slots in
+//                stable order (ascending slot within an expert); block 0
+//                writes the routing table (U ascending) and the grouped-GEMM
+//                tile list (256-slot M-tiles of one expert, no padding
+//                stored); the inverse permutation is kept for the combine.
+//   3. gate/up : grouped GEMM per (256-slot tile, 128 h columns): gathered x
 //                rows times the gate and up rows of w13 (bf16 MFMA), SiLU-and-
 //                mul in registers, h stored as fp16 in sorted slot order (the
-//                shared expert's tiles cover tokens in order).
-//   5. down    : grouped GEMM per (routed expert tile, 256 output columns):
-//                h (fp16) times w2 (bf16 converted to fp16 on its way into
-//                LDS, exact for |w| >= 2^-14) into fp16 y per slot.
-//   6. shared down + combine : the shared expert's down GEMM per (128 tokens,
-//                256 columns) whose epilogue adds sum_j w_j * y_j in rank order
-//                and rounds once to bf16.
-// The pre-norm block adds a first launch, the RMSNorm of r into the workspace
-// buffer the router and gate/up GEMMs then read as x (one wave per token),
-// and the combine adds r before its one rounding.
-// All GEMMs share one block-level scheme: 256 threads (4 waves); A and B
-// tiles move from global memory straight into LDS (LDS-direct loads, no
-// register staging) 32 K-elements at a time through a three-stage ring, so
-// two stages' loads are in flight while the third feeds the matrix cores;
+//                shared expert's tiles cover the tokens in order).
+//   4. down    : grouped GEMM per (routed 256-slot tile, 256 output columns):
+//                h (fp16) times w2 (bf16 converted to fp16 in registers) into
+//                the unweighted fp16 y of each slot.
+//   5. shared down + combine : the shared expert's down GEMM per (256
+//                tokens, 256 columns) whose epilogue adds sum_j w_j * y_j in
+//                rank order (+ r for the block) and rounds once to bf16.
+// All GEMMs share one block-level scheme (BlockGemm): A and B tiles move
+// from global memory straight into LDS (LDS-direct loads, no register
+// staging) 32 K-elements at a time through a three-stage ring, so two
+// stages' loads are in flight while the third feeds the matrix cores;
 // 64-byte LDS rows with their 16-byte chunks XOR-swizzled by row, so that
-// the fragment reads of 16 consecutive rows hit distinct banks; each wave
-// owns a 64x128 (or 64x64) tile of 32x32x16 MFMAs.
-// Numerics: fp32 accumulation everywhere; h and y are stored as fp16 (11-bit
-// significand), so the roundings this path adds to the decode path's fp32
-// arithmetic are those of h and y to fp16 and of tiny w2 values to fp16
-// subnormals.  h and y must stay within fp16's range (|v| < 65504).
+// the fragment reads of consecutive rows hit distinct banks.  The grouped
+// GEMMs run 256 x 256 block tiles on eight waves of 64 x 128 (32x32x16
+// MFMAs); the router 32 x 256 on four waves of 32 x 64.
+// Numerics: fp32 accumulation everywhere.  h and y cross the launches as
+// fp16 (11-bit significand) carrying a power-of-two bias: h is stored as
+// fp16(h * 2^-8), so the down GEMMs produce y * 2^-8, which the routed down
+// stores as fp16 and the combine multiplies back by 2^8 (exactly) after the
+// weighted sum.  The bias moves fp16's overflow threshold from 65504 to
+// 65504 * 2^8 = 1.68e7 for |h| and |y|; values below 2^-6 are stored with
+// the fp16 subnormal spacing, an absolute error of at most 2^-17.  w2 is
+// widened from bf16 to fp16 exactly for 2^-14 <= |w| <= 65504; smaller
+// weights keep an absolute error below 2^-25.
 //
 // What is computed follows "vLLM Day-0 Support for Recursive's Flint"
 // (section "Flint Model Architecture", bullet "MoE Structure"; section
@@ -57,6 +64,10 @@ constexpr int I = kInter;
 constexpr int kThreads = 256;
 constexpr int kMT = kPrefillTile;   // tokens per router / scatter block
 constexpr int kGM = kGroupTile;     // slots per grouped-GEMM M-tile
+// Power-of-two bias of the fp16 h (and so of the down GEMMs' results): see
+// the numerics note above.  Multiplying by either is exact.
+constexpr float kH16Bias = 1.0f / 256.0f;
+constexpr float kH16Unbias = 256.0f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -634,7 +645,7 @@ __global__ __launch_bounds__(GateUpGemm::kBlockThreads, 1) void prefill_gateup_k
         for (int ct = 0; ct < 2; ++ct) {
           const int col = nb * 128 + wn * 64 + ct * 32 + (lane & 31);
           const float gv = g.acc[rt][ct][r], uv = g.acc[rt][ct + 2][r];
-          h16[(size_t)(hrow0 + row) * I + col] = (_Float16)(silu(gv) * uv);
+          h16[(size_t)(hrow0 + row) * I + col] = (_Float16)(silu(gv) * uv * kH16Bias);
         }
       }
     }
@@ -815,6 +826,8 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_com
           o[7] = fmaf(w, f16_hi(y.w), o[7]);
         }
       }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[c] *= kH16Unbias;   // shared + weighted routed y, unbiased
       if (a.resid) {
         const u32x4 rr = *reinterpret_cast<const u32x4*>(a.resid + (size_t)t * H + nb * 256 + c8);
         o[0] += bf16_lo(rr.x);
@@ -880,7 +893,7 @@ __global__ __launch_bounds__(GateUpGemm::kBlockThreads, 1) void dense_gateup_gem
         for (int ct = 0; ct < 2; ++ct) {
           const int col = nb * 128 + wn * 64 + ct * 32 + (lane & 31);
           const float gv = g.acc[rt][ct][r], uv = g.acc[rt][ct + 2][r];
-          a.h16[(size_t)(start + row) * a.inter + col] = (_Float16)(silu(gv) * uv);
+          a.h16[(size_t)(start + row) * a.inter + col] = (_Float16)(silu(gv) * uv * kH16Bias);
         }
       }
     }
@@ -923,7 +936,7 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void dense_down_gemm_ke
         for (int ct = 0; ct < DownGemm::CT; ++ct) {
           const int col = nb * 256 + wn * DownGemm::TN + ct * 32 + (lane & 31);
           const size_t idx = (size_t)(start + row) * H + col;
-          float o = g.acc[rt][ct][r];
+          float o = g.acc[rt][ct][r] * kH16Unbias;
           if (a.resid) o += bf16_lo(a.resid[idx]);
           a.out[idx] = f32_to_bf16_rne(o);
         }

@@ -148,3 +148,28 @@ def test_dense_bitwise_deterministic():
         a, _, _ = run(d, xb, max_tokens=128)
         b, _, _ = run(d, xb, max_tokens=128)
         assert np.array_equal(a, b)
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+def test_dense_prefill_large_activations_past_fp16_range():
+    """The dense MLP's gate/up weights times 2^8 (exact in bf16): |h| far past
+    fp16's 65504 on the prefill path, every token against the oracle."""
+    import sparse_expert_gemv_amd as sg
+    from oracle.block import f64_to_bf16_bits
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say("dense prefill with |h| past the fp16 range, I_d=512, T=130")
+    S = SyntheticDenseMLP(seed=2, inter=512)
+    w13 = f64_to_bf16_bits(bf16_to_f64(S.w13()) * 256.0).reshape(S.w13().shape)
+    M = DenseMLP(2048, 512, w13, S.w2())
+    xb = make_x(130, seed=2, x_seed=1)
+    m = sg.FlintMLP(inter=512, max_tokens=256)
+    x = sg.bf16_tensor(xb, "cuda")
+    out = torch.empty_like(x)
+    m.forward(sg.bf16_tensor(w13, "cuda"), sg.bf16_tensor(S.w2(), "cuda"), x, out)
+    torch.cuda.synchronize()
+    refs = mlp_forward(M, xb)
+    h_max = max(float(np.max(np.abs(h))) for _, h in refs)
+    print(f"max |h| = {h_max:.3e}")
+    assert h_max > 4 * 65504
+    check_out(sg.bf16_bits(out), refs, block=False)

@@ -118,3 +118,44 @@ def test_decode_and_prefill_agree_at_the_boundary(flint_bf16):
     for out in (d["out"], p["out"][:64]):
         g = grade(out, d["ids"], res)
         assert g.ok, str(g)
+
+
+def _scaled_bits(bits, factor):
+    from oracle import bf16_to_f64
+    from oracle.block import f64_to_bf16_bits
+    return f64_to_bf16_bits(bf16_to_f64(bits) * factor).reshape(bits.shape)
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+def test_prefill_large_activations_past_fp16_range(flint_bf16):
+    """Every gate/up weight times 2^8 (exact in bf16): |h| reaches ~1e6 and
+    |y| ~1e5, far past fp16's 65504; the prefill path's biased fp16
+    intermediates keep them.  A 16-expert layer, T = 300, every token."""
+    import sparse_expert_gemv_amd as sg
+    from oracle import OracleLayer
+    from synth import LayerShape, SyntheticLayer
+    say("prefill with |h| past the fp16 range, T=300, 16 experts")
+    S = SyntheticLayer(3, LayerShape(n_experts=16))
+    w13 = np.stack([_scaled_bits(S.w13(e), 256.0) for e in range(16)])
+    w2 = np.stack([S.w2(e) for e in range(16)])
+    sh13, sh2 = _scaled_bits(S.w13(-1), 256.0), S.w2(-1)
+    t = lambda b: sg.bf16_tensor(b, "cuda")
+    W = sg.DeviceWeights(t(S.router_w()), None, sg.DeviceBank(t(w13), t(w2)),
+                         sg.DeviceBank(t(sh13[None]), t(sh2[None])))
+    L = OracleLayer(2048, 16, 6, 512, S.router_w(), None,
+                    lambda e: (w13[e], w2[e]) if e >= 0 else (sh13, sh2))
+    T = 300
+    xb = make_x(T, seed=3, x_seed=1)
+    moe = sg.FlintMoE(n_experts=16, max_tokens=T)
+    x = sg.bf16_tensor(xb, "cuda")
+    out = torch.empty_like(x)
+    ids = torch.full((T, 6), -1, dtype=torch.int32, device="cuda")
+    moe.forward(W, x, out, ids, None, moe.new_workspace(T, "cuda"))
+    torch.cuda.synchronize()
+    res = moe_forward(L, xb)
+    h_max = max(max(np.max(np.abs(r.h_routed)), np.max(np.abs(r.h_shared))) for r in res)
+    print(f"max |h| = {h_max:.3e}")
+    assert h_max > 4 * 65504
+    g = grade(sg.bf16_bits(out), ids.cpu().numpy(), res, tol=TOL_BF16)
+    print(g)
+    assert g.ok, str(g)
