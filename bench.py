@@ -137,6 +137,9 @@ def parse():
                    help="time the pre-norm block (RMSNorm + layer + residual add)")
     p.add_argument("--mlp", action="store_true",
                    help="time the dense MLP of layers 0-1 instead of the MoE layer")
+    p.add_argument("--lowlat", action="store_true",
+                   help="also time the low-latency decode path (attention output projection, "
+                        "layer, next norm) at T=1 and T=8, fused and in five launches")
     p.add_argument("--mlp-inter", type=int, default=14336,
                    help="intermediate size of the dense MLP")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -246,7 +249,7 @@ def kernel_names(nk: int, mlp: bool):
                 nk, [f"kernel{i}" for i in range(nk)])
 
 
-def time_kernels(timed_step, steps, stream, mlp=False):
+def time_kernels(timed_step, steps, stream, mlp=False, names=None):
     """K eager steps, each kernel bracketed by its own start/stop events.
     Returns (names, mean us per kernel, eager wall us per step)."""
     import numpy as np
@@ -265,7 +268,7 @@ def time_kernels(timed_step, steps, stream, mlp=False):
     eager_wall = (time.perf_counter() - t0) / steps
     kern_ms = np.array([[evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for j in range(nk)]
                         for i in range(steps)])
-    names = kernel_names(nk, mlp)
+    names = names[:nk] if names else kernel_names(nk, mlp)
     kern_us = kern_ms.mean(axis=0) * 1e3
     log("per-kernel us: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, kern_us)))
     return names, kern_us, eager_wall * 1e6
@@ -601,6 +604,71 @@ def measure(args, name, structs, dev, gamma, x_bits):
     return entry
 
 
+LOWLAT_NAMES = {True: ["oproj_route", "gateup", "down_nextnorm"],
+                False: ["oproj", "route", "gateup", "down", "nextnorm"]}
+
+
+def measure_lowlat(args, T, structs, wo_copies, dev, syn):
+    """The low-latency decode path (attention output projection + residual +
+    norm + layer + residual + next norm) at T tokens, fused (three launches)
+    and in five launches; returns a per-config entry."""
+    import numpy as np
+    import torch
+
+    import sparse_expert_gemv_amd as sg
+    from synth import make_attn, make_next_gain, make_residual
+
+    moe = sg.FlintMoE(max_tokens=8)
+    d = lambda b: sg.bf16_tensor(b, dev)
+    attn = d(make_attn(T, seed=args.seed, x_seed=0))
+    r = d(make_residual(T, seed=args.seed, x_seed=0))
+    gamma, gnext = d(syn.norm_weight()), d(make_next_gain(seed=args.seed))
+    r_out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    n_out = torch.empty_like(r_out)
+    ids = torch.empty((T, K_TOP), dtype=torch.int32, device=dev)
+    ws = moe.new_workspace(T, dev)
+    P = lambda t: int(t.data_ptr())
+    wos = [P(w) for w in wo_copies]
+    entry = {"workload": f"flint_moe_lowlat_t{T}", "T": T, "weights": "bf16",
+             "path": "r1 = r + Wo a; n = RMSNorm(r1) g; r_out = r1 + MoE(n); "
+                     "n_out = RMSNorm(r_out) g_next"}
+    stream = torch.cuda.current_stream(dev)
+    for fused in (True, False):
+        def step(i, sh, fused=fused):
+            st = moe.lowlat_forward_raw(structs[i % len(structs)], wos[i % len(wos)], P(attn), P(r),
+                                        P(gamma), P(gnext), EPS, T, P(r_out), P(n_out), P(ids), None,
+                                        P(ws), ws.numel(), fused, sh)
+            if st != sg.FLINT_OK:
+                raise sg.FlintError(st, moe.last_error())
+
+        def timed(i, sh, events, fused=fused):
+            st, nk = moe.lowlat_forward_timed_raw(structs[i % len(structs)], wos[i % len(wos)],
+                                                  P(attn), P(r), P(gamma), P(gnext), EPS, T,
+                                                  P(r_out), P(n_out), P(ids), None, P(ws),
+                                                  ws.numel(), fused, sh, events)
+            if st != sg.FLINT_OK:
+                raise sg.FlintError(st, moe.last_error())
+            return nk
+
+        for i in range(args.warmup):
+            step(i, stream.cuda_stream)
+        torch.cuda.synchronize()
+        n_active = int(np.unique(ids.cpu().numpy()).size)
+        names, kern_us, eager_us = time_kernels(timed, args.steps, stream, names=LOWLAT_NAMES[fused])
+        us = time_graph(step, args.steps, dev)
+        key = "fused" if fused else "unfused"
+        entry[key] = {"launches": len(names), "us_per_step": round(us, 3),
+                      "kernels_us": {n: round(float(v), 3) for n, v in zip(names, kern_us)},
+                      "eager_wall_us_per_step": round(eager_us, 2)}
+        entry["n_active"] = n_active
+        log(f"lowlat T={T} {key}: {us:.2f} us/step over {len(names)} launches")
+    w13_bytes, w2_bytes = EXPERT_BYTES["bf16"]
+    entry["algorithmic_bytes"] = (H * 4096 * 2 + ROUTER_BYTES + (entry["n_active"] + 1) *
+                                  (w13_bytes + w2_bytes) + T * (4096 + 4 * H) * 2 + 2 * H * 2)
+    entry["fused_speedup"] = round(entry["unfused"]["us_per_step"] / entry["fused"]["us_per_step"], 3)
+    return entry
+
+
 def hbm_calibration(args, dev, sizes):
     """Read rate of the plain streaming kernel at each size (bytes): windows of
     that size from a 4 GiB buffer, a different window each step (the set is
@@ -677,6 +745,14 @@ def main():
         for n in todo:
             structs = weight_structs(sg, copies, fmt, WORKLOADS[n]["bias"])
             entries[n] = measure(args, n, structs, dev, gamma, inputs[n])
+        if fmt == "bf16" and (args.workload == "suite" or args.lowlat) and not args.block:
+            from synth import make_o_proj
+            wo0 = sg.bf16_tensor(make_o_proj(seed=args.seed), dev)
+            wo_copies = [wo0] + [wo0.clone() for _ in range(1, len(copies))]
+            structs = weight_structs(sg, copies, "bf16", False)
+            for T in (1, 8):
+                entries[f"lowlat_t{T}"] = measure_lowlat(args, T, structs, wo_copies, dev, syn)
+            del wo_copies, wo0
         del copies
         torch.cuda.empty_cache()
 

@@ -138,7 +138,11 @@ typedef struct flint_moe_ws_layout {
                         for token t in row T*k + t */
   size_t extra;      /* path-private scratch (prefill-sized T only) */
   size_t normed;     /* bf16 [T][H]: the block's normalised input n (flint_moe_block_forward
-                        only; unused by flint_moe_forward) */
+                        and flint_moe_lowlat_forward; unused by flint_moe_forward) */
+  size_t resid1;     /* bf16 [T][H]: r1 = bf16(r + Wo a) (flint_moe_lowlat_forward; sized for
+                        T <= 8 only) */
+  size_t norm_part;  /* fp32 [256][T]: per down block, per token partial sums of squares of
+                        r_out (flint_moe_lowlat_forward with gamma_next; T <= 8 only) */
 } flint_moe_ws_layout;
 
 /* Validate `cfg` and create a context.  Touches no GPU state.
@@ -231,6 +235,50 @@ flint_status flint_moe_block_forward_timed(flint_moe_ctx* ctx, const flint_moe_w
 flint_status flint_moe_forward_noalloc(flint_moe_ctx* ctx, const flint_moe_weights* w,
                                        const uint16_t* x, int32_t T, uint16_t* out,
                                        int32_t* topk_ids, float* topk_w, void* stream);
+
+/* The low-latency decode path ("vLLM Day-0 Support for Recursive's Flint",
+ * section "Optimization Strategies", bullet "Low-Latency Decode Path": for up
+ * to 8 requests the MoE layer's routing and expert combine are fused into the
+ * neighbouring GEMV kernels).  Around the pre-norm block it computes, per
+ * token, the attention output projection with its residual add before the
+ * layer and the next layer's norm after it (Flint: 49 pre-norm layers, GQA
+ * with 32 query heads, "Flint Model Architecture"):
+ *   r1    = bf16_rne( r + Wo a )                     (fp32 accumulate, one rounding)
+ *   n     = bf16_rne( RMSNorm(r1) * gamma )          (as flint_moe_block_forward)
+ *   r_out = bf16_rne( r1 + layer(n) )
+ *   n_out = bf16_rne( RMSNorm(r_out) * gamma_next )  (only with gamma_next)
+ *   wo     device bf16 [H][4096] (row-major: output row o has K = 4096 contiguous)
+ *   attn   device bf16 [T][4096]: the attention output (32 heads x 128)
+ *   r      device bf16 [T][H]: the residual stream entering the projection's add
+ *   gamma  device bf16 [H]: the layer's RMSNorm gain;  eps finite, >= 0 (both norms)
+ *   gamma_next device bf16 [H] or NULL: the next layer's input-norm gain
+ *   r_out  device bf16 [T][H]: the residual stream leaving the layer (no overlap with r, attn)
+ *   n_out  device bf16 [T][H] or NULL (NULL exactly when gamma_next is NULL): the next
+ *          layer's normalised input (no overlap with r, r_out)
+ *   fused  1: three launches (projection + residual add + norm + router GEMV + routing;
+ *          gate/up; down + combine + residual add + next norm);
+ *          0: the same arithmetic in five launches (projection; norm + router + routing;
+ *          gate/up; down; next norm), for comparison
+ * T <= 8 (FLINT_ERR_UNSUPPORTED above); all 16-byte aligned; r1 is left in the
+ * workspace region `resid1` and n in `normed`.  The other arguments, the
+ * validation and the errors are those of flint_moe_forward. */
+flint_status flint_moe_lowlat_forward(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                      const uint16_t* wo, const uint16_t* attn, const uint16_t* r,
+                                      const uint16_t* gamma, const uint16_t* gamma_next, float eps,
+                                      int32_t T, uint16_t* r_out, uint16_t* n_out,
+                                      int32_t* topk_ids, float* topk_w, void* workspace,
+                                      size_t workspace_bytes, int32_t fused, void* stream);
+
+/* flint_moe_lowlat_forward with the per-kernel timing of flint_moe_forward_timed. */
+flint_status flint_moe_lowlat_forward_timed(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                            const uint16_t* wo, const uint16_t* attn,
+                                            const uint16_t* r, const uint16_t* gamma,
+                                            const uint16_t* gamma_next, float eps, int32_t T,
+                                            uint16_t* r_out, uint16_t* n_out, int32_t* topk_ids,
+                                            float* topk_w, void* workspace,
+                                            size_t workspace_bytes, int32_t fused, void* stream,
+                                            void* const* events, int32_t n_events,
+                                            int32_t* n_kernels);
 
 /* Release a context.  NULL is allowed. */
 void flint_moe_destroy(flint_moe_ctx* ctx);

@@ -431,10 +431,17 @@ __device__ void build_route_table(const LayerArgs& a, RouteLds& L) {
 // The end of a router launch: the last block to finish (it sees every
 // logit) routes every token — wave w takes tokens w, w + kWaves, ..., up to
 // 4 at a time, interleaved — and builds the routing table.
+// `routers` is the number of blocks that computed logits (the grid, unless
+// only some of the launch's blocks route); with reset_oproj the routing block
+// also clears the low-latency path's projection counter, which every router
+// block has read by the time it takes its ticket here.
 template <int kWaves>
-__device__ __forceinline__ void route_tail(const LayerArgs& a, RouteLds& L, int* s_flag) {
+__device__ __forceinline__ void route_tail(const LayerArgs& a, RouteLds& L, int* s_flag,
+                                           uint32_t routers, bool reset_oproj = false) {
   const int wave = threadIdx.x / kWave;
-  if (!last_block_ticket(a.ws.header + kHdrRouterDone, gridDim.x, s_flag)) return;
+  if (!last_block_ticket(a.ws.header + kHdrRouterDone, routers, s_flag)) return;
+  if (reset_oproj && threadIdx.x == 0)
+    __hip_atomic_store(a.ws.header + kHdrOprojDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int mine = (a.T - wave + kWaves - 1) / kWaves;
   if (mine == 1) {
     route_tokens<1>(a, wave, kWaves, 1, L.ids);
@@ -502,13 +509,23 @@ __device__ __forceinline__ float wave_sum8_transposed(float (&v)[8]) {
 
 __device__ __forceinline__ int bitrev3(int x) { return ((x & 1) << 2) | (x & 2) | ((x & 4) >> 2); }
 
+// A 16-byte vector written by another block of the same launch: four
+// coherent 32-bit loads.
+__device__ __forceinline__ u32x4 load_coherent_x4(const uint16_t* p) {
+  const int32_t* q = reinterpret_cast<const int32_t*>(p);
+  return u32x4{(uint32_t)load_coherent(q), (uint32_t)load_coherent(q + 1),
+               (uint32_t)load_coherent(q + 2), (uint32_t)load_coherent(q + 3)};
+}
+
 // Pre-norm block: rows c0 .. c0+n-1 of n = bf16(r / rms(r) * gamma) into
 // LDS, made in registers from r (thread i owns the 16-byte vector i of each
-// row, gv the matching 8 gains).  The sums of squares meet in s_ss; block 0
-// also stores the rows to `normed`, the input of the gate/up launch.
+// row, gv the matching 8 gains).  The sums of squares meet in s_ss; with
+// store_normed the block also stores the rows to `normed`, the input of the
+// gate/up launch.  kCoherent: r was written by other blocks of this launch.
 // Contains a __syncthreads: every thread of the block calls it.
+template <bool kCoherent = false>
 __device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, int n, u32x4* xs,
-                                                  const u32x4& gv, float* s_ss) {
+                                                  const u32x4& gv, float* s_ss, bool store_normed) {
   static_assert(kRouteXChunk == 8, "one transposed 8-value reduction per chunk");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -517,7 +534,10 @@ __device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, in
 #pragma unroll
   for (int j = 0; j < kRouteXChunk; ++j) {
     rv[j] = u32x4{0u, 0u, 0u, 0u};
-    if (j < n) rv[j] = reinterpret_cast<const u32x4*>(a.resid + (size_t)(c0 + j) * H)[threadIdx.x];
+    if (j < n) {
+      const uint16_t* src = a.resid + (size_t)(c0 + j) * H + 8 * threadIdx.x;
+      rv[j] = kCoherent ? load_coherent_x4(src) : *reinterpret_cast<const u32x4*>(src);
+    }
   }
 #pragma unroll
   for (int j = 0; j < kRouteXChunk; ++j) ss[j] = sumsq_bf16x8(rv[j]);
@@ -537,9 +557,62 @@ __device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, in
       const float inv_j = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), j));
       const u32x4 v = rms_scale_bf16x8(rv[j], gv, inv_j);
       xs[j * kVecH + threadIdx.x] = v;
-      if (blockIdx.x == 0) reinterpret_cast<u32x4*>(a.normed + (size_t)(c0 + j) * H)[threadIdx.x] = v;
+      if (store_normed) reinterpret_cast<u32x4*>(a.normed + (size_t)(c0 + j) * H)[threadIdx.x] = v;
     }
   }
+}
+
+// Router of the pre-norm block, block rb of `routers`: wave w computes the
+// logits of expert 4 rb + w for all T tokens, whose rows stream through LDS
+// kRouteXChunk at a time, normalised from r on the way in (kCoherentR: r was
+// written by other blocks of the same launch); router block 0 also stores
+// n for the gate/up launch.  The last router block to finish routes every
+// token and builds the routing table.
+template <bool kCoherentR>
+__device__ void route_norm_block(const LayerArgs& a, int rb, int routers, u32x4* xs, RouteLds& L,
+                                 float* s_ss, int* s_flag, bool reset_oproj) {
+  constexpr int XC = kRouteXChunk;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int e = rb * kRouterRows + wave;
+  const int er = min(e, a.E - 1);
+  for (int i = threadIdx.x; i < kMaxExperts; i += kThreads) L.cnt[i] = 0;
+  for (int i = threadIdx.x; i < kMaxExperts * kMaskWords; i += kThreads) L.occ[i] = 0;
+  u32x4 wv[kVecPerLaneH];
+  const u32x4* row = reinterpret_cast<const u32x4*>(a.router_w + (size_t)er * H);
+#pragma unroll
+  for (int i = 0; i < kVecPerLaneH; ++i) wv[i] = load_stream(row + lane + i * kWave);
+  const float bias = a.router_b ? a.router_b[er] : 0.f;
+  const u32x4 gv = reinterpret_cast<const u32x4*>(a.norm_w)[threadIdx.x];
+  auto stage = [&](int c0) __attribute__((always_inline)) {
+    stage_normed_rows<kCoherentR>(a, c0, min(XC, a.T - c0), xs, gv, s_ss, rb == 0);
+  };
+  stage(0);   // in flight together with the router rows
+  for (int c0 = 0; c0 < a.T; c0 += XC) {
+    const int n = min(XC, a.T - c0);
+    __syncthreads();   // the chunk's normalised rows are in LDS
+    float acc[XC];
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+      acc[j] = 0.f;
+      if (j < n) {
+#pragma unroll
+        for (int i = 0; i < kVecPerLaneH; ++i) acc[j] = dot8_bf16(wv[i], xs[j * kVecH + lane + i * kWave], acc[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+      if (j < n) {
+        const float z = wave_sum_lane63(acc[j]);
+        if (lane == kWave - 1 && e < a.E) store_coherent(a.ws.logits + (size_t)(c0 + j) * a.E + e, z + bias);
+      }
+    }
+    if (c0 + XC < a.T) {
+      lds_barrier();   // every wave is done with this chunk's x
+      stage(c0 + XC);
+    }
+  }
+  route_tail<kRouteWaves>(a, L, s_flag, routers, reset_oproj);
 }
 
 // Threads of a route_kernel block: 4 waves (one router row each); the bare
@@ -565,6 +638,10 @@ __global__ __launch_bounds__(route_threads(kNorm, kFused)) void route_kernel(Lay
   __shared__ RouteLds L;
   __shared__ int s_flag;
   __shared__ float s_ss[kRouteWaves * kRouteXChunk];
+  if constexpr (kNorm && !kFused) {
+    route_norm_block<false>(a, blockIdx.x, gridDim.x, xs, L, s_ss, &s_flag, false);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   // Waves kRouterRows and up (bare layer, ticketed routing) only rank tokens.
@@ -612,7 +689,7 @@ __global__ __launch_bounds__(route_threads(kNorm, kFused)) void route_kernel(Lay
   auto stage = [&](int c0) __attribute__((always_inline)) {
     const int n = min(XC, a.T - c0);
     if (kNorm) {
-      stage_normed_rows(a, c0, n, xs, gv, s_ss);
+      stage_normed_rows(a, c0, n, xs, gv, s_ss, blockIdx.x == 0);
     } else if (threadIdx.x < kVecH) {
       for (int j = 0; j < n; ++j) stage_x_row(xs + j * kVecH, a.x + (size_t)(c0 + j) * H);
     }
@@ -648,7 +725,7 @@ __global__ __launch_bounds__(route_threads(kNorm, kFused)) void route_kernel(Lay
     }
   }
   if (kFused) return;
-  route_tail<kNT / kWave>(a, L, &s_flag);
+  route_tail<kNT / kWave>(a, L, &s_flag, gridDim.x);
 }
 
 // Router of larger bare-layer batches (T > kRouteBareMinT): 16 waves per
@@ -720,7 +797,7 @@ __global__ __launch_bounds__(kRouteBareThreads) void route_bare_kernel(LayerArgs
       stage(c0 + kRouteBareXChunk);
     }
   }
-  route_tail<kRouteBareWaves>(a, L, &s_flag);
+  route_tail<kRouteBareWaves>(a, L, &s_flag, gridDim.x);
 }
 
 // Routing of a small batch inside one block, from the logits of the router
@@ -883,6 +960,9 @@ void gateup_kernel(LayerArgs a) {
   gateup_compute(wv, unit * kPairsPerItem, cnt, TokenList{s_slots, a.k, 0}, a.x, a.ws.h, xs);
 }
 
+
+// The low-latency path's next-layer norm at the end of the down launch.
+__device__ void next_norm_tail(const LayerArgs& a);
 
 // Down + combine.  Block b owns output rows [8b, 8b + 8) of every token and
 // walks the |U| active experts and then the shared expert; wave w takes
@@ -1192,14 +1272,174 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
     }
   }
   __syncthreads();
-  for (int q = threadIdx.x; q < T * kDownRowsPerBlock; q += kDownThreads) {
+  const bool next_norm = a.norm_next_w != nullptr;
+  static_assert(kDecodeMaxT * kDownRowsPerBlock <= kDownThreads, "one (token, row) per thread");
+  if ((int)threadIdx.x < T * kDownRowsPerBlock) {
+    const int q = threadIdx.x;
     const int t = q / kDownRowsPerBlock;
     const int r = q - t * kDownRowsPerBlock;
     float o = part[(T * k + t) * kDownRowsPerBlock + r];
     for (int j = 0; j < k; ++j)
       o = fmaf(s_wts[t * k + j], part[(t * k + j) * kDownRowsPerBlock + r], o);
     if (a.resid) o += bf16_lo(a.resid[(size_t)t * H + r0 + r]);
-    a.out[(size_t)t * H + r0 + r] = f32_to_bf16_rne(o);
+    const uint16_t ob = f32_to_bf16_rne(o);
+    if (!next_norm) {
+      a.out[(size_t)t * H + r0 + r] = ob;
+    } else {
+      // The 8 rows of token t are 8 consecutive lanes of one wave: their
+      // squares (of the stored bf16 values) summed in a fixed tree, the row
+      // pairs stored as write-through 32-bit words for the norm tail.
+      const float v = bf16_lo(ob);
+      float ss = v * v;
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      ss += __shfl_xor(ss, 4);
+      const uint32_t odd = (uint32_t)__shfl_xor((int)ob, 1);
+      if ((r & 1) == 0)
+        store_coherent(reinterpret_cast<int32_t*>(a.out + (size_t)t * H + r0 + r), (int32_t)(ob | (odd << 16)));
+      if (r == 0) store_coherent(a.ws.norm_part + (size_t)blockIdx.x * T + t, ss);
+    }
+  }
+  if (next_norm) next_norm_tail(a);
+}
+
+// ---------------------------------------------------------------- low-latency decode path
+
+// The attention output projection with the residual add, for up to
+// kLowLatMaxT tokens: block b owns output rows [8b, 8b + 8), wave w rows
+// 8b + 2w and 8b + 2w + 1 (8 KiB of Wo each; lane l holds columns
+// [8l + 512i, +8), i = 0..7), and the T tokens' attention rows are staged in
+// LDS.  r1[t][row] = bf16(r[t][row] + sum_k Wo[row][k] a[t][k]) with fp32
+// accumulation and one rounding; a wave stores its two rows of a token as
+// one 32-bit word (kCoherent: write-through, for readers in the same launch).
+constexpr int kAttnVec = kAttnWidth / 8;              // 512 16-byte vectors per row
+constexpr int kAttnVecPerLane = kAttnVec / kWave;     // 8
+constexpr int kOprojRows = H / kOprojBlocks;          // 8 per block
+static_assert(kOprojRows == 2 * kRouteWaves, "two projection rows per wave");
+static_assert(kAttnVec % kThreads == 0, "attention row staging");
+
+struct OprojLds {
+  u32x4 attn[kLowLatMaxT * kAttnVec];   // 64 KiB; then the router's chunk of normalised rows
+  RouteLds route;
+  float ss[kRouteWaves * kRouteXChunk];
+  int flag;
+};
+static_assert(kRouteXChunk * kVecH <= kLowLatMaxT * kAttnVec, "router chunk fits the attention staging");
+
+template <bool kCoherent>
+__device__ __forceinline__ void oproj_rows(const LayerArgs& a, u32x4* xs_attn) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int row0 = blockIdx.x * kOprojRows + 2 * wave;
+  const int T = a.T;
+  u32x4 w[2][kAttnVecPerLane];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < kAttnVecPerLane; ++i)
+      w[r][i] = load_stream(reinterpret_cast<const u32x4*>(a.wo + (size_t)(row0 + r) * kAttnWidth) + lane +
+                            i * kWave);
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int u = 0; u < kAttnVec / kThreads; ++u) {
+      const int v = threadIdx.x + u * kThreads;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(a.attn + (size_t)j * kAttnWidth) + v,
+                                       (lds_ptr_t)(xs_attn + j * kAttnVec + (v & ~(kWave - 1))), 16, 0, 0);
+    }
+  // r's two entries of every token (one 32-bit word each), in flight with the rest.
+  uint32_t rp[kLowLatMaxT];
+#pragma unroll
+  for (int j = 0; j < kLowLatMaxT; ++j)
+    rp[j] = j < T ? *reinterpret_cast<const uint32_t*>(a.resid0 + (size_t)j * H + row0) : 0u;
+  wait_vmem_all();
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kLowLatMaxT; ++j) {
+    if (j >= T) break;
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kAttnVecPerLane; ++i) {
+      const u32x4 xv = xs_attn[j * kAttnVec + lane + i * kWave];
+      acc0 = dot8_bf16(w[0][i], xv, acc0);
+      acc1 = dot8_bf16(w[1][i], xv, acc1);
+    }
+    acc0 = wave_sum_lane63(acc0);
+    acc1 = wave_sum_lane63(acc1);
+    if (lane == kWave - 1) {
+      const uint32_t r1 = pack_bf16x2_rne(bf16_lo(rp[j]) + acc0, bf16_hi(rp[j]) + acc1);
+      int32_t* dst = reinterpret_cast<int32_t*>(a.ws.resid1 + (size_t)j * H + row0);
+      if (kCoherent) store_coherent(dst, (int32_t)r1);
+      else *dst = (int32_t)r1;
+    }
+  }
+}
+
+// Bounded wait (one thread) until *counter reaches target.  Every wave gets
+// past it: after kSpinLimit polls it gives up and sets *expired, which the
+// caller's tests check, so that a wait that cannot end still lets the grid
+// drain.
+constexpr int kSpinLimit = 1 << 22;
+__device__ __forceinline__ void wait_count(uint32_t* counter, uint32_t target, uint32_t* expired) {
+  for (int i = 0; i < kSpinLimit; ++i) {
+    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __hip_atomic_store(expired, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The projection, and with kFused the routing fused into it ("vLLM Day-0
+// Support for Recursive's Flint", section "Optimization Strategies", bullet
+// "Low-Latency Decode Path"): every block takes a ticket once its r1 rows
+// are stored; the last `routers` blocks to arrive become the router blocks
+// (the ticket order makes the waits deadlock-free: a waiting block has
+// finished its projection and holds one of at most `routers` of the chip's
+// block slots while the rest of the grid, already started or free to start,
+// completes), wait until every projection block has counted in, and run the
+// pre-norm router and the routing tail on r1.
+template <bool kFused>
+__global__ __launch_bounds__(kThreads) void oproj_kernel(LayerArgs a) {
+  __shared__ OprojLds S;
+  oproj_rows<kFused>(a, S.attn);
+  if constexpr (kFused) {
+    drain_memory_ops();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      S.flag = (int)__hip_atomic_fetch_add(a.ws.header + kHdrOprojDone, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int ticket = S.flag;
+    const int routers = (a.E + kRouterRows - 1) / kRouterRows;
+    const int first = (int)gridDim.x - routers;
+    if (ticket < first) return;
+    if (threadIdx.x == 0) wait_count(a.ws.header + kHdrOprojDone, gridDim.x, a.ws.header + kHdrWaitExpired);
+    __syncthreads();
+    route_norm_block<true>(a, ticket - first, routers, S.attn, S.route, S.ss, &S.flag, true);
+  }
+}
+
+// The next layer's norm, fused into the down launch: every down block has
+// stored its rows of out (r2) write-through and its per-token partial sums of
+// their squares; the last block to finish adds the partials in a fixed order,
+// and writes bf16(r2 / rms(r2) * gamma_next) for every token.
+__device__ void next_norm_tail(const LayerArgs& a) {
+  __shared__ float s_inv[kDecodeMaxT];
+  __shared__ int s_flag;
+  if (!last_block_ticket(a.ws.header + kHdrDownDone, gridDim.x, &s_flag)) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int T = a.T;
+  for (int t = wave; t < T; t += kDownWaves) {
+    float v = 0.f;
+    for (int b = lane; b < (int)gridDim.x; b += kWave) v += load_coherent(a.ws.norm_part + (size_t)b * T + t);
+    v = wave_sum_lane63(v);
+    if (lane == kWave - 1) s_inv[t] = rms_inv<H>(v, a.eps);
+  }
+  __syncthreads();
+  const int vi = threadIdx.x & (kVecH - 1);
+  const u32x4 g = reinterpret_cast<const u32x4*>(a.norm_next_w)[vi];
+  for (int t = threadIdx.x / kVecH; t < T; t += kDownThreads / kVecH) {
+    const u32x4 rv = load_coherent_x4(a.out + (size_t)t * H + 8 * vi);
+    reinterpret_cast<u32x4*>(a.normed_next + (size_t)t * H)[vi] = rms_scale_bf16x8(rv, g, s_inv[t]);
   }
 }
 
@@ -1347,6 +1587,35 @@ static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Lau
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
   return a.nvfp4 ? launch_decode_impl<true>(a, stream, launch)
                  : launch_decode_impl<false>(a, stream, launch);
+}
+
+template <bool kFp4>
+static hipError_t launch_lowlat_impl(const LayerArgs& a, bool fused, hipStream_t stream, Launcher& launch) {
+  const int n_router = (a.E + kRouterRows - 1) / kRouterRows;
+  const int n_routed = min(a.E, a.T * a.k) * kUnitsPerExpert;
+  if (fused) {
+    launch(oproj_kernel<true>, dim3(kOprojBlocks), dim3(kThreads), stream, a);
+  } else {
+    launch(oproj_kernel<false>, dim3(kOprojBlocks), dim3(kThreads), stream, a);
+    launch(route_kernel<true, false>, dim3(n_router), dim3(kThreads), stream, a);
+  }
+  launch(gateup_kernel<kFp4, false>, dim3(kUnitsPerExpert + n_routed), dim3(kThreads), stream, a);
+  if (fused) {
+    launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  } else {
+    LayerArgs b = a;
+    b.norm_next_w = nullptr;
+    launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, b);
+    if (a.norm_next_w) launch_rmsnorm(a.out, a.norm_next_w, a.eps, a.normed_next, a.T, stream, launch);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lowlat(const LayerArgs& a, bool fused, hipStream_t stream, Launcher& launch) {
+  static_assert(kOprojBlocks * (H / kOprojBlocks) == H, "projection rows");
+  static_assert(kOprojBlocks >= (kMaxExperts + kRouterRows - 1) / kRouterRows, "router blocks");
+  return a.nvfp4 ? launch_lowlat_impl<true>(a, fused, stream, launch)
+                 : launch_lowlat_impl<false>(a, fused, stream, launch);
 }
 
 }  // namespace flint

@@ -20,7 +20,16 @@ constexpr int kGroupTile = 256;    // slots per grouped-GEMM M-tile (prefill-siz
 // are zero before a forward starts and zero after it ends.
 constexpr int kLine = 64;                       // words per 256-byte line
 constexpr int kHdrRouterDone = 0 * kLine;       // decode: router blocks done
+constexpr int kHdrOprojDone = 1 * kLine;        // low-latency path: projection blocks done
+constexpr int kHdrDownDone = 2 * kLine;         // low-latency path: down blocks done
+constexpr int kHdrWaitExpired = 3 * kLine;      // set to 1 if a bounded wait ever gave up
 constexpr int kHeaderWords = 84 * kLine;        // 21 KiB
+
+// Low-latency decode path (the attention output projection, the MoE layer
+// and the next layer's norm around it), for up to kLowLatMaxT tokens.
+constexpr int kLowLatMaxT = 8;
+constexpr int kAttnWidth = 4096;                // attention output: 32 heads x 128
+constexpr int kOprojBlocks = 256;               // projection blocks (8 output rows each)
 
 // Routing table (int32), written once per forward by the block that
 // finishes routing:
@@ -49,6 +58,8 @@ struct Workspace {
   float* wts;         // [T][k]
   int32_t* route;     // routing table (see above)
   float* h;           // [T*k + T][I] (decode-sized T)
+  uint16_t* resid1;   // low-latency path: r1 = bf16(r + Wo a) [T][H]
+  float* norm_part;   // low-latency path: per down block, per token sums of squares [blocks][T]
   PrefillWs pre;      // prefill-sized T
   void* extra;
 };
@@ -73,6 +84,15 @@ struct LayerArgs {
   const uint16_t* norm_w;    // gamma [H]
   uint16_t* normed;          // [T][H], == x
   float eps;
+  // Low-latency decode path only (nullptr otherwise): the first kernel
+  // computes r1 = bf16(resid0 + wo attn) into ws.resid1, which is then the
+  // block's r (resid); with norm_next_w the down kernel also writes the next
+  // layer's normalised input bf16(RMSNorm(out) * norm_next_w) to normed_next.
+  const uint16_t* attn;      // [T][kAttnWidth]
+  const uint16_t* wo;        // [H][kAttnWidth]
+  const uint16_t* resid0;    // r [T][H]
+  const uint16_t* norm_next_w;   // gamma_next [H] or nullptr
+  uint16_t* normed_next;     // [T][H]
   const uint16_t* router_w;  // [E][H]
   const float* router_b;     // [E] or nullptr
   Bank routed, shared;
@@ -129,6 +149,12 @@ hipError_t launch_dense_prefill(const DenseArgs& a, hipStream_t stream, Launcher
 
 // The decode path (T <= kDecodeMaxT) for bf16 or NVFP4 expert weights.
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream, Launcher& launch);
+
+// The low-latency decode path (T <= kLowLatMaxT).  fused: three launches
+// (projection + residual + norm + router + routing; gate/up; down + residual
+// + next norm); otherwise five (projection + residual; norm + router +
+// routing; gate/up; down + residual; next norm).
+hipError_t launch_lowlat(const LayerArgs& a, bool fused, hipStream_t stream, Launcher& launch);
 
 // The prefill path (T > kDecodeMaxT), bf16 expert weights.
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& launch);

@@ -70,6 +70,9 @@ void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L
   L->normed = o;   o = align_up(o + t * H * sizeof(uint16_t));
   const bool prefill = T > flint::kDecodeMaxT;
   L->h = o;        o = align_up(o + (prefill ? 0 : (t * k + t) * I * sizeof(float)));
+  const bool lowlat = T <= flint::kLowLatMaxT;
+  L->resid1 = o;   o = align_up(o + (lowlat ? t * H * sizeof(uint16_t) : 0));
+  L->norm_part = o; o = align_up(o + (lowlat ? (size_t)(H / 8) * t * sizeof(float) : 0));
   L->extra = o;
   if (prefill) o = L->extra + prefill_extra_bytes(c, T, nullptr);
   L->total_bytes = o;
@@ -164,11 +167,20 @@ struct NormArgs {
   float eps = 0.f;
 };
 
+// The low-latency decode path's own arguments (flint_moe_lowlat_forward).
+struct LowLatArgs {
+  const uint16_t* wo = nullptr;
+  const uint16_t* attn = nullptr;
+  const uint16_t* gamma_next = nullptr;
+  uint16_t* n_out = nullptr;
+  bool fused = true;
+};
+
 flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const uint16_t* x,
                           int32_t T, uint16_t* out, int32_t* topk_ids, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* stream,
                           flint::Launcher& launch, const NormArgs& norm = NormArgs(),
-                          bool zero_header_first = false) {
+                          bool zero_header_first = false, const LowLatArgs* ll = nullptr) {
   if (!ctx) return FLINT_ERR_INVALID_ARG;
   ctx->last_error.clear();
   const flint_moe_config& c = ctx->cfg;
@@ -180,6 +192,27 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   if (T == 0) return FLINT_OK;
   if (!w || !x || !out || !workspace)
     return fail(ctx, FLINT_ERR_INVALID_ARG, "weights, x, out and workspace must be non-NULL");
+  if (ll) {
+    if (T > flint::kLowLatMaxT) {
+      char buf[128];
+      std::snprintf(buf, sizeof buf, "the low-latency path takes T <= %d (got T=%d)",
+                    flint::kLowLatMaxT, T);
+      return fail(ctx, FLINT_ERR_UNSUPPORTED, buf);
+    }
+    if (!ll->wo || !ll->attn)
+      return fail(ctx, FLINT_ERR_INVALID_ARG, "wo and attn must be non-NULL");
+    if (!aligned(ll->wo, 16) || !aligned(ll->attn, 16) ||
+        (ll->gamma_next && !aligned(ll->gamma_next, 16)) || (ll->n_out && !aligned(ll->n_out, 16)))
+      return fail(ctx, FLINT_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    if (!ll->gamma_next != !ll->n_out)
+      return fail(ctx, FLINT_ERR_INVALID_ARG, "gamma_next and n_out go together");
+    const size_t act = (size_t)T * ctx->cfg.hidden * sizeof(uint16_t);
+    const size_t attn_bytes = (size_t)T * flint::kAttnWidth * sizeof(uint16_t);
+    if (ranges_overlap(ll->attn, attn_bytes, out, act))
+      return fail(ctx, FLINT_ERR_INVALID_ARG, "r_out overlaps attn");
+    if (ll->n_out && (ranges_overlap(ll->n_out, act, out, act) || ranges_overlap(ll->n_out, act, x, act)))
+      return fail(ctx, FLINT_ERR_INVALID_ARG, "n_out overlaps r or r_out");
+  }
   if (norm.gamma && !aligned(norm.gamma, 16))
     return fail(ctx, FLINT_ERR_INVALID_ARG, "gamma must be 16-byte aligned");
   if (norm.gamma && !(std::isfinite(norm.eps) && norm.eps >= 0.f))
@@ -253,6 +286,18 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.renormalize = c.renormalize;
   a.routed_scale = c.routed_scale;
   a.nvfp4 = c.format == FLINT_W_NVFP4;
+  if (ll) {
+    // r1 = bf16(r + Wo attn) lands in the workspace and is the block's r from
+    // there on; x is the incoming residual stream r.
+    a.resid0 = x;
+    a.attn = ll->attn;
+    a.wo = ll->wo;
+    a.ws.resid1 = reinterpret_cast<uint16_t*>(ws + L.resid1);
+    a.ws.norm_part = reinterpret_cast<float*>(ws + L.norm_part);
+    a.resid = a.ws.resid1;
+    a.norm_next_w = ll->gamma_next;
+    a.normed_next = ll->n_out;
+  }
 
   (void)hipGetLastError();  // do not report an earlier, unrelated failure
   if (zero_header_first) {
@@ -261,8 +306,10 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
     const hipError_t ez = hipGetLastError();
     if (ez != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(ez));
   }
-  const hipError_t err = prefill ? flint::launch_prefill(a, static_cast<hipStream_t>(stream), launch)
-                                 : flint::launch_decode(a, static_cast<hipStream_t>(stream), launch);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t err = ll ? flint::launch_lowlat(a, ll->fused, hs, launch)
+                         : prefill ? flint::launch_prefill(a, hs, launch)
+                                   : flint::launch_decode(a, hs, launch);
   if (err != hipSuccess) return fail(ctx, FLINT_ERR_HIP, hipGetErrorString(err));
   return FLINT_OK;
 }
@@ -294,6 +341,65 @@ FLINT_API flint_status flint_moe_forward_timed(flint_moe_ctx* ctx, const flint_m
   launch.n = n_events;
   const flint_status s = forward_impl(ctx, w, x, T, out, topk_ids, topk_w, workspace,
                                       workspace_bytes, stream, launch);
+  *n_kernels = launch.used;
+  return s;
+}
+
+namespace {
+
+flint_status lowlat_common(flint_moe_ctx* ctx, const flint_moe_weights* w, const uint16_t* wo,
+                           const uint16_t* attn, const uint16_t* r, const uint16_t* gamma,
+                           const uint16_t* gamma_next, float eps, int32_t T, uint16_t* r_out,
+                           uint16_t* n_out, int32_t* topk_ids, float* topk_w, void* workspace,
+                           size_t workspace_bytes, int32_t fused, void* stream,
+                           flint::Launcher& launch) {
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  if (!gamma && T != 0) return fail(ctx, FLINT_ERR_INVALID_ARG, "gamma must be non-NULL");
+  if (fused != 0 && fused != 1) return fail(ctx, FLINT_ERR_INVALID_ARG, "fused must be 0 or 1");
+  NormArgs norm;
+  norm.gamma = gamma;
+  norm.eps = eps;
+  LowLatArgs ll;
+  ll.wo = wo;
+  ll.attn = attn;
+  ll.gamma_next = gamma_next;
+  ll.n_out = n_out;
+  ll.fused = fused != 0;
+  return forward_impl(ctx, w, r, T, r_out, topk_ids, topk_w, workspace, workspace_bytes, stream,
+                      launch, norm, false, &ll);
+}
+
+}  // namespace
+
+FLINT_API flint_status flint_moe_lowlat_forward(flint_moe_ctx* ctx, const flint_moe_weights* w,
+                                                const uint16_t* wo, const uint16_t* attn,
+                                                const uint16_t* r, const uint16_t* gamma,
+                                                const uint16_t* gamma_next, float eps, int32_t T,
+                                                uint16_t* r_out, uint16_t* n_out, int32_t* topk_ids,
+                                                float* topk_w, void* workspace,
+                                                size_t workspace_bytes, int32_t fused, void* stream) {
+  flint::Launcher launch;
+  return lowlat_common(ctx, w, wo, attn, r, gamma, gamma_next, eps, T, r_out, n_out, topk_ids,
+                       topk_w, workspace, workspace_bytes, fused, stream, launch);
+}
+
+FLINT_API flint_status flint_moe_lowlat_forward_timed(
+    flint_moe_ctx* ctx, const flint_moe_weights* w, const uint16_t* wo, const uint16_t* attn,
+    const uint16_t* r, const uint16_t* gamma, const uint16_t* gamma_next, float eps, int32_t T,
+    uint16_t* r_out, uint16_t* n_out, int32_t* topk_ids, float* topk_w, void* workspace,
+    size_t workspace_bytes, int32_t fused, void* stream, void* const* events, int32_t n_events,
+    int32_t* n_kernels) {
+  if (!ctx) return FLINT_ERR_INVALID_ARG;
+  if (!events || n_events < 16 || !n_kernels)
+    return fail(ctx, FLINT_ERR_INVALID_ARG, "events (>= 16) and n_kernels are required");
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return fail(ctx, FLINT_ERR_INVALID_ARG, "NULL event handle");
+  flint::Launcher launch;
+  launch.events = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  launch.n = n_events;
+  const flint_status s = lowlat_common(ctx, w, wo, attn, r, gamma, gamma_next, eps, T, r_out, n_out,
+                                       topk_ids, topk_w, workspace, workspace_bytes, fused, stream,
+                                       launch);
   *n_kernels = launch.used;
   return s;
 }

@@ -38,6 +38,8 @@ ABI_SYMBOLS = (
     "flint_moe_forward_noalloc",
     "flint_moe_block_forward",
     "flint_moe_block_forward_timed",
+    "flint_moe_lowlat_forward",
+    "flint_moe_lowlat_forward_timed",
     "flint_moe_destroy",
     "flint_moe_status_string",
     "flint_moe_last_error",
@@ -74,7 +76,7 @@ class Weights(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("total_bytes", "header", "logits", "topk_ids", "topk_w",
-                 "route", "h", "extra", "normed")]
+                 "route", "h", "extra", "normed", "resid1", "norm_part")]
 
 
 class MlpConfig(ctypes.Structure):
@@ -130,6 +132,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                   ctypes.POINTER(P), ctypes.c_int32,
                                                   ctypes.POINTER(ctypes.c_int32)]
     lib.flint_moe_block_forward_timed.restype = ctypes.c_int
+    ll = [P, ctypes.POINTER(Weights), P, P, P, P, P, ctypes.c_float, ctypes.c_int32, P, P, P, P,
+          P, ctypes.c_size_t, ctypes.c_int32, P]
+    lib.flint_moe_lowlat_forward.argtypes = ll
+    lib.flint_moe_lowlat_forward.restype = ctypes.c_int
+    lib.flint_moe_lowlat_forward_timed.argtypes = ll + [ctypes.POINTER(P), ctypes.c_int32,
+                                                        ctypes.POINTER(ctypes.c_int32)]
+    lib.flint_moe_lowlat_forward_timed.restype = ctypes.c_int
     lib.flint_mlp_init.argtypes = [ctypes.POINTER(MlpConfig), ctypes.POINTER(P)]
     lib.flint_mlp_init.restype = ctypes.c_int
     lib.flint_mlp_workspace_bytes.argtypes = [P, ctypes.c_int32]
@@ -319,6 +328,47 @@ class FlintMoE:
                                     workspace.numel() * workspace.element_size(), stream.cuda_stream)
         if st != FLINT_OK:
             raise FlintError(st, f"flint_moe_block_forward: {status_string(st)}: {self.last_error()}")
+
+    def lowlat_forward_raw(self, weights: Weights, wo_ptr, attn_ptr, r_ptr, gamma_ptr,
+                           gamma_next_ptr, eps, T, r_out_ptr, n_out_ptr, ids_ptr, w_ptr, ws_ptr,
+                           ws_bytes, fused, stream_ptr) -> int:
+        """The low-latency path's C call with raw addresses; returns the status code."""
+        return self.lib.flint_moe_lowlat_forward(self.handle, ctypes.byref(weights), wo_ptr, attn_ptr,
+                                                 r_ptr, gamma_ptr, gamma_next_ptr, float(eps), T,
+                                                 r_out_ptr, n_out_ptr, ids_ptr, w_ptr, ws_ptr,
+                                                 ws_bytes, int(fused), stream_ptr)
+
+    def lowlat_forward_timed_raw(self, weights: Weights, wo_ptr, attn_ptr, r_ptr, gamma_ptr,
+                                 gamma_next_ptr, eps, T, r_out_ptr, n_out_ptr, ids_ptr, w_ptr,
+                                 ws_ptr, ws_bytes, fused, stream_ptr, event_handles) -> tuple:
+        """The low-latency path's timed C call; returns (status, kernels launched)."""
+        n = len(event_handles)
+        arr = (ctypes.c_void_p * n)(*event_handles)
+        nk = ctypes.c_int32(0)
+        st = self.lib.flint_moe_lowlat_forward_timed(
+            self.handle, ctypes.byref(weights), wo_ptr, attn_ptr, r_ptr, gamma_ptr, gamma_next_ptr,
+            float(eps), T, r_out_ptr, n_out_ptr, ids_ptr, w_ptr, ws_ptr, ws_bytes, int(fused),
+            stream_ptr, arr, n, ctypes.byref(nk))
+        return st, nk.value
+
+    def lowlat_forward(self, weights: DeviceWeights, wo, attn, r, gamma, r_out, gamma_next=None,
+                       n_out=None, eps=1e-6, topk_ids=None, topk_w=None, workspace=None,
+                       fused=True, stream=None) -> None:
+        """r_out = r1 + layer(RMSNorm(r1) * gamma) with r1 = r + Wo attn, and
+        n_out = RMSNorm(r_out) * gamma_next: the low-latency decode path.  Raises on error."""
+        import torch
+        T = int(r.shape[0])
+        if workspace is None:
+            workspace = self.new_workspace(T, r.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(r.device)
+        st = self.lowlat_forward_raw(weights.struct(), _ptr(wo), _ptr(attn), _ptr(r), _ptr(gamma),
+                                     _ptr(gamma_next), eps, T, _ptr(r_out), _ptr(n_out),
+                                     _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), fused,
+                                     stream.cuda_stream)
+        if st != FLINT_OK:
+            raise FlintError(st, f"flint_moe_lowlat_forward: {status_string(st)}: {self.last_error()}")
 
     def new_workspace(self, T: int, device):
         """A zero-filled workspace for up to T tokens (the header must start at zero)."""

@@ -18,5 +18,8 @@ from .flint_layer import (  # noqa: F401
     bf16_bits_to_f32,
     make_x,
     make_residual,
+    make_o_proj,
+    make_attn,
+    make_next_gain,
 )
 from .nvfp4_pack import quantize_nvfp4, NvFp4Tensor  # noqa: F401

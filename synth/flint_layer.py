@@ -26,6 +26,9 @@ fixed order, so any single tensor can be regenerated without the others:
   child 4+2E         norm gamma
 Activations use a separate SeedSequence keyed by (seed, T, x_seed); the
 residual stream another, and its outlier channels one keyed by the seed alone.
+The low-latency path's attention side (output projection Wo bf16 [2048, 4096]
+~ N(0, 0.02), attention outputs bf16 [T, 4096] ~ N(0, 1), the next layer's
+norm gain ~ 1 + N(0, 0.25)) has a domain of its own.
 
 fp32 -> bf16 conversion is round-to-nearest-even on the bit pattern.
 """
@@ -55,6 +58,8 @@ RESID_OUTLIER_GAIN = 20.0
 _X_DOMAIN = 0x5EED_0001  # keeps activation streams apart from weight streams
 _R_DOMAIN = 0x5EED_0002  # residual-stream inputs of the pre-norm block
 _D_DOMAIN = 0x5EED_0003  # dense-MLP weights (layers 0 and 1)
+_A_DOMAIN = 0x5EED_0004  # attention side of the low-latency path: Wo, attention outputs, next gain
+ATTN_WIDTH = 4096        # attention output width: 32 query heads x head dim 128
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -221,3 +226,23 @@ class SyntheticDenseMLP:
             g = np.float32(1.0) + rng.standard_normal(self.hidden, dtype=np.float32) * np.float32(GAMMA_STD)
             self._cache["gamma"] = f32_to_bf16_bits(g)
         return self._cache["gamma"]
+
+
+def make_o_proj(seed: int = 0, hidden: int = FLINT_HIDDEN, width: int = ATTN_WIDTH) -> np.ndarray:
+    """bf16 bits [H, 4096] of an attention output projection, ~ N(0, 0.02), keyed by seed."""
+    return _normal_bf16(np.random.SeedSequence([_A_DOMAIN, int(seed), 0]), (int(hidden), int(width)),
+                        WEIGHT_STD)
+
+
+def make_attn(T: int, seed: int = 0, x_seed: int = 0, width: int = ATTN_WIDTH) -> np.ndarray:
+    """bf16 bits [T, 4096] of attention outputs (per-head weighted sums of
+    values), ~ N(0, 1), keyed by (seed, T, x_seed)."""
+    seq = np.random.SeedSequence([_A_DOMAIN, int(seed), 1, int(T), int(x_seed)])
+    return _normal_bf16(seq, (int(T), int(width)), X_STD)
+
+
+def make_next_gain(seed: int = 0, hidden: int = FLINT_HIDDEN) -> np.ndarray:
+    """bf16 bits [H]: the next layer's RMSNorm gain, ~ 1 + N(0, 0.25), keyed by seed."""
+    rng = np.random.default_rng(np.random.SeedSequence([_A_DOMAIN, int(seed), 2]))
+    g = np.float32(1.0) + rng.standard_normal(int(hidden), dtype=np.float32) * np.float32(GAMMA_STD)
+    return f32_to_bf16_bits(g)
