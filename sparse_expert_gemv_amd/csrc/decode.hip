@@ -562,15 +562,30 @@ __device__ __forceinline__ void stage_normed_rows(const LayerArgs& a, int c0, in
   }
 }
 
+// Bounded wait (one thread) until *counter reaches target.  Every wave gets
+// past it: after kSpinLimit polls it gives up and sets *expired, which the
+// caller's tests check, so that a wait that cannot end still lets the grid
+// drain.
+constexpr int kSpinLimit = 1 << 22;
+__device__ __forceinline__ void wait_count(uint32_t* counter, uint32_t target, uint32_t* expired) {
+  for (int i = 0; i < kSpinLimit; ++i) {
+    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __hip_atomic_store(expired, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Router of the pre-norm block, block rb of `routers`: wave w computes the
 // logits of expert 4 rb + w for all T tokens, whose rows stream through LDS
 // kRouteXChunk at a time, normalised from r on the way in (kCoherentR: r was
 // written by other blocks of the same launch); router block 0 also stores
 // n for the gate/up launch.  The last router block to finish routes every
 // token and builds the routing table.
+// With wait_oproj (the fused low-latency path) the block waits, once its
+// router rows are on their way, until every projection block has counted in.
 template <bool kCoherentR>
 __device__ void route_norm_block(const LayerArgs& a, int rb, int routers, u32x4* xs, RouteLds& L,
-                                 float* s_ss, int* s_flag, bool reset_oproj) {
+                                 float* s_ss, int* s_flag, bool wait_oproj) {
   constexpr int XC = kRouteXChunk;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -584,6 +599,10 @@ __device__ void route_norm_block(const LayerArgs& a, int rb, int routers, u32x4*
   for (int i = 0; i < kVecPerLaneH; ++i) wv[i] = load_stream(row + lane + i * kWave);
   const float bias = a.router_b ? a.router_b[er] : 0.f;
   const u32x4 gv = reinterpret_cast<const u32x4*>(a.norm_w)[threadIdx.x];
+  if (wait_oproj) {
+    if (threadIdx.x == 0) wait_count(a.ws.header + kHdrOprojDone, gridDim.x, a.ws.header + kHdrWaitExpired);
+    __syncthreads();
+  }
   auto stage = [&](int c0) __attribute__((always_inline)) {
     stage_normed_rows<kCoherentR>(a, c0, min(XC, a.T - c0), xs, gv, s_ss, rb == 0);
   };
@@ -612,7 +631,7 @@ __device__ void route_norm_block(const LayerArgs& a, int rb, int routers, u32x4*
       stage(c0 + XC);
     }
   }
-  route_tail<kRouteWaves>(a, L, s_flag, routers, reset_oproj);
+  route_tail<kRouteWaves>(a, L, s_flag, routers, wait_oproj);
 }
 
 // Threads of a route_kernel block: 4 waves (one router row each); the bare
@@ -1374,19 +1393,6 @@ __device__ __forceinline__ void oproj_rows(const LayerArgs& a, u32x4* xs_attn) {
   }
 }
 
-// Bounded wait (one thread) until *counter reaches target.  Every wave gets
-// past it: after kSpinLimit polls it gives up and sets *expired, which the
-// caller's tests check, so that a wait that cannot end still lets the grid
-// drain.
-constexpr int kSpinLimit = 1 << 22;
-__device__ __forceinline__ void wait_count(uint32_t* counter, uint32_t target, uint32_t* expired) {
-  for (int i = 0; i < kSpinLimit; ++i) {
-    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  __hip_atomic_store(expired, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // The projection, and with kFused the routing fused into it ("vLLM Day-0
 // Support for Recursive's Flint", section "Optimization Strategies", bullet
 // "Low-Latency Decode Path"): every block takes a ticket once its r1 rows
@@ -1411,8 +1417,6 @@ __global__ __launch_bounds__(kThreads) void oproj_kernel(LayerArgs a) {
     const int routers = (a.E + kRouterRows - 1) / kRouterRows;
     const int first = (int)gridDim.x - routers;
     if (ticket < first) return;
-    if (threadIdx.x == 0) wait_count(a.ws.header + kHdrOprojDone, gridDim.x, a.ws.header + kHdrWaitExpired);
-    __syncthreads();
     route_norm_block<true>(a, ticket - first, routers, S.attn, S.route, S.ss, &S.flag, true);
   }
 }
