@@ -143,6 +143,8 @@ typedef struct flint_moe_ws_layout {
                         T <= 8 only) */
   size_t norm_part;  /* fp32 [256][T]: per down block, per token partial sums of squares of
                         r_out (flint_moe_lowlat_forward with gamma_next; T <= 8 only) */
+  size_t items;      /* int32 [min(E, T*k)][2 + T] item records (T <= 64): record a < |U| is
+                        {U[a], c = its slot count, its c slots ascending} */
 } flint_moe_ws_layout;
 
 /* Validate `cfg` and create a context.  Touches no GPU state.

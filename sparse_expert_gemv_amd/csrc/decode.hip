@@ -372,6 +372,7 @@ struct RouteLds {
   int ids[kDecodeMaxT * kMaxTopK];
   int cnt[kMaxExperts];
   int aoff[kMaxExperts];     // offset of expert e's slots
+  int aidx[kMaxExperts];     // active index of expert e
   uint32_t occ[kMaxExperts * kMaskWords];
 };
 
@@ -406,9 +407,13 @@ __device__ void build_route_table(const LayerArgs& a, RouteLds& L) {
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
       L.aoff[e] = o;
+      L.aidx[e] = act;
       if (c[q] > 0) {
         r_active[act] = e;
         r_off[act] = o;
+        int32_t* rec = a.ws.items + (size_t)act * item_record_ints(a.T);
+        rec[0] = e;
+        rec[1] = c[q];
         ++act;
       }
       o += c[q];
@@ -425,6 +430,7 @@ __device__ void build_route_table(const LayerArgs& a, RouteLds& L) {
     int rank = __popc(m[s >> 5] & ((1u << (s & 31)) - 1u));
     for (int w = 0; w < (s >> 5); ++w) rank += __popc(m[w]);
     r_slots[L.aoff[e] + rank] = s;
+    a.ws.items[(size_t)L.aidx[e] * item_record_ints(a.T) + 2 + rank] = s;
   }
 }
 
@@ -957,25 +963,21 @@ void gateup_kernel(LayerArgs a) {
     gateup_compute(wv, unit * kPairsPerItem, cnt, TokenList{FL.sorted_s + off, a.k, 0}, a.x, a.ws.h, xs);
     return;
   }
-  const int32_t* route = a.ws.route;
-  const int E = a.E;
-  // |U|, U[ai] and its slot range in one round trip (all in bounds: ai < E).
-  if (threadIdx.x == 0) {
-    s_meta[0] = route[0];
-    s_meta[1] = route[1 + ai];
-    s_meta[2] = route[1 + E + ai];
-    s_meta[3] = route[1 + E + ai + 1];
-  }
+  // |U| and item ai's record (expert, slot count, slots) in one round trip
+  // (ai < min(E, T k), the number of records the table has room for); the
+  // weights and the x rows are then requested together.
+  const int rec_ints = item_record_ints(a.T);
+  static_assert(2 + kDecodeMaxT < kThreads - 1, "record and |U| loads on distinct threads");
+  int v = 0;
+  if ((int)threadIdx.x < rec_ints) v = a.ws.items[(size_t)ai * rec_ints + threadIdx.x];
+  if (threadIdx.x == kThreads - 1) s_meta[0] = a.ws.route[0];
+  if (threadIdx.x < 2) s_meta[1 + threadIdx.x] = v;
+  else if ((int)threadIdx.x < rec_ints) s_slots[threadIdx.x - 2] = (int16_t)v;
   __syncthreads();
   if (ai >= s_meta[0]) return;
-  const int e = s_meta[1], off = s_meta[2], cnt = s_meta[3] - s_meta[2];
-  // The slot list is requested before the weights, so that only its load
-  // is waited for before the x rows are requested (cnt <= T <= kThreads).
-  const int my_slot = (int)threadIdx.x < cnt ? route[2 + 2 * E + off + threadIdx.x] : 0;
+  const int e = s_meta[1], cnt = s_meta[2];
   GateUpRows<kFp4> wv;
   wv.load(a.routed, e, unit * kPairsPerItem);
-  if ((int)threadIdx.x < cnt) s_slots[threadIdx.x] = (int16_t)my_slot;
-  __syncthreads();
   gateup_compute(wv, unit * kPairsPerItem, cnt, TokenList{s_slots, a.k, 0}, a.x, a.ws.h, xs);
 }
 

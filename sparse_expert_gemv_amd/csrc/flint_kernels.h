@@ -40,6 +40,11 @@ constexpr int kOprojBlocks = 256;               // projection blocks (8 output r
 //   [2 + 2E, 2 + 2E + T*k)   slot ids s = t*k + j, grouped by active index,
 //                            ascending within a group
 __host__ __device__ constexpr int route_table_ints(int E, int T, int k) { return 2 + 2 * E + T * k; }
+// Item records (decode-sized T, written with the routing table): record a
+// (a < |U|) = {U[a], slot count c, its c slots ascending}, a fixed stride of
+// item_record_ints(T) ints (an expert holds at most T slots), so that a
+// gate/up block reads its expert and token list in one round trip.
+__host__ __device__ constexpr int item_record_ints(int T) { return 2 + T; }
 
 // Regions used only by the prefill-sized path.
 struct PrefillWs {
@@ -58,6 +63,7 @@ struct Workspace {
   float* wts;         // [T][k]
   int32_t* route;     // routing table (see above)
   float* h;           // [T*k + T][I] (decode-sized T)
+  int32_t* items;     // [min(E, T*k)][item_record_ints(T)] item records (decode-sized T)
   uint16_t* resid1;   // low-latency path: r1 = bf16(r + Wo a) [T][H]
   float* norm_part;   // low-latency path: per down block, per token sums of squares [blocks][T]
   PrefillWs pre;      // prefill-sized T

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -70,6 +71,8 @@ void compute_layout(const flint_moe_config& c, int32_t T, flint_moe_ws_layout* L
   L->normed = o;   o = align_up(o + t * H * sizeof(uint16_t));
   const bool prefill = T > flint::kDecodeMaxT;
   L->h = o;        o = align_up(o + (prefill ? 0 : (t * k + t) * I * sizeof(float)));
+  L->items = o;    o = align_up(o + (prefill ? 0 : std::min(E, t * k) * (size_t)flint::item_record_ints(T) *
+                                                   sizeof(int32_t)));
   const bool lowlat = T <= flint::kLowLatMaxT;
   L->resid1 = o;   o = align_up(o + (lowlat ? t * H * sizeof(uint16_t) : 0));
   L->norm_part = o; o = align_up(o + (lowlat ? (size_t)(H / 8) * t * sizeof(float) : 0));
@@ -278,6 +281,7 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
   a.ws.wts = reinterpret_cast<float*>(ws + L.topk_w);
   a.ws.route = reinterpret_cast<int32_t*>(ws + L.route);
   a.ws.h = reinterpret_cast<float*>(ws + L.h);
+  a.ws.items = reinterpret_cast<int32_t*>(ws + L.items);
   a.ws.extra = ws + L.extra;
   if (prefill) prefill_extra_bytes(c, T, &a.ws.pre, ws + L.extra);
   a.T = T;

@@ -76,7 +76,7 @@ class Weights(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("total_bytes", "header", "logits", "topk_ids", "topk_w",
-                 "route", "h", "extra", "normed", "resid1", "norm_part")]
+                 "route", "h", "extra", "normed", "resid1", "norm_part", "items")]
 
 
 class MlpConfig(ctypes.Structure):
