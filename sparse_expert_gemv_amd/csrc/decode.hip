@@ -1011,6 +1011,10 @@ struct DownItem {
   bool shared;
   int off;          // routed: the item's slots start at slots[off]
   int j0, nj;
+  // The item has more slots than one entry takes, so the block's other
+  // entries of it read the same rows: load them through the caches (the
+  // repeats then hit L2) rather than with the streaming hint.
+  bool cached;
 };
 
 __device__ __forceinline__ DownItem shared_entry(const LayerArgs& a, int q) {
@@ -1020,6 +1024,7 @@ __device__ __forceinline__ DownItem shared_entry(const LayerArgs& a, int q) {
   d.off = 0;
   d.j0 = q * kDnSlots;
   d.nj = min(kDnSlots, a.T - d.j0);
+  d.cached = a.T > kDnSlots;
   return d;
 }
 
@@ -1033,6 +1038,7 @@ __device__ __forceinline__ DownItem down_entry(const LayerArgs& a, int entry,
   d.off = s_off[item - 1];
   d.j0 = q * kDnSlots;
   d.nj = min(kDnSlots, s_off[item] - d.off - d.j0);
+  d.cached = s_off[item] - d.off > kDnSlots;
   return d;
 }
 
@@ -1049,13 +1055,20 @@ template <>
 struct DownRows<false> {
   u32x4 w[kDownRowsPerBlock];
   f32x4 h0[kDnSlots], h1[kDnSlots];
+  template <bool kCached>
   __device__ __forceinline__ void load(const LayerArgs& a, const DownItem& d, int r0) {
     const Bank& bank = d.shared ? a.shared : a.routed;
     const uint16_t* w2 = reinterpret_cast<const uint16_t*>(bank.w2) + (size_t)d.e * H * I;
     const int lane = threadIdx.x & (kWave - 1);
+    if (kCached && __builtin_amdgcn_readfirstlane((int)d.cached)) {
 #pragma unroll
-    for (int r = 0; r < kDownRowsPerBlock; ++r)
-      w[r] = load_stream(reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I) + lane);
+      for (int r = 0; r < kDownRowsPerBlock; ++r)
+        w[r] = reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I)[lane];
+    } else {
+#pragma unroll
+      for (int r = 0; r < kDownRowsPerBlock; ++r)
+        w[r] = load_stream(reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I) + lane);
+    }
   }
   __device__ __forceinline__ float scale() const { return 1.0f; }
   // Lane partial of row r: its 8 columns of w2 . h.
@@ -1082,15 +1095,24 @@ struct DownRows<true> {
   uint32_t sc[kDownRowsPerBlock];
   float g;
   f32x4 h0[kDnSlots], h1[kDnSlots];
+  template <bool kCached>
   __device__ __forceinline__ void load(const LayerArgs& a, const DownItem& d, int r0) {
     const Bank& bank = d.shared ? a.shared : a.routed;
     const uint8_t* w2 = bank.w2 + (size_t)d.e * H * (I / 2);
     const uint8_t* s2 = bank.w2_scale + (size_t)d.e * H * (I / 16);
     const int lane = threadIdx.x & (kWave - 1);
+    if (kCached && __builtin_amdgcn_readfirstlane((int)d.cached)) {
 #pragma unroll
-    for (int r = 0; r < kDownRowsPerBlock; ++r) {
-      q[r] = load_stream(reinterpret_cast<const uint32_t*>(w2 + (size_t)(r0 + r) * (I / 2)) + lane);
-      sc[r] = load_stream(s2 + (size_t)(r0 + r) * (I / 16) + lane / 2);
+      for (int r = 0; r < kDownRowsPerBlock; ++r) {
+        q[r] = reinterpret_cast<const uint32_t*>(w2 + (size_t)(r0 + r) * (I / 2))[lane];
+        sc[r] = s2[(size_t)(r0 + r) * (I / 16) + lane / 2];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kDownRowsPerBlock; ++r) {
+        q[r] = load_stream(reinterpret_cast<const uint32_t*>(w2 + (size_t)(r0 + r) * (I / 2)) + lane);
+        sc[r] = load_stream(s2 + (size_t)(r0 + r) * (I / 16) + lane / 2);
+      }
     }
     g = bank.w2_gscale[d.e];
   }
@@ -1113,11 +1135,11 @@ struct DownRows<true> {
   }
 };
 
-template <bool kFp4>
+template <bool kFp4, bool kCached>
 __device__ __forceinline__ void prefetch_entry(DownRows<kFp4>& p, const LayerArgs& a, const DownItem& d,
                                                int r0, const int16_t* s_slots) {
   const int lane = threadIdx.x & (kWave - 1);
-  p.load(a, d, r0);
+  p.template load<kCached>(a, d, r0);
 #pragma unroll
   for (int j = 0; j < kDnSlots; ++j) {
     // Entries past nj re-read slot 0's h (in bounds, unused).
@@ -1156,7 +1178,11 @@ __device__ __forceinline__ void down_entry_rows(const LayerArgs& a, const DownIt
 // columns [8l, 8l + 8) of each row.  Per (h row, output row) the 64-lane
 // partial dot products are summed in a fixed tree and parked in LDS; the
 // block then combines out = shared + sum_j w_j * routed_j in a fixed order.
-template <bool kFp4>
+// kCached (batches above 8 tokens, where experts with many slots are
+// common): items cut into several entries load their rows through the caches
+// (DownItem::cached).  The smaller batches keep the one streaming load path:
+// the second path's code alone measured ~1 us slower at T = 1 and T = 8.
+template <bool kFp4, bool kCached>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   __shared__ int16_t s_active[kMaxExperts];
   __shared__ int16_t s_off[kMaxExperts + 1];
@@ -1187,10 +1213,11 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
         d.off = ai;
         d.j0 = 0;
         d.nj = 1;
+        d.cached = false;
         if (lane == 0) s_slots[ai] = (int16_t)route[2 + 2 * E + ai];   // read back by this wave only
       }
       DownRows<kFp4> p;
-      prefetch_entry(p, a, d, r0, s_slots);
+      prefetch_entry<kFp4, false>(p, a, d, r0, s_slots);
       down_entry_rows(a, d, p, s_slots, part);
     }
   } else {
@@ -1229,14 +1256,14 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
     };
     if (w + kDownWaves < n_sh) {
       da = shared_entry(a, w);
-      prefetch_entry(pa, a, da, r0, s_slots);
+      prefetch_entry<kFp4, kCached>(pa, a, da, r0, s_slots);
       db = shared_entry(a, w + kDownWaves);
-      prefetch_entry(pb, a, db, r0, s_slots);
+      prefetch_entry<kFp4, kCached>(pb, a, db, r0, s_slots);
       store_table();
       asm volatile("; down: two shared entries in flight" ::: "memory");
     } else if (w < n_sh) {
       da = shared_entry(a, w);
-      prefetch_entry(pa, a, da, r0, s_slots);
+      prefetch_entry<kFp4, kCached>(pa, a, da, r0, s_slots);
       store_table();
       asm volatile("; down: one shared entry in flight" ::: "memory");
     } else {
@@ -1263,30 +1290,30 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
 
     if (w >= n_sh && w < total) {
       da = down_entry(a, s_work[w], s_active, s_off);
-      prefetch_entry(pa, a, da, r0, s_slots);
+      prefetch_entry<kFp4, kCached>(pa, a, da, r0, s_slots);
     }
     if (w + kDownWaves >= n_sh && w + kDownWaves < total) {
       db = down_entry(a, s_work[w + kDownWaves], s_active, s_off);
-      prefetch_entry(pb, a, db, r0, s_slots);
+      prefetch_entry<kFp4, kCached>(pb, a, db, r0, s_slots);
     }
     while (w < total) {
       if (w + 2 * kDownWaves < total) {
         dc = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
-        prefetch_entry(pc, a, dc, r0, s_slots);
+        prefetch_entry<kFp4, kCached>(pc, a, dc, r0, s_slots);
       }
       down_entry_rows(a, da, pa, s_slots, part);
       w += kDownWaves;
       if (w >= total) break;
       if (w + 2 * kDownWaves < total) {
         da = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
-        prefetch_entry(pa, a, da, r0, s_slots);
+        prefetch_entry<kFp4, kCached>(pa, a, da, r0, s_slots);
       }
       down_entry_rows(a, db, pb, s_slots, part);
       w += kDownWaves;
       if (w >= total) break;
       if (w + 2 * kDownWaves < total) {
         db = down_entry(a, s_work[w + 2 * kDownWaves], s_active, s_off);
-        prefetch_entry(pb, a, db, r0, s_slots);
+        prefetch_entry<kFp4, kCached>(pb, a, db, r0, s_slots);
       }
       down_entry_rows(a, dc, pc, s_slots, part);
       w += kDownWaves;
@@ -1586,7 +1613,10 @@ static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Lau
       launch(route_kernel<false, false>, g_route, dim3(route_threads(false, false)), stream, a);
     launch(gateup_kernel<kFp4, false>, g_gateup, dim3(kThreads), stream, a);
   }
-  launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  if (a.T > kRouteBareMinT)
+    launch(down_kernel<kFp4, true>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  else
+    launch(down_kernel<kFp4, false>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
   return hipGetLastError();
 }
 
@@ -1607,11 +1637,11 @@ static hipError_t launch_lowlat_impl(const LayerArgs& a, bool fused, hipStream_t
   }
   launch(gateup_kernel<kFp4, false>, dim3(kUnitsPerExpert + n_routed), dim3(kThreads), stream, a);
   if (fused) {
-    launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+    launch(down_kernel<kFp4, false>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
   } else {
     LayerArgs b = a;
     b.norm_next_w = nullptr;
-    launch(down_kernel<kFp4>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, b);
+    launch(down_kernel<kFp4, false>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, b);
     if (a.norm_next_w) launch_rmsnorm(a.out, a.norm_next_w, a.eps, a.normed_next, a.T, stream, launch);
   }
   return hipGetLastError();
