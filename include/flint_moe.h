@@ -26,7 +26,8 @@
  *   h_e   = silu(W13_e[0:I] x_t) * (W13_e[I:2I] x_t)       (fp32 accumulate)
  *   out_t = W2_sh h_sh + sum_j w_j W2_{S_j} h_{S_j}          (fp32, rounded once to bf16, RNE)
  * Intermediate precision: for T <= 64 (the decode kernels) h is kept in fp32
- * and never rounded.  For T > 64 (the MFMA GEMMs) h and each slot's
+ * and never rounded with bf16 weights; with NVFP4 weights (W4A16: 16-bit
+ * activations) it is rounded once to bf16 (RNE) between the two GEMVs.  For T > 64 (the MFMA GEMMs) h and each slot's
  * unweighted W2 h cross between launches as fp16 carrying a 2^-8 bias (the
  * stored value is fp16(v * 2^-8)): 11 significant bits, finite for
  * |h|, |W2 h| < 65504 * 2^8 = 1.68e7, values below 2^-6 kept to an absolute
@@ -97,7 +98,7 @@ typedef struct flint_moe_config {
  *   NVFP4: w13 = uint8 [n][2I][H/2]  two E2M1 codes per byte, even k in the
  *                                    low nibble, nibble bit 3 = sign
  *          w2  = uint8 [n][H][I/2]
- *          w13_scale = uint8 [n][2I][H/16], w2_scale = uint8 [n][H][I/16]
+ *          w13_scale = uint8 [n][2I][H/16], w2_scale = uint8 [n][H][I/16] (16-byte aligned too)
  *                      E4M3FN, one per 16 consecutive K elements
  *          w13_gscale, w2_gscale = fp32 [n], one per tensor
  *          element value = e2m1(code) * e4m3(scale) * gscale            */
@@ -134,8 +135,9 @@ typedef struct flint_moe_ws_layout {
                                                  off[|U|] = T*k
                           [2+2E, 2+2E+T*k)       slots s = t*k + j grouped by U, ascending
                                                  within a group */
-  size_t h;          /* fp32 [T*k + T][I]: h of slot s in row s; h of the shared expert
-                        for token t in row T*k + t */
+  size_t h;          /* [T*k + T][I]: h of slot s in row s; h of the shared expert for
+                        token t in row T*k + t; fp32 rows with bf16 weights, bf16 rows
+                        (I values, packed from the start of the region) with NVFP4 */
   size_t extra;      /* path-private scratch (prefill-sized T only) */
   size_t normed;     /* bf16 [T][H]: the block's normalised input n (flint_moe_block_forward
                         and flint_moe_lowlat_forward; unused by flint_moe_forward) */

@@ -19,7 +19,8 @@
 //                from the start: they need no routing), then (active expert
 //                a, 8 gate/up row pairs) per block; the rows are streamed
 //                once for all of the expert's tokens; SiLU-and-mul in
-//                registers; h stays fp32.
+//                registers; h stays fp32 for bf16 weights and is stored
+//                as bf16 for NVFP4 (W4A16: 16-bit activations).
 //   3. down    : 8 output rows of every token per block, over the shared
 //                expert and the |U| active experts, each expert's w2 rows
 //                read once; the partial dot products meet in LDS and combine
@@ -233,9 +234,15 @@ __device__ __forceinline__ void gateup_compute(GateUpRows<kFp4>& wv, int p0, int
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = wave_sum_lane63(acc[r]) * wv.g;
       if (lane == kWave - 1) {
-        float* hr = h + (size_t)list.hrow(c0 + j) * hstride + p;
-        hr[0] = silu(acc[0]) * acc[2];
-        hr[1] = silu(acc[1]) * acc[3];
+        if constexpr (kFp4) {
+          // W4A16: h crosses to the down launch as 16-bit activations (bf16).
+          uint16_t* hr = reinterpret_cast<uint16_t*>(h) + (size_t)list.hrow(c0 + j) * hstride + p;
+          *reinterpret_cast<uint32_t*>(hr) = pack_bf16x2_rne(silu(acc[0]) * acc[2], silu(acc[1]) * acc[3]);
+        } else {
+          float* hr = h + (size_t)list.hrow(c0 + j) * hstride + p;
+          hr[0] = silu(acc[0]) * acc[2];
+          hr[1] = silu(acc[1]) * acc[3];
+        }
       }
     }
     if (c0 + kChunk < count) {
@@ -1070,6 +1077,13 @@ struct DownRows<false> {
         w[r] = load_stream(reinterpret_cast<const u32x4*>(w2 + (size_t)(r0 + r) * I) + lane);
     }
   }
+  // Slot j's h row (fp32): lane l's columns [8l, 8l + 8).
+  __device__ __forceinline__ void load_h(const LayerArgs& a, int j, int hrow) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)hrow * I) + lane * 2;
+    h0[j] = hp[0];
+    h1[j] = hp[1];
+  }
   __device__ __forceinline__ float scale() const { return 1.0f; }
   // Lane partial of row r: its 8 columns of w2 . h.
   __device__ __forceinline__ float partial(int r, const f32x4& a0, const f32x4& a1) const {
@@ -1086,52 +1100,52 @@ struct DownRows<false> {
   }
 };
 
-// NVFP4: the lane's 8 columns are one 32-bit word of E2M1 codes, all in one
-// 16-element block (one E4M3 scale); codes widen exactly to fp32 so h keeps
-// full precision.
+// NVFP4 (W4A16): one wave instruction covers four rows, 16 lanes per row.
+// Lane l holds columns [32 c, 32 c + 32), c = l % 16, of rows 4 i + l / 16
+// (i = 0, 1): 16 bytes of E2M1 codes and, in one 16-bit load, the E4M3
+// scales of its two 16-column blocks; and the same 32 columns of each
+// slot's h, which the gate/up launch of this format stores as bf16 (the
+// 16-bit activations of W4A16).  Every E2M1 value is a bf16 value, so the
+// products run on dot2_bf16 with fp32 accumulation; the block scales are
+// applied to the two 16-column sums and the tensor scale to the row total.
 template <>
 struct DownRows<true> {
-  uint32_t q[kDownRowsPerBlock];
-  uint32_t sc[kDownRowsPerBlock];
+  u32x4 q[2];
+  uint32_t sc[2];
   float g;
-  f32x4 h0[kDnSlots], h1[kDnSlots];
+  u32x4 h[kDnSlots][4];
   template <bool kCached>
   __device__ __forceinline__ void load(const LayerArgs& a, const DownItem& d, int r0) {
+    static_assert(I / 2 == 16 * 16 && I / 16 == 16 * 2, "16 lanes x 16 bytes of codes per row");
     const Bank& bank = d.shared ? a.shared : a.routed;
     const uint8_t* w2 = bank.w2 + (size_t)d.e * H * (I / 2);
     const uint8_t* s2 = bank.w2_scale + (size_t)d.e * H * (I / 16);
     const int lane = threadIdx.x & (kWave - 1);
+    const int c = lane & 15;
     if (kCached && __builtin_amdgcn_readfirstlane((int)d.cached)) {
 #pragma unroll
-      for (int r = 0; r < kDownRowsPerBlock; ++r) {
-        q[r] = reinterpret_cast<const uint32_t*>(w2 + (size_t)(r0 + r) * (I / 2))[lane];
-        sc[r] = s2[(size_t)(r0 + r) * (I / 16) + lane / 2];
+      for (int i = 0; i < 2; ++i) {
+        const int row = r0 + 4 * i + (lane >> 4);
+        q[i] = reinterpret_cast<const u32x4*>(w2 + (size_t)row * (I / 2))[c];
+        sc[i] = reinterpret_cast<const uint16_t*>(s2 + (size_t)row * (I / 16))[c];
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < kDownRowsPerBlock; ++r) {
-        q[r] = load_stream(reinterpret_cast<const uint32_t*>(w2 + (size_t)(r0 + r) * (I / 2)) + lane);
-        sc[r] = load_stream(s2 + (size_t)(r0 + r) * (I / 16) + lane / 2);
+      for (int i = 0; i < 2; ++i) {
+        const int row = r0 + 4 * i + (lane >> 4);
+        q[i] = load_stream(reinterpret_cast<const u32x4*>(w2 + (size_t)row * (I / 2)) + c);
+        sc[i] = load_stream(reinterpret_cast<const uint16_t*>(s2 + (size_t)row * (I / 16)) + c);
       }
     }
     g = bank.w2_gscale[d.e];
   }
-  __device__ __forceinline__ float scale() const { return g; }
-  __device__ __forceinline__ float partial(int r, const f32x4& a0, const f32x4& a1) const {
-    const uint32_t c = q[r];
-    const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
-    const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
-    const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
-    const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
-    float s = p0.x * a0.x;
-    s = fmaf(p0.y, a0.y, s);
-    s = fmaf(p1.x, a0.z, s);
-    s = fmaf(p1.y, a0.w, s);
-    s = fmaf(p2.x, a1.x, s);
-    s = fmaf(p2.y, a1.y, s);
-    s = fmaf(p3.x, a1.z, s);
-    s = fmaf(p3.y, a1.w, s);
-    return s * __builtin_amdgcn_cvt_f32_fp8((int)sc[r], 0);
+  // Slot j's h row (bf16): columns [32 c, 32 c + 32).
+  __device__ __forceinline__ void load_h(const LayerArgs& a, int j, int hrow) {
+    const int c = threadIdx.x & 15;
+    const u32x4* hp = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.ws.h) +
+                                                     (size_t)hrow * I) + c * 4;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) h[j][v] = hp[v];
   }
 };
 
@@ -1140,14 +1154,9 @@ __device__ __forceinline__ void prefetch_entry(DownRows<kFp4>& p, const LayerArg
                                                int r0, const int16_t* s_slots) {
   const int lane = threadIdx.x & (kWave - 1);
   p.template load<kCached>(a, d, r0);
+  // Entries past nj re-read slot 0's h (in bounds, unused).
 #pragma unroll
-  for (int j = 0; j < kDnSlots; ++j) {
-    // Entries past nj re-read slot 0's h (in bounds, unused).
-    const int hrow = down_hrow(a, d, j < d.nj ? j : 0, s_slots);
-    const f32x4* hp = reinterpret_cast<const f32x4*>(a.ws.h + (size_t)hrow * I) + lane * 2;
-    p.h0[j] = hp[0];
-    p.h1[j] = hp[1];
-  }
+  for (int j = 0; j < kDnSlots; ++j) p.load_h(a, j, down_hrow(a, d, j < d.nj ? j : 0, s_slots));
 }
 
 template <bool kFp4>
@@ -1155,15 +1164,56 @@ __device__ __forceinline__ void down_entry_rows(const LayerArgs& a, const DownIt
                                                 const DownRows<kFp4>& p, const int16_t* s_slots,
                                                 float* part) {
   const int lane = threadIdx.x & (kWave - 1);
+  if constexpr (kFp4) {
+    // Codes to bf16 once per entry (shared by its slots); per slot and row
+    // the 16 lanes' partials meet in a fixed butterfly, which leaves the row
+    // total in all of them.
+    u32x4 wv[2][4];
+    float s_lo[2], s_hi[2];
 #pragma unroll
-  for (int j = 0; j < kDnSlots; ++j) {
-    if (j >= d.nj) break;
-    float v[kDownRowsPerBlock];
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t cw[4] = {p.q[i].x, p.q[i].y, p.q[i].z, p.q[i].w};
 #pragma unroll
-    for (int r = 0; r < kDownRowsPerBlock; ++r) v[r] = p.partial(r, p.h0[j], p.h1[j]);
-    const float tot = wave_sum8_transposed(v);
-    if (lane < kDownRowsPerBlock)
-      part[down_hrow(a, d, j, s_slots) * kDownRowsPerBlock + bitrev3(lane)] = tot * p.scale();
+      for (int w = 0; w < 4; ++w)
+        wv[i][w] = u32x4{fp4x2_to_bf16x2<0>(cw[w]), fp4x2_to_bf16x2<1>(cw[w]), fp4x2_to_bf16x2<2>(cw[w]),
+                         fp4x2_to_bf16x2<3>(cw[w])};
+      s_lo[i] = __builtin_amdgcn_cvt_f32_fp8((int)p.sc[i], 0);
+      s_hi[i] = __builtin_amdgcn_cvt_f32_fp8((int)p.sc[i], 1);
+    }
+#pragma unroll
+    for (int j = 0; j < kDnSlots; ++j) {
+      if (j >= d.nj) break;
+      float v[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float lo = dot8_bf16(wv[i][1], p.h[j][1], dot8_bf16(wv[i][0], p.h[j][0], 0.f));
+        const float hi = dot8_bf16(wv[i][3], p.h[j][3], dot8_bf16(wv[i][2], p.h[j][2], 0.f));
+        v[i] = fmaf(hi, s_hi[i], lo * s_lo[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        v[i] += dpp<0xB1>(v[i]);    // lane ^ 1
+        v[i] += dpp<0x4E>(v[i]);    // lane ^ 2
+        v[i] += dpp<0x141>(v[i]);   // row_half_mirror: sums of 8
+        v[i] += dpp<0x140>(v[i]);   // row_mirror: sums of 16
+      }
+      if ((lane & 15) == 0) {
+        float* dst = part + down_hrow(a, d, j, s_slots) * kDownRowsPerBlock + (lane >> 4);
+        dst[0] = v[0] * p.g;
+        dst[4] = v[1] * p.g;
+      }
+    }
+  } else {
+  #pragma unroll
+    for (int j = 0; j < kDnSlots; ++j) {
+      if (j >= d.nj) break;
+      float v[kDownRowsPerBlock];
+  #pragma unroll
+      for (int r = 0; r < kDownRowsPerBlock; ++r) v[r] = p.partial(r, p.h0[j], p.h1[j]);
+      const float tot = wave_sum8_transposed(v);
+      if (lane < kDownRowsPerBlock)
+        part[down_hrow(a, d, j, s_slots) * kDownRowsPerBlock + bitrev3(lane)] = tot * p.scale();
+    }
   }
 }
 
@@ -1175,9 +1225,10 @@ __device__ __forceinline__ void down_entry_rows(const LayerArgs& a, const DownIt
 // takes entries w, w + 8, ... and keeps the next two
 // entries' w2 rows and h rows in flight while it reduces the current one
 // (two-slot entries keep three buffers within the register budget).  Lane l holds
-// columns [8l, 8l + 8) of each row.  Per (h row, output row) the 64-lane
-// partial dot products are summed in a fixed tree and parked in LDS; the
-// block then combines out = shared + sum_j w_j * routed_j in a fixed order.
+// columns [8l, 8l + 8) of each bf16 row (NVFP4: see DownRows<true>).  Per
+// (h row, output row) the lanes' partial dot products are summed in a fixed
+// tree and parked in LDS; the block then combines
+// out = shared + sum_j w_j * routed_j in a fixed order.
 // kCached (batches above 8 tokens, where experts with many slots are
 // common): items cut into several entries load their rows through the caches
 // (DownItem::cached).  The smaller batches keep the one streaming load path:

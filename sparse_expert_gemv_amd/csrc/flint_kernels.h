@@ -139,7 +139,7 @@ struct DenseArgs {
   const uint16_t* resid;   // r [T][H] for the pre-norm block, else nullptr
   const uint16_t* w13;     // [2 I][H], rows [0, I) gate, [I, 2I) up
   const uint16_t* w2;      // [H][I]
-  float* h;                // [T][I] fp32 (decode-sized T)
+  float* h;                // [T][I] fp32 (decode-sized T; bf16, 1 KiB rows, for NVFP4)
   _Float16* h16;           // [T][I] fp16 (prefill-sized T)
   int T, inter;
 };

@@ -230,6 +230,8 @@ flint_status forward_impl(flint_moe_ctx* ctx, const flint_moe_weights* w, const 
     for (const flint_expert_bank* b : banks) {
       if (!b->w13_scale || !b->w2_scale || !b->w13_gscale || !b->w2_gscale)
         return fail(ctx, FLINT_ERR_INVALID_ARG, "NVFP4 weights need block and tensor scales");
+      if (!aligned(b->w13_scale, 16) || !aligned(b->w2_scale, 16))
+        return fail(ctx, FLINT_ERR_INVALID_ARG, "block scales must be 16-byte aligned");
       if (!aligned(b->w13_gscale, 4) || !aligned(b->w2_gscale, 4))
         return fail(ctx, FLINT_ERR_INVALID_ARG, "tensor scales must be 4-byte aligned");
     }

@@ -104,6 +104,10 @@ def test_forward_host_validation_without_gpu():
     need4 = m4.workspace_bytes(4)
     assert m4.forward_raw(W, x, 4, out, None, None, ws, need4, None) == sg.FLINT_ERR_INVALID_ARG
     assert "scales" in m4.last_error()
+    b4 = ExpertBank(1 << 20, (1 << 20) + 4096, 1 << 24, (1 << 24) + 8, 1 << 25, (1 << 25) + 4)
+    W4 = Weights((1 << 20) + 8192, None, b4, b4)
+    assert m4.forward_raw(W4, x, 4, out, None, None, ws, need4, None) == sg.FLINT_ERR_INVALID_ARG
+    assert "block scales must be 16-byte aligned" in m4.last_error()
     lib = sg.load_library()
     assert lib.flint_moe_forward(None, None, None, 1, None, None, None, None, 0, None) == \
         sg.FLINT_ERR_INVALID_ARG
