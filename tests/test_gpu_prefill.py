@@ -79,6 +79,13 @@ def test_prefill_t8192_full(flint_bf16):
     print(g)
     assert g.ok, str(g)
     assert g.n_graded == int(keep.sum())
+    # The whole workspace header is zero again after the forward, and a
+    # second forward gives the same bits.
+    from sparse_expert_gemv_amd.flint_moe import HEADER_BYTES
+    hdr = r["ws"][lay["header"]:lay["header"] + HEADER_BYTES].cpu().numpy().view(np.uint32)
+    assert not hdr.any(), np.nonzero(hdr)
+    r2 = run(flint_bf16, xb)
+    np.testing.assert_array_equal(r2["out"], r["out"])
 
 
 def test_prefill_multi_tile_groups(flint_bf16):
