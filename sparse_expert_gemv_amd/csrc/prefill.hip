@@ -141,7 +141,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // (BM / WM) x (BN / WN) tile of 32x32x16 MFMAs.  kF16: A is fp16 and B (bf16
 // in memory) is converted to fp16 in registers before the MFMA; otherwise
 // both are bf16.
-template <int BM, int BN, int WM, int WN, bool kF16, int S, int KC>
+template <int BM, int BN, int WM, int WN, bool kF16, int SA, int SB, int KC>
 struct BlockGemm {
   static constexpr int kWM = WM, kWN = WN;
   static constexpr int NW = WM * WN;                  // waves per block
@@ -153,11 +153,14 @@ struct BlockGemm {
   static constexpr int RPI = 64 / CPR;                // rows per LDS-direct instruction
   static constexpr int NA = BM / (NW * RPI), NB = BN / (NW * RPI);   // instructions per thread per stage
   static constexpr int NL = NA + NB;
-  static constexpr int kStage = (BM + BN) * kRow;
-  static constexpr int kLds = S * kStage;
+  static constexpr int kStageA = BM * kRow, kStageB = BN * kRow;
+  static constexpr int kLds = SA * kStageA + SB * kStageB;   // A ring, then B ring
+  // Outstanding loads allowed at the top of a step in steady state: those
+  // issued after the last one the step needs (see run).
+  static constexpr int kWaitN = SA == SB ? (SA - 2) * NL : NB + (SA - 2) * NL;
   static_assert(KC == 32 || KC == 64, "K chunk");
   static_assert(TM % 32 == 0 && TN % 32 == 0 && BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "tile shape");
-  static_assert(S >= 2 && (S - 2) * NL < 64, "pipeline depth");
+  static_assert(SA >= 2 && SB >= SA && kWaitN < 64, "pipeline depth");
 
   f32x16 acc[RT][CT];
 
@@ -193,61 +196,90 @@ struct BlockGemm {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     const int nk = K / KC;
-    auto issue = [&](int kc) {
-      uint8_t* st = lds + (kc % S) * kStage;
-      const int k0 = kc * KC;
+    uint8_t* ldsB = lds + SA * kStageA;
+    auto issue_a = [&](int kc) {
+      uint8_t* st = lds + (kc % SA) * kStageA;
 #pragma unroll
       for (int j = 0; j < NA; ++j)
-        __builtin_amdgcn_global_load_lds(ag[j] + k0, (lds_ptr_t)(st + (wave * NA + j) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ag[j] + kc * KC, (lds_ptr_t)(st + (wave * NA + j) * 1024), 16, 0, 0);
+    };
+    auto issue_b = [&](int kc) {
+      uint8_t* st = ldsB + (kc % SB) * kStageB;
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        __builtin_amdgcn_global_load_lds(bg[j] + k0, (lds_ptr_t)(st + BM * kRow + (wave * NB + j) * 1024),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(bg[j] + kc * KC, (lds_ptr_t)(st + (wave * NB + j) * 1024), 16, 0, 0);
     };
-    // Fragment reads: rows wm*TM + rt*32 + lane%32 (A) and BM + wn*TN +
-    // ct*32 + lane%32 (B) all have swz == swz(lane % 32).
+    // Step kc issues A chunk kc + SA - 1, then B chunk kc + SB - 1; the
+    // prologue issues what the steps before 0 would have.  A step needs A
+    // and B chunk kc: with SA == SB the later of the two is B chunk kc, with
+    // SB > SA it is A chunk kc (B's ring runs further ahead), and kWaitN
+    // loads were issued after it.  Near the end fewer were: wait for all.
+#pragma unroll
+    for (int j = -(SB - 1); j < 0; ++j) {
+      if (j + SA - 1 >= 0 && j + SA - 1 < nk) issue_a(j + SA - 1);
+      if (j + SB - 1 < nk) issue_b(j + SB - 1);
+    }
+    // Fragment reads: rows wm*TM + rt*32 + lane%32 (A) and wn*TN + ct*32 +
+    // lane%32 (B) all have swz == swz(lane % 32).
     int koff[KC / 16];
 #pragma unroll
     for (int ks = 0; ks < KC / 16; ++ks) koff[ks] = (((ks * 2 + (lane >> 5)) ^ swz(lane & 31)) * 16);
     const int a_rd = (wm * TM + (lane & 31)) * kRow;
-    const int b_rd = (BM + wn * TN + (lane & 31)) * kRow;
+    const int b_rd = (wn * TN + (lane & 31)) * kRow;
+    constexpr int KS = KC / 16;
+    auto mfmas = [&](const u32x4 (&af)[RT], u32x4 (&bfr)[CT]) __attribute__((always_inline)) {
+      if constexpr (kF16) {
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-      if (s < nk) issue(s);
-    for (int kc = 0; kc < nk; ++kc) {
-      if (kc + S - 2 < nk) wait_vmem<(S - 2) * NL>();
-      else wait_vmem<0>();
-      stage_barrier();   // stage kc is in LDS for every wave; stage kc-1 is free
-      const uint8_t* st = lds + (kc % S) * kStage;
-      // All fragments of the stage first, then its MFMAs.
-      constexpr int KS = KC / 16;
-      u32x4 af[KS][RT], bfr[KS][CT];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int i = 0; i < RT; ++i)
-          af[ks][i] = *reinterpret_cast<const u32x4*>(st + a_rd + i * 32 * kRow + koff[ks]);
-#pragma unroll
-        for (int j = 0; j < CT; ++j)
-          bfr[ks][j] = *reinterpret_cast<const u32x4*>(st + b_rd + j * 32 * kRow + koff[ks]);
+        for (int j = 0; j < CT; ++j) bfr[j] = bf16x8_to_f16x8(bfr[j]);
       }
-      // The next stage's loads go out while the fragment reads are in flight
-      // (its buffer was last read in step kc - 1, before the barrier).
-      if (kc + S - 1 < nk) issue(kc + S - 1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (kF16) {
+      for (int i = 0; i < RT; ++i) {
+        if (i >= rt_n) continue;
 #pragma unroll
-          for (int j = 0; j < CT; ++j) bfr[ks][j] = bf16x8_to_f16x8(bfr[ks][j]);
+        for (int j = 0; j < CT; ++j) {
+          if constexpr (kF16) acc[i][j] = mfma_f16(af[i], bfr[j], acc[i][j]);
+          else acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
         }
+      }
+    };
+    for (int kc = 0; kc < nk; ++kc) {
+      if (kc + SB - 2 < nk) wait_vmem<kWaitN>();
+      else wait_vmem<0>();
+      stage_barrier();   // chunk kc is in LDS for every wave; the slots of chunk kc - 1 are free
+      const uint8_t* sa = lds + (kc % SA) * kStageA;
+      const uint8_t* sb = ldsB + (kc % SB) * kStageB;
+      if constexpr (SA == SB) {
+        // All fragments of the chunk first, then the next chunks' loads
+        // (issued while the fragment reads are in flight), then the MFMAs.
+        u32x4 af[KS][RT], bfr[KS][CT];
 #pragma unroll
-        for (int i = 0; i < RT; ++i) {
-          if (i >= rt_n) continue;
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-          for (int j = 0; j < CT; ++j) {
-            if constexpr (kF16) acc[i][j] = mfma_f16(af[ks][i], bfr[ks][j], acc[i][j]);
-            else acc[i][j] = mfma_bf16(af[ks][i], bfr[ks][j], acc[i][j]);
-          }
+          for (int i = 0; i < RT; ++i)
+            af[ks][i] = *reinterpret_cast<const u32x4*>(sa + a_rd + i * 32 * kRow + koff[ks]);
+#pragma unroll
+          for (int j = 0; j < CT; ++j)
+            bfr[ks][j] = *reinterpret_cast<const u32x4*>(sb + b_rd + j * 32 * kRow + koff[ks]);
+        }
+        if (kc + SA - 1 < nk) issue_a(kc + SA - 1);
+        if (kc + SB - 1 < nk) issue_b(kc + SB - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) mfmas(af[ks], bfr[ks]);
+      } else {
+        // Deeper B ring (128-byte K chunks): the next chunks' loads first,
+        // then each 16-wide K step's fragments and MFMAs.
+        if (kc + SA - 1 < nk) issue_a(kc + SA - 1);
+        if (kc + SB - 1 < nk) issue_b(kc + SB - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 af[RT], bfr[CT];
+#pragma unroll
+          for (int i = 0; i < RT; ++i)
+            af[i] = *reinterpret_cast<const u32x4*>(sa + a_rd + i * 32 * kRow + koff[ks]);
+#pragma unroll
+          for (int j = 0; j < CT; ++j)
+            bfr[j] = *reinterpret_cast<const u32x4*>(sb + b_rd + j * 32 * kRow + koff[ks]);
+          mfmas(af, bfr);
         }
       }
     }
@@ -287,7 +319,7 @@ __device__ __forceinline__ float unord_f32(uint32_t k) {
 // 32 tokens per block (256 blocks at T = 8192, one per CU) with 128-byte K
 // chunks: the router matrix is small and shared by every block, so the
 // GEMM is bound by each block's latency per K step, not by bytes.
-using RouterGemm = BlockGemm<kMT, kMaxExperts, 1, 4, false, 3, 64>;
+using RouterGemm = BlockGemm<kMT, kMaxExperts, 1, 4, false, 3, 3, 64>;
 // RMSNorm rows: n = bf16(r / rms(r) * gamma), one wave per token; lane l
 // owns the 16-byte vectors l, l + 64, l + 128, l + 192 of the row.
 constexpr int kNormVecPerLane = H / 8 / 64;   // 4
@@ -581,7 +613,7 @@ __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(LayerArg
 // acc[.][ct] with acc[.][ct + 2] in registers.  The 256-slot M-tile stages a
 // third fewer operand bytes per MFMA than a 128-slot one at the same waves
 // per SIMD (one 96 KiB block per CU).
-using GateUpGemm = BlockGemm<kGM, 256, 4, 2, false, 3, 32>;
+using GateUpGemm = BlockGemm<kGM, 256, 4, 2, false, 2, 3, 64>;
 constexpr int kGuColBlocks = I / 128;   // 4
 
 __global__ __launch_bounds__(GateUpGemm::kBlockThreads, 1) void prefill_gateup_kernel(LayerArgs a,
@@ -655,7 +687,7 @@ __global__ __launch_bounds__(GateUpGemm::kBlockThreads, 1) void prefill_gateup_k
 
 // Block tile: 256 slots x 256 output columns, eight waves; wave (wm, wn)
 // owns slots [64 wm, +64) x columns [128 wn, +128).
-using DownGemm = BlockGemm<kGM, 256, 4, 2, true, 3, 32>;
+using DownGemm = BlockGemm<kGM, 256, 4, 2, true, 3, 3, 32>;
 constexpr int kDnColBlocks = H / 256;   // 8
 // Epilogue: each half of the fp16 y tile (128 slots x 256 columns) is
 // parked row-major in LDS and stored as 16-byte vectors.
