@@ -29,12 +29,15 @@
 //                rank order (+ r for the block) and rounds once to bf16.
 // All GEMMs share one block-level scheme (BlockGemm): A and B tiles move
 // from global memory straight into LDS (LDS-direct loads, no register
-// staging) 32 K-elements at a time through a three-stage ring, so two
-// stages' loads are in flight while the third feeds the matrix cores;
-// 64-byte LDS rows with their 16-byte chunks XOR-swizzled by row, so that
-// the fragment reads of consecutive rows hit distinct banks.  The grouped
-// GEMMs run 256 x 256 block tiles on eight waves of 64 x 128 (32x32x16
-// MFMAs); the router 32 x 256 on four waves of 32 x 64.
+// staging) through one ring per operand, with rows' 16-byte chunks
+// XOR-swizzled so that the fragment reads of consecutive rows hit distinct
+// banks.  The ring depths and K chunk per GEMM: gate/up 128-byte chunks (64
+// K-elements) with two stages for the gathered x rows (L2-resident) and
+// three for the weights (from HBM), 160 KiB; the routed and dense down GEMMs
+// 64-byte chunks with two stages of h and four of w2; the router and the
+// shared-expert down + combine three and three of 64 (router: 128) bytes.
+// The grouped GEMMs run 256 x 256 block tiles on eight waves of 64 x 128
+// (32x32x16 MFMAs); the router 32 x 256 on four waves of 32 x 64.
 // Numerics: fp32 accumulation everywhere.  h and y cross the launches as
 // fp16 (11-bit significand) carrying a power-of-two bias: h is stored as
 // fp16(h * 2^-8), so the down GEMMs produce y * 2^-8, which the routed down
@@ -689,14 +692,21 @@ __global__ __launch_bounds__(GateUpGemm::kBlockThreads, 1) void prefill_gateup_k
 // owns slots [64 wm, +64) x columns [128 wn, +128).
 using DownGemm = BlockGemm<kGM, 256, 4, 2, true, 3, 3, 32>;
 constexpr int kDnColBlocks = H / 256;   // 8
+// The routed down GEMM and the dense MLP's down GEMM stream their w2 rows
+// through a four-deep ring (h, from L2, through a two-deep one): routed down
+// 237.8 -> 228 us, dense down (I_d 14336) 756 -> 664 us at T = 8192, against
+// three and three.  The combine's shared-expert GEMM keeps three and three
+// (65 -> 71 us with four).
+using DownGemmB4 = BlockGemm<kGM, 256, 4, 2, true, 2, 4, 32>;
 // Epilogue: each half of the fp16 y tile (128 slots x 256 columns) is
 // parked row-major in LDS and stored as 16-byte vectors.
 constexpr int kYRow = 256 + 8;          // halves per LDS row of the parked tile
 static_assert(kGM * kYRow <= DownGemm::kLds, "half a y tile fits the GEMM's LDS");
+static_assert(kGM * kYRow <= DownGemmB4::kLds, "half a y tile fits the routed down GEMM's LDS");
 static_assert(kGM * kMaxTopK % DownGemm::kBlockThreads == 0, "slot positions per thread");
 
-__global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_down_kernel(LayerArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemm::kLds];
+__global__ __launch_bounds__(DownGemmB4::kBlockThreads, 1) void prefill_down_kernel(LayerArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemmB4::kLds];
   const PrefillWs& p = a.ws.pre;
   const int n_items = p.tiles[0] * kDnColBlocks;
   const int item = xcd_item(n_items);
@@ -708,36 +718,36 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_down_kerne
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.routed.w2) + (size_t)tl[0] * H * I;
   const int start = tl[1], count = tl[2];
   const uint16_t* h16 = reinterpret_cast<const uint16_t*>(p.h16);
-  const uint16_t* ag[DownGemm::NA];
-  const uint16_t* bg[DownGemm::NB];
+  const uint16_t* ag[DownGemmB4::NA];
+  const uint16_t* bg[DownGemmB4::NB];
 #pragma unroll
-  for (int i = 0; i < DownGemm::NA; ++i) {
-    const int fr = DownGemm::fetch_row_a(i);
-    ag[i] = h16 + (size_t)(start + min(fr, count - 1)) * I + DownGemm::chunk_elems(fr);
+  for (int i = 0; i < DownGemmB4::NA; ++i) {
+    const int fr = DownGemmB4::fetch_row_a(i);
+    ag[i] = h16 + (size_t)(start + min(fr, count - 1)) * I + DownGemmB4::chunk_elems(fr);
   }
 #pragma unroll
-  for (int i = 0; i < DownGemm::NB; ++i) {
-    const int n = DownGemm::fetch_row_b(i);
-    bg[i] = W + (size_t)(nb * 256 + n) * I + DownGemm::chunk_elems(n);
+  for (int i = 0; i < DownGemmB4::NB; ++i) {
+    const int n = DownGemmB4::fetch_row_b(i);
+    bg[i] = W + (size_t)(nb * 256 + n) * I + DownGemmB4::chunk_elems(n);
   }
-  const int rt_n = max(0, min(DownGemm::RT, (count - wm * DownGemm::TM + 31) / 32));
-  DownGemm g;
+  const int rt_n = max(0, min(DownGemmB4::RT, (count - wm * DownGemmB4::TM + 31) / 32));
+  DownGemmB4 g;
   g.run(lds, ag, bg, I, rt_n);   // LDS is free afterwards
   _Float16* ys = reinterpret_cast<_Float16*>(lds);
   constexpr int kHalf = kGM / 2;
   for (int half = 0; half < 2; ++half) {
-    if (wm / (DownGemm::kWM / 2) == half) {
+    if (wm / (DownGemmB4::kWM / 2) == half) {
 #pragma unroll
-      for (int rt = 0; rt < DownGemm::RT; ++rt)
+      for (int rt = 0; rt < DownGemmB4::RT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < DownGemm::CT; ++ct)
+        for (int ct = 0; ct < DownGemmB4::CT; ++ct)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            ys[(wm * DownGemm::TM - half * kHalf + rt * 32 + acc_row(r, lane)) * kYRow + wn * DownGemm::TN +
+            ys[(wm * DownGemmB4::TM - half * kHalf + rt * 32 + acc_row(r, lane)) * kYRow + wn * DownGemmB4::TN +
                ct * 32 + (lane & 31)] = (_Float16)g.acc[rt][ct][r];
     }
     __syncthreads();
-    for (int u = tid; u < kHalf * 32; u += DownGemm::kBlockThreads) {
+    for (int u = tid; u < kHalf * 32; u += DownGemmB4::kBlockThreads) {
       const int row = half * kHalf + (u >> 5), c8 = (u & 31) * 8;
       if (row < count)
         *reinterpret_cast<u32x4*>(p.y16 + (size_t)(start + row) * H + nb * 256 + c8) =
@@ -934,8 +944,8 @@ __global__ __launch_bounds__(GateUpGemm::kBlockThreads, 1) void dense_gateup_gem
 // Down GEMM of the dense MLP: tile (128 tokens, 256 output columns), h fp16
 // times w2 (widened to fp16 into LDS), K = I_d; epilogue adds r for the
 // pre-norm block and rounds once to bf16.
-__global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void dense_down_gemm_kernel(DenseArgs a, int n_items) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemm::kLds];
+__global__ __launch_bounds__(DownGemmB4::kBlockThreads, 1) void dense_down_gemm_kernel(DenseArgs a, int n_items) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemmB4::kLds];
   const int item = xcd_item(n_items);
   if (item >= n_items) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -943,30 +953,30 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void dense_down_gemm_ke
   const int q = item / kDnColBlocks, nb = item % kDnColBlocks;
   const int start = q * kGM, count = min(kGM, a.T - start);
   const uint16_t* h16 = reinterpret_cast<const uint16_t*>(a.h16);
-  const uint16_t* ag[DownGemm::NA];
-  const uint16_t* bg[DownGemm::NB];
+  const uint16_t* ag[DownGemmB4::NA];
+  const uint16_t* bg[DownGemmB4::NB];
 #pragma unroll
-  for (int i = 0; i < DownGemm::NA; ++i) {
-    const int fr = DownGemm::fetch_row_a(i);
-    ag[i] = h16 + (size_t)(start + min(fr, count - 1)) * a.inter + DownGemm::chunk_elems(fr);
+  for (int i = 0; i < DownGemmB4::NA; ++i) {
+    const int fr = DownGemmB4::fetch_row_a(i);
+    ag[i] = h16 + (size_t)(start + min(fr, count - 1)) * a.inter + DownGemmB4::chunk_elems(fr);
   }
 #pragma unroll
-  for (int i = 0; i < DownGemm::NB; ++i) {
-    const int n = DownGemm::fetch_row_b(i);
-    bg[i] = a.w2 + (size_t)(nb * 256 + n) * a.inter + DownGemm::chunk_elems(n);
+  for (int i = 0; i < DownGemmB4::NB; ++i) {
+    const int n = DownGemmB4::fetch_row_b(i);
+    bg[i] = a.w2 + (size_t)(nb * 256 + n) * a.inter + DownGemmB4::chunk_elems(n);
   }
-  const int rt_n = max(0, min(DownGemm::RT, (count - wm * DownGemm::TM + 31) / 32));
-  DownGemm g;
+  const int rt_n = max(0, min(DownGemmB4::RT, (count - wm * DownGemmB4::TM + 31) / 32));
+  DownGemmB4 g;
   g.run(lds, ag, bg, a.inter, rt_n);
 #pragma unroll
-  for (int rt = 0; rt < DownGemm::RT; ++rt)
+  for (int rt = 0; rt < DownGemmB4::RT; ++rt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = wm * DownGemm::TM + rt * 32 + acc_row(r, lane);
+      const int row = wm * DownGemmB4::TM + rt * 32 + acc_row(r, lane);
       if (row < count) {
 #pragma unroll
-        for (int ct = 0; ct < DownGemm::CT; ++ct) {
-          const int col = nb * 256 + wn * DownGemm::TN + ct * 32 + (lane & 31);
+        for (int ct = 0; ct < DownGemmB4::CT; ++ct) {
+          const int col = nb * 256 + wn * DownGemmB4::TN + ct * 32 + (lane & 31);
           const size_t idx = (size_t)(start + row) * H + col;
           float o = g.acc[rt][ct][r] * kH16Unbias;
           if (a.resid) o += bf16_lo(a.resid[idx]);
@@ -983,7 +993,7 @@ hipError_t launch_dense_prefill(const DenseArgs& a, hipStream_t stream, Launcher
   const int n_gu = n_tiles * (a.inter / 128);
   launch(dense_gateup_gemm_kernel, dim3(round8(n_gu)), dim3(GateUpGemm::kBlockThreads), stream, a, n_gu);
   const int n_dn = n_tiles * kDnColBlocks;
-  launch(dense_down_gemm_kernel, dim3(round8(n_dn)), dim3(DownGemm::kBlockThreads), stream, a, n_dn);
+  launch(dense_down_gemm_kernel, dim3(round8(n_dn)), dim3(DownGemmB4::kBlockThreads), stream, a, n_dn);
   return hipGetLastError();
 }
 
