@@ -376,7 +376,8 @@ __device__ void rank_rows(const LayerArgs& a, const float* zs, int t0, int i0, i
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      key[g][q] = (e < E && t0 + i < T) ? ord_f32(zs[i * kZRow + e]) : 0u;
+      const uint32_t kz = ord_f32(zs[i * kZRow + e]);
+      key[g][q] = (e < E && t0 + i < T) ? kz : 0u;
       ex[g][q] = e;
     }
     auto cx = [&](int u, int v) __attribute__((always_inline)) {
@@ -394,6 +395,8 @@ __device__ void rank_rows(const LayerArgs& a, const float* zs, int t0, int i0, i
     cx(1, 3);
     cx(1, 2);
   }
+  // Rounds unrolled to the largest k (uniform exit at k): the pops and the
+  // picks are selects, not branches.
   int my_e[G];
   uint32_t my_key[G];
 #pragma unroll
@@ -401,8 +404,9 @@ __device__ void rank_rows(const LayerArgs& a, const float* zs, int t0, int i0, i
     my_e[g] = 0;
     my_key[g] = 0;
   }
-#pragma unroll 1
-  for (int j = 0; j < k; ++j) {
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= k) break;
     uint32_t m[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) m[g] = key[g][0];
@@ -412,26 +416,23 @@ __device__ void rank_rows(const LayerArgs& a, const float* zs, int t0, int i0, i
       const uint32_t M = (uint32_t)__builtin_amdgcn_readlane((int)m[g], 63);
       const int win = (int)__builtin_ctzll(__ballot(key[g][0] == M));
       const int best = __builtin_amdgcn_readlane(ex[g][0], win);
-      if (lane == win) {
-        key[g][0] = key[g][1];
-        key[g][1] = key[g][2];
-        key[g][2] = key[g][3];
-        key[g][3] = 0u;
-        ex[g][0] = ex[g][1];
-        ex[g][1] = ex[g][2];
-        ex[g][2] = ex[g][3];
-      }
-      if (lane == j) {
-        my_e[g] = best;
-        my_key[g] = M;
-      }
+      const bool pop = lane == win;
+      key[g][0] = pop ? key[g][1] : key[g][0];
+      key[g][1] = pop ? key[g][2] : key[g][1];
+      key[g][2] = pop ? key[g][3] : key[g][2];
+      key[g][3] = pop ? 0u : key[g][3];
+      ex[g][0] = pop ? ex[g][1] : ex[g][0];
+      ex[g][1] = pop ? ex[g][2] : ex[g][1];
+      ex[g][2] = pop ? ex[g][3] : ex[g][2];
+      my_e[g] = lane == j ? best : my_e[g];
+      my_key[g] = lane == j ? M : my_key[g];
     }
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int t = t0 + i0 + g * di;
     const float sc = lane < k ? sigmoid(unord_f32(my_key[g])) : 0.f;
-    const float sum = __shfl(wave_sum_lane63(sc), 63);
+    const float sum = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_lane63(sc)), 63));
     if (t < T && lane < k) {
       const float w = (a.renormalize ? sc / sum : sc) * a.routed_scale;
       a.ws.ids[t * k + lane] = my_e[g];
@@ -763,10 +764,13 @@ __global__ __launch_bounds__(DownGemmB4::kBlockThreads, 1) void prefill_down_ker
 // GEMM.  Epilogue in four parts of 64 tokens: the owning waves park their
 // accumulators in LDS, then every thread finishes 8 consecutive columns of a
 // token at a time: out = shared + sum_j w_j y_j in rank order, one bf16
-// rounding, 16-byte loads of y and stores of out.
+// rounding, 16-byte loads of y and stores of out.  KT is the number of y
+// loads per unit (6 for k <= 6, else 8), fixed so that the next unit's loads
+// can be in flight under exact wait counts.
 constexpr int kCbRow = 256 + 4;   // floats per LDS row of the parked tile
 constexpr int kCbLds = cmax(DownGemm::kLds, DownGemm::TM * kCbRow * 4);
 
+template <int KT>
 __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_combine_kernel(LayerArgs a,
                                                                                          int n_items) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kCbLds];
@@ -821,6 +825,31 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_com
   }
 
   float* park = reinterpret_cast<float*>(lds);
+  // Thread tid's combine units: 64 tokens x 32 groups of 8 columns per part,
+  // kUnits per thread; unit it + 1's y rows are requested before unit it is
+  // summed (every unit issues KT loads, ranks past k re-read rank k - 1 and
+  // rows past count row count - 1, so the wait counts stay exact).
+  constexpr int kUnits = DownGemm::TM * 32 / DownGemm::kBlockThreads;
+  constexpr int kIters = DownGemm::kWM * kUnits;
+  u32x4 yv[2][KT];
+  float wj[2][KT];
+  u32x4 rr[2];
+  auto load_unit = [&](int it, int buf) __attribute__((always_inline)) {
+    const int part = it / kUnits, s = it % kUnits;
+    const int u = tid + s * DownGemm::kBlockThreads;
+    const int row = u >> 5, c8 = (u & 31) * 8;
+    const int lrow = min(part * DownGemm::TM + row, count - 1);
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int jj = min(j, k - 1);
+      wj[buf][j] = s_w[lrow * k + jj];
+      yv[buf][j] = *reinterpret_cast<const u32x4*>(p.y16 + (size_t)s_pos[lrow * k + jj] * H + nb * 256 + c8);
+    }
+    if (a.resid) rr[buf] = *reinterpret_cast<const u32x4*>(a.resid + (size_t)(t0 + lrow) * H + nb * 256 + c8);
+  };
+  __syncthreads();   // s_pos and s_w
+  load_unit(0, 0);
+#pragma unroll
   for (int part = 0; part < DownGemm::kWM; ++part) {
     if (wm == part) {
 #pragma unroll
@@ -833,31 +862,22 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_com
                 g.acc[rt][ct][r];
     }
     __syncthreads();
-    // 64 tokens x 32 groups of 8 columns = 2048 units, four per thread.
-    for (int u = tid; u < DownGemm::TM * 32; u += DownGemm::kBlockThreads) {
+#pragma unroll
+    for (int s = 0; s < kUnits; ++s) {
+      const int it = part * kUnits + s;
+      if (it + 1 < kIters) load_unit(it + 1, (it + 1) & 1);
+      const int buf = it & 1;
+      const int u = tid + s * DownGemm::kBlockThreads;
       const int row = u >> 5, c8 = (u & 31) * 8;
       const int lrow = part * DownGemm::TM + row;
-      if (lrow >= count) continue;
-      const int t = t0 + lrow;
       const f32x4 s0 = *reinterpret_cast<const f32x4*>(park + row * kCbRow + c8);
       const f32x4 s1 = *reinterpret_cast<const f32x4*>(park + row * kCbRow + c8 + 4);
       float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      // Every rank's y and weight requested before the first is used (the
-      // loads are independent); then added in rank order.
-      u32x4 yv[kMaxTopK];
-      float wj[kMaxTopK];
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
+      for (int j = 0; j < KT; ++j) {
         if (j < k) {
-          wj[j] = s_w[lrow * k + j];
-          yv[j] = *reinterpret_cast<const u32x4*>(p.y16 + (size_t)s_pos[lrow * k + j] * H + nb * 256 + c8);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k) {
-          const float w = wj[j];
-          const u32x4 y = yv[j];
+          const float w = wj[buf][j];
+          const u32x4 y = yv[buf][j];
           o[0] = fmaf(w, f16_lo(y.x), o[0]);
           o[1] = fmaf(w, f16_hi(y.x), o[1]);
           o[2] = fmaf(w, f16_lo(y.y), o[2]);
@@ -868,29 +888,36 @@ __global__ __launch_bounds__(DownGemm::kBlockThreads, 1) void prefill_shared_com
           o[7] = fmaf(w, f16_hi(y.w), o[7]);
         }
       }
+      if (lrow < count) {
+        const int t = t0 + lrow;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] *= kH16Unbias;   // shared + weighted routed y, unbiased
-      if (a.resid) {
-        const u32x4 rr = *reinterpret_cast<const u32x4*>(a.resid + (size_t)t * H + nb * 256 + c8);
-        o[0] += bf16_lo(rr.x);
-        o[1] += bf16_hi(rr.x);
-        o[2] += bf16_lo(rr.y);
-        o[3] += bf16_hi(rr.y);
-        o[4] += bf16_lo(rr.z);
-        o[5] += bf16_hi(rr.z);
-        o[6] += bf16_lo(rr.w);
-        o[7] += bf16_hi(rr.w);
+        for (int c = 0; c < 8; ++c) o[c] *= kH16Unbias;   // shared + weighted routed y, unbiased
+        if (a.resid) {
+          const u32x4 r = rr[buf];
+          o[0] += bf16_lo(r.x);
+          o[1] += bf16_hi(r.x);
+          o[2] += bf16_lo(r.y);
+          o[3] += bf16_hi(r.y);
+          o[4] += bf16_lo(r.z);
+          o[5] += bf16_hi(r.z);
+          o[6] += bf16_lo(r.w);
+          o[7] += bf16_hi(r.w);
+        }
+        u32x4 ob;
+        ob.x = pack_bf16x2_rne(o[0], o[1]);
+        ob.y = pack_bf16x2_rne(o[2], o[3]);
+        ob.z = pack_bf16x2_rne(o[4], o[5]);
+        ob.w = pack_bf16x2_rne(o[6], o[7]);
+        *reinterpret_cast<u32x4*>(a.out + (size_t)t * H + nb * 256 + c8) = ob;
       }
-      u32x4 ob;
-      ob.x = pack_bf16x2_rne(o[0], o[1]);
-      ob.y = pack_bf16x2_rne(o[2], o[3]);
-      ob.z = pack_bf16x2_rne(o[4], o[5]);
-      ob.w = pack_bf16x2_rne(o[6], o[7]);
-      *reinterpret_cast<u32x4*>(a.out + (size_t)t * H + nb * 256 + c8) = ob;
     }
     __syncthreads();
   }
 }
+// Both instances explicitly: with only the launch sites, the compiler left
+// the second one's host handle undefined.
+template __global__ void prefill_shared_combine_kernel<6>(LayerArgs, int);
+template __global__ void prefill_shared_combine_kernel<8>(LayerArgs, int);
 
 // ---------------------------------------------------------------- dense MLP
 
@@ -1021,7 +1048,10 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& laun
   const int n_dn = n_routed_max * kDnColBlocks;
   launch(prefill_down_kernel, dim3(round8(n_dn)), dim3(DownGemm::kBlockThreads), stream, a);
   const int n_sc = n_shared * kDnColBlocks;
-  launch(prefill_shared_combine_kernel, dim3(round8(n_sc)), dim3(DownGemm::kBlockThreads), stream, a, n_sc);
+  if (a.k <= 6)
+    launch(prefill_shared_combine_kernel<6>, dim3(round8(n_sc)), dim3(DownGemm::kBlockThreads), stream, a, n_sc);
+  else
+    launch(prefill_shared_combine_kernel<8>, dim3(round8(n_sc)), dim3(DownGemm::kBlockThreads), stream, a, n_sc);
   return hipGetLastError();
 }
 
