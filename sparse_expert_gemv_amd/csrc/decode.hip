@@ -991,6 +991,8 @@ void gateup_kernel(LayerArgs a) {
 
 // The low-latency path's next-layer norm at the end of the down launch.
 __device__ void next_norm_tail(const LayerArgs& a);
+__device__ __forceinline__ void down_combine(const LayerArgs& a, const float* part, const float* s_wts,
+                                             int r0);
 
 // Down + combine.  Block b owns output rows [8b, 8b + 8) of every token and
 // walks the |U| active experts and then the shared expert; wave w takes
@@ -1371,6 +1373,16 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
     }
   }
   __syncthreads();
+  down_combine(a, part, s_wts, r0);
+}
+
+// The combine of a down block (rows [r0, r0 + 8)), once every (h row, output
+// row) partial is in part: out = shared + sum_j w_j * routed_j in rank order,
+// the residual added, one bf16 rounding; with a next-layer norm, the row
+// pairs and the token's partial sum of squares are stored for its tail.
+__device__ __forceinline__ void down_combine(const LayerArgs& a, const float* part, const float* s_wts,
+                                             int r0) {
+  const int T = a.T, k = a.k;
   const bool next_norm = a.norm_next_w != nullptr;
   static_assert(kDecodeMaxT * kDownRowsPerBlock <= kDownThreads, "one (token, row) per thread");
   if ((int)threadIdx.x < T * kDownRowsPerBlock) {
@@ -1401,6 +1413,182 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(LayerArgs a) {
   }
   if (next_norm) next_norm_tail(a);
 }
+
+// NVFP4 down + combine for small batches (2 <= T <= kDnSmallMaxT): the same
+// row-owner blocks (block b: output rows [8b, 8b + 8)) as down_kernel, laid
+// out so that all of a wave's loads are in flight together and every wait
+// is exact.  Each wave reads its share of the routing table into registers
+// (lane s: its s-th active expert), then the h rows it stages for the block
+// (bf16, 1 KiB each; T k + T of them) and the shared expert's rows; once the
+// table has arrived it requests all kS of its experts' codes (wave w:
+// active experts w, w + 8, ...; an entry covers all of the expert's slots),
+// parks the h rows in LDS and reduces the shared expert's token w and then
+// each expert as its codes land.  Every wave issues the same loads whatever
+// the batch (an index past the end repeats a valid one), and only ordinary
+// loads precede the waits (with an LDS-direct load in flight the compiler
+// waits for every load), so each wait leaves exactly the later loads in
+// flight; only reductions are skipped.
+constexpr int kDnSmallMaxT = 8;
+constexpr int kDnSmallHRows = kDnSmallMaxT * kMaxTopK + kDnSmallMaxT;   // 72 rows of 1 KiB
+constexpr int kDnSmallHVec = I / 8;                                     // 16-byte vectors per h row
+constexpr int kDnSmallHPerWave = (kDnSmallHRows + kDownWaves - 1) / kDownWaves;
+static_assert(kDnSmallHVec == kWave, "one h row per wave instruction");
+static_assert(kDnSmallMaxT * kMaxTopK <= kDownWaves * 8 && kDnSmallMaxT * kMaxTopK <= kWave,
+              "every active expert has a wave slot; every slot id a lane");
+
+// Experts per wave (kS) for a batch: the eight waves cover T k slots.
+__host__ __device__ constexpr int down_small_slots(int T, int k) { return T * k <= 6 * kDownWaves ? 6 : 8; }
+
+__host__ __device__ constexpr bool down_small_applies(int T, bool nvfp4) {
+  return nvfp4 && T >= 2 && T <= kDnSmallMaxT;
+}
+
+// One expert's tensor scale and its 8 rows of E2M1 codes and E4M3 block
+// scales in a lane (lane l: columns [32 c, 32 c + 32), c = l % 16, of rows
+// r0 + 4 i + l / 16).
+struct DnCodes {
+  float g;
+  u32x4 q[2];
+  uint16_t sc[2];
+  __device__ __forceinline__ void load(const Bank& bank, int e, int r0) {
+    g = bank.w2_gscale[e];
+    const uint8_t* w2 = bank.w2 + (size_t)e * H * (I / 2);
+    const uint8_t* s2 = bank.w2_scale + (size_t)e * H * (I / 16);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int c = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = r0 + 4 * i + (lane >> 4);
+      q[i] = load_stream(reinterpret_cast<const u32x4*>(w2 + (size_t)row * (I / 2)) + c);
+      sc[i] = load_stream(reinterpret_cast<const uint16_t*>(s2 + (size_t)row * (I / 16)) + c);
+    }
+  }
+};
+
+// The vector of bf16 h row `row` that LDS position `lane` of the row holds:
+// position 16 v + c takes vector 4 c + v, so that lane c's four reads
+// (columns [32 c, 32 c + 32)) are consecutive across the 16 lanes of a row
+// group.
+__device__ __forceinline__ u32x4 load_h_vec(const float* h, int row) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(h) + (size_t)row * I);
+  return src[4 * (lane & 15) + (lane >> 4)];
+}
+
+// The partials of one expert entry for h rows hrow(j), j < n: per row, the
+// two 16-column block sums scaled by their E4M3 scales, the 16 lanes of a
+// row group summed in a fixed butterfly, times the tensor scale.
+template <typename HRow>
+__device__ __forceinline__ void dn_small_rows(const DnCodes& p, float g, const u32x4* hs, int n, HRow hrow,
+                                              float* part) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane & 15;
+  u32x4 wv[2][4];
+  float s_lo[2], s_hi[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t cw[4] = {p.q[i].x, p.q[i].y, p.q[i].z, p.q[i].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      wv[i][w] = u32x4{fp4x2_to_bf16x2<0>(cw[w]), fp4x2_to_bf16x2<1>(cw[w]), fp4x2_to_bf16x2<2>(cw[w]),
+                       fp4x2_to_bf16x2<3>(cw[w])};
+    s_lo[i] = __builtin_amdgcn_cvt_f32_fp8((int)p.sc[i], 0);
+    s_hi[i] = __builtin_amdgcn_cvt_f32_fp8((int)p.sc[i], 1);
+  }
+  for (int j = 0; j < n; ++j) {
+    const int hr = hrow(j);
+    const u32x4* hp = hs + hr * kDnSmallHVec + c;
+    const u32x4 h0 = hp[0], h1 = hp[16], h2 = hp[32], h3 = hp[48];
+    float v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float lo = dot8_bf16(wv[i][1], h1, dot8_bf16(wv[i][0], h0, 0.f));
+      const float hi = dot8_bf16(wv[i][3], h3, dot8_bf16(wv[i][2], h2, 0.f));
+      v[i] = fmaf(hi, s_hi[i], lo * s_lo[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      v[i] += dpp<0xB1>(v[i]);    // lane ^ 1
+      v[i] += dpp<0x4E>(v[i]);    // lane ^ 2
+      v[i] += dpp<0x141>(v[i]);   // row_half_mirror: sums of 8
+      v[i] += dpp<0x140>(v[i]);   // row_mirror: sums of 16
+    }
+    if (c == 0) {
+      float* dst = part + hr * kDownRowsPerBlock + (lane >> 4);
+      dst[0] = v[0] * g;
+      dst[4] = v[1] * g;
+    }
+  }
+}
+
+template <int kS>
+__global__ __launch_bounds__(kDownThreads) void down_small_kernel(LayerArgs a) {
+  static_assert(kS < kWave, "a lane for the stand-in expert");
+  __shared__ u32x4 hs[kDnSmallHRows * kDnSmallHVec];   // 72 KiB
+  __shared__ float s_wts[kDnSmallMaxT * kMaxTopK];
+  __shared__ float part[kDnSmallHRows * kDownRowsPerBlock];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int r0 = blockIdx.x * kDownRowsPerBlock;
+  const int T = a.T, k = a.k, E = a.E;
+  const int nh = T * k + T;
+  const int32_t* route = a.ws.route;
+
+  // The scheduling fences keep this issue order: table, h rows, shared
+  // rows | experts, so that each wait leaves exactly the later loads in
+  // flight.
+  // 1. This wave's share of the routing table: lane s < kS the active index
+  // i = w + 8 s (expert, slot range), the other lanes the first active
+  // expert (the stand-in for indices past the end); lane l slot id l.
+  const int li = lane < kS ? wave + lane * kDownWaves : 0;
+  const int v_act = route[1 + min(li, E - 1)];
+  const int v_off0 = route[1 + E + min(li, E)];
+  const int v_off1 = route[1 + E + min(li + 1, E)];
+  const int v_slot = route[2 + 2 * E + min(lane, T * k - 1)];
+  const int v_n = route[0];
+  const float v_wt = a.ws.wts[min((int)threadIdx.x, T * k - 1)];
+  const float g_sh = a.shared.w2_gscale[0];
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. The h rows this wave parks (w, w + 8, ...; past nh the last row
+  // again, to its own place).
+  u32x4 hv[kDnSmallHPerWave];
+#pragma unroll
+  for (int i = 0; i < kDnSmallHPerWave; ++i) hv[i] = load_h_vec(a.ws.h, min(wave + i * kDownWaves, nh - 1));
+  // 3. The shared expert's rows (every wave: wave t reduces token t).
+  DnCodes sh;
+  sh.load(a.shared, 0, r0);
+  __builtin_amdgcn_sched_barrier(0);
+  const int n = __builtin_amdgcn_readfirstlane(v_n);
+  const int act0 = __builtin_amdgcn_readlane(v_act, kS);
+
+  // 4. All of this wave's experts, then the h rows into LDS as they land.
+  DnCodes pe[kS];
+#pragma unroll
+  for (int s = 0; s < kS; ++s)
+    pe[s].load(a.routed, wave + s * kDownWaves < n ? __builtin_amdgcn_readlane(v_act, s) : act0, r0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kDnSmallHPerWave; ++i)
+    hs[min(wave + i * kDownWaves, nh - 1) * kDnSmallHVec + lane] = hv[i];
+  s_wts[min((int)threadIdx.x, T * k - 1)] = v_wt;   // past the end: the last weight again
+  lds_barrier();
+  if (wave < T) dn_small_rows(sh, g_sh, hs, 1, [&](int) { return T * k + wave; }, part);
+#pragma unroll
+  for (int s = 0; s < kS; ++s) {
+    if (wave + s * kDownWaves < n) {
+      const int off = __builtin_amdgcn_readlane(v_off0, s);
+      const int cnt = __builtin_amdgcn_readlane(v_off1, s) - off;
+      dn_small_rows(pe[s], pe[s].g, hs, cnt, [&](int j) { return __builtin_amdgcn_readlane(v_slot, off + j); },
+                    part);
+    }
+  }
+  __syncthreads();
+  down_combine(a, part, s_wts, r0);
+}
+// Both instances explicitly: with only the launch sites, the compiler can
+// leave the second one's host handle undefined.
+template __global__ void down_small_kernel<6>(LayerArgs);
+template __global__ void down_small_kernel<8>(LayerArgs);
 
 // ---------------------------------------------------------------- low-latency decode path
 
@@ -1666,6 +1854,10 @@ static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Lau
   }
   if (a.T > kRouteBareMinT)
     launch(down_kernel<kFp4, true>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  else if (down_small_applies(a.T, kFp4) && down_small_slots(a.T, a.k) == 6)
+    launch(down_small_kernel<6>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  else if (down_small_applies(a.T, kFp4))
+    launch(down_small_kernel<8>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
   else
     launch(down_kernel<kFp4, false>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
   return hipGetLastError();
