@@ -670,21 +670,32 @@ __global__ __launch_bounds__(GateUpGemm::kBlockThreads, 1) void prefill_gateup_k
   GateUpGemm g;
   g.run(lds, ag, bg, H, rt_n);
 
-  _Float16* h16 = p.h16;
+  // The tile's h (256 slots x 128 columns, fp16) parked in LDS, then stored
+  // as 16-byte vectors.
+  constexpr int kHRow = 128 + 8;   // halves per LDS row
+  static_assert(kGM * kHRow * 2 <= GateUpGemm::kLds, "the h tile fits the ring's LDS");
+  _Float16* hs = reinterpret_cast<_Float16*>(lds);
 #pragma unroll
   for (int rt = 0; rt < GateUpGemm::RT; ++rt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = wm * GateUpGemm::TM + rt * 32 + acc_row(r, lane);
-      if (row < count) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int col = nb * 128 + wn * 64 + ct * 32 + (lane & 31);
-          const float gv = g.acc[rt][ct][r], uv = g.acc[rt][ct + 2][r];
-          h16[(size_t)(hrow0 + row) * I + col] = (_Float16)(silu(gv) * uv * kH16Bias);
-        }
+      for (int ct = 0; ct < 2; ++ct) {
+        const float gv = g.acc[rt][ct][r], uv = g.acc[rt][ct + 2][r];
+        hs[row * kHRow + wn * 64 + ct * 32 + (lane & 31)] = (_Float16)(silu(gv) * uv * kH16Bias);
       }
     }
+  __syncthreads();
+  _Float16* h16 = p.h16;
+#pragma unroll
+  for (int i = 0; i < kGM * 16 / GateUpGemm::kBlockThreads; ++i) {
+    const int u = tid + i * GateUpGemm::kBlockThreads;
+    const int row = u >> 4, c8 = (u & 15) * 8;
+    if (row < count)
+      *reinterpret_cast<u32x4*>(h16 + (size_t)(hrow0 + row) * I + nb * 128 + c8) =
+          *reinterpret_cast<const u32x4*>(hs + row * kHRow + c8);
+  }
 }
 
 // ---------------------------------------------------------------- 5. down (routed)
@@ -699,15 +710,15 @@ constexpr int kDnColBlocks = H / 256;   // 8
 // three and three.  The combine's shared-expert GEMM keeps three and three
 // (65 -> 71 us with four).
 using DownGemmB4 = BlockGemm<kGM, 256, 4, 2, true, 2, 4, 32>;
-// Epilogue: each half of the fp16 y tile (128 slots x 256 columns) is
-// parked row-major in LDS and stored as 16-byte vectors.
+// Epilogue: the fp16 y tile (256 slots x 256 columns) is parked row-major in
+// LDS by all eight waves at once and stored as 16-byte vectors (the block's
+// LDS is sized for it: 132 KiB; two halves through the ring's 96 KiB, one
+// half's waves parking while the others waited, measured 7 us slower).
 constexpr int kYRow = 256 + 8;          // halves per LDS row of the parked tile
-static_assert(kGM * kYRow <= DownGemm::kLds, "half a y tile fits the GEMM's LDS");
-static_assert(kGM * kYRow <= DownGemmB4::kLds, "half a y tile fits the routed down GEMM's LDS");
 static_assert(kGM * kMaxTopK % DownGemm::kBlockThreads == 0, "slot positions per thread");
 
 __global__ __launch_bounds__(DownGemmB4::kBlockThreads, 1) void prefill_down_kernel(LayerArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[DownGemmB4::kLds];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[cmax(DownGemmB4::kLds, kGM * kYRow * 2)];
   const PrefillWs& p = a.ws.pre;
   const int n_items = p.tiles[0] * kDnColBlocks;
   const int item = xcd_item(n_items);
@@ -734,27 +745,25 @@ __global__ __launch_bounds__(DownGemmB4::kBlockThreads, 1) void prefill_down_ker
   const int rt_n = max(0, min(DownGemmB4::RT, (count - wm * DownGemmB4::TM + 31) / 32));
   DownGemmB4 g;
   g.run(lds, ag, bg, I, rt_n);   // LDS is free afterwards
+  // The whole y tile (fp16) parked in LDS by every wave at once, then
+  // stored as 16-byte vectors.
   _Float16* ys = reinterpret_cast<_Float16*>(lds);
-  constexpr int kHalf = kGM / 2;
-  for (int half = 0; half < 2; ++half) {
-    if (wm / (DownGemmB4::kWM / 2) == half) {
 #pragma unroll
-      for (int rt = 0; rt < DownGemmB4::RT; ++rt)
+  for (int rt = 0; rt < DownGemmB4::RT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < DownGemmB4::CT; ++ct)
+    for (int ct = 0; ct < DownGemmB4::CT; ++ct)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            ys[(wm * DownGemmB4::TM - half * kHalf + rt * 32 + acc_row(r, lane)) * kYRow + wn * DownGemmB4::TN +
-               ct * 32 + (lane & 31)] = (_Float16)g.acc[rt][ct][r];
-    }
-    __syncthreads();
-    for (int u = tid; u < kHalf * 32; u += DownGemmB4::kBlockThreads) {
-      const int row = half * kHalf + (u >> 5), c8 = (u & 31) * 8;
-      if (row < count)
-        *reinterpret_cast<u32x4*>(p.y16 + (size_t)(start + row) * H + nb * 256 + c8) =
-            *reinterpret_cast<const u32x4*>(ys + (row - half * kHalf) * kYRow + c8);
-    }
-    __syncthreads();
+      for (int r = 0; r < 16; ++r)
+        ys[(wm * DownGemmB4::TM + rt * 32 + acc_row(r, lane)) * kYRow + wn * DownGemmB4::TN + ct * 32 +
+           (lane & 31)] = (_Float16)g.acc[rt][ct][r];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kGM * 32 / DownGemmB4::kBlockThreads; ++i) {
+    const int u = tid + i * DownGemmB4::kBlockThreads;
+    const int row = u >> 5, c8 = (u & 31) * 8;
+    if (row < count)
+      *reinterpret_cast<u32x4*>(p.y16 + (size_t)(start + row) * H + nb * 256 + c8) =
+          *reinterpret_cast<const u32x4*>(ys + row * kYRow + c8);
   }
 }
 
