@@ -90,7 +90,10 @@ __device__ __forceinline__ u32x4 rms_scale_bf16x8(const u32x4& x, const u32x4& g
   return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigma(g), with the hardware reciprocal (about 1 ulp) in place
+// of an IEEE division: a tenth of the instructions, which the prefill gate/up
+// epilogue (64 of them per thread and tile) feels: 320 -> 312 us.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
