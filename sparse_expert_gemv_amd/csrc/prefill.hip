@@ -288,6 +288,14 @@ struct BlockGemm {
     }
     __syncthreads();
   }
+
+  // For a block's waves past the NW that run the GEMM: the same barriers
+  // as run(), nothing else.
+  __device__ __forceinline__ void shadow(int K) {
+    const int nk = K / KC;
+    for (int kc = 0; kc < nk; ++kc) stage_barrier();
+    __syncthreads();
+  }
 };
 
 // Block -> work item, XCD-aware: the hardware deals blocks to the 8 XCDs
@@ -444,13 +452,19 @@ __device__ void rank_rows(const LayerArgs& a, const float* zs, int t0, int i0, i
   }
 }
 
-__global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
+// Eight waves: the first four run the GEMM (the others only keep its
+// barriers), then all eight rank the tile's rows, two waves per SIMD
+// instead of one (the ranking is a chain of dependent wave reductions).
+constexpr int kRouterThreads = 2 * RouterGemm::kBlockThreads;
+
+__global__ __launch_bounds__(kRouterThreads) void prefill_router_kernel(LayerArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[cmax(RouterGemm::kLds, kMT * kZRow * 4)];
   __shared__ int hist[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, k = a.k;
   const int t0 = blockIdx.x * kMT;
-  for (int i = tid; i < kMaxExperts; i += kThreads) hist[i] = 0;
+  for (int i = tid; i < kMaxExperts; i += kRouterThreads) hist[i] = 0;
+  const bool gemm = wave < RouterGemm::NW;
 
   // logits[t0 .. t0+64) x [0, 256): token rows clamped to T-1, experts to E-1.
   const uint16_t* ag[RouterGemm::NA];
@@ -466,29 +480,31 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(LayerArgs a) {
     bg[i] = a.router_w + (size_t)min(r, E - 1) * H + RouterGemm::chunk_elems(r);
   }
   RouterGemm g;
-  g.run(lds, ag, bg, H, RouterGemm::RT);   // LDS is free afterwards
-
   float* zs = reinterpret_cast<float*>(lds);
+  if (gemm) {
+    g.run(lds, ag, bg, H, RouterGemm::RT);   // LDS is free afterwards
 #pragma unroll
-  for (int rt = 0; rt < RouterGemm::RT; ++rt)
+    for (int rt = 0; rt < RouterGemm::RT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < RouterGemm::CT; ++ct) {
-      const int e = wave * RouterGemm::TN + ct * 32 + (lane & 31);
-      const float b = (a.router_b && e < E) ? a.router_b[e] : 0.f;
+      for (int ct = 0; ct < RouterGemm::CT; ++ct) {
+        const int e = wave * RouterGemm::TN + ct * 32 + (lane & 31);
+        const float b = (a.router_b && e < E) ? a.router_b[e] : 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) zs[(rt * 32 + acc_row(r, lane)) * kZRow + e] = g.acc[rt][ct][r] + b;
-    }
+        for (int r = 0; r < 16; ++r) zs[(rt * 32 + acc_row(r, lane)) * kZRow + e] = g.acc[rt][ct][r] + b;
+      }
+  } else {
+    g.shadow(H);
+  }
   __syncthreads();
   if (tid < E)
     for (int i = 0; i < kMT && t0 + i < T; ++i) a.ws.logits[(size_t)(t0 + i) * E + tid] = zs[i * kZRow + tid];
 
-  // Top-k: wave w ranks tile rows w, w + 4, ..., four at a time (rank_rows).
-  static_assert(kMT % (4 * kThreads / 64) == 0, "whole groups of four rows per wave");
-#pragma unroll 1
-  for (int i0 = wave; i0 < kMT; i0 += 4 * (kThreads / 64))
-    rank_rows<4>(a, zs, t0, i0, kThreads / 64, hist);
+  // Top-k: wave w ranks tile rows w, w + 8, w + 16, w + 24 (rank_rows).
+  constexpr int kRW = kRouterThreads / 64;
+  static_assert(kMT == 4 * kRW, "four rows per wave");
+  rank_rows<4>(a, zs, t0, wave, kRW, hist);
   __syncthreads();
-  for (int e = tid; e < E; e += kThreads) a.ws.pre.counts[(size_t)blockIdx.x * E + e] = hist[e];
+  for (int e = tid; e < E; e += kRouterThreads) a.ws.pre.counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
 // ---------------------------------------------------------------- 2. bucketing
@@ -1048,7 +1064,7 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream, Launcher& laun
   const int n_routed_max = prefill_tiles_max(a.T, a.E, a.k);
   const int n_shared = (a.T + kGM - 1) / kGM;
   if (a.norm_w) launch_rmsnorm(a.resid, a.norm_w, a.eps, a.normed, a.T, stream, launch);
-  launch(prefill_router_kernel, dim3(nb), dim3(kThreads), stream, a);
+  launch(prefill_router_kernel, dim3(nb), dim3(kRouterThreads), stream, a);
   launch(prefill_bucket_kernel, dim3(nb), dim3(kBucketThreads), stream, a, nb);
   // The grouped GEMMs' grids cover the longest possible tile list; the
   // kernels read the real one.
