@@ -151,3 +151,45 @@ def test_nvfp4_block_matches_oracle(dev4, T, x_seed):
     g = grade_block(sg.bf16_bits(out), ids.cpu().numpy(), res, tol=TOL_NVFP4)
     print(g)
     assert g.ok, str(g)
+
+
+@pytest.mark.parametrize("E,k", [(64, 8), (32, 1)])
+def test_nvfp4_other_expert_counts(E, k):
+    """Expert counts and top-k other than Flint's with NVFP4 weights, at the
+    batch sizes of the small-batch down kernel (eight active experts per
+    wave at T k > 48, six below) and past it."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_expert_gemv_amd as sg
+    from synth import LayerShape
+    say(f"nvfp4 layer E={E} k={k}")
+    syn = SyntheticLayer(5, LayerShape(n_experts=E, top_k=k))
+    syn.routed_banks()
+    q = nvfp4_layer(syn)
+    t = upload_nvfp4(syn, q, "cuda")
+
+    def bank(name):
+        return sg.DeviceBank(t[f"{name}_w13_q"], t[f"{name}_w2_q"], t[f"{name}_w13_s"],
+                             t[f"{name}_w2_s"], t[f"{name}_w13_g"], t[f"{name}_w2_g"])
+
+    W = sg.DeviceWeights(t["router_w"], None, bank("routed"), bank("shared"))
+
+    def raw(e):
+        b, i = ("shared", 0) if e < 0 else ("routed", e)
+        d = q[b]
+        return ((d["w13_q"][i], d["w13_s"][i], d["w13_g"][i]),
+                (d["w2_q"][i], d["w2_s"][i], d["w2_g"][i]))
+
+    L = OracleLayer(2048, E, k, 512, syn.router_w(), None, raw, fmt="nvfp4")
+    moe = sg.FlintMoE(n_experts=E, top_k=k, max_tokens=16, fmt=sg.FLINT_W_NVFP4)
+    for T in (2, 5, 7, 8, 13):
+        say(f"  nvfp4 E={E} k={k} T={T}")
+        xb = make_x(T, seed=5, x_seed=T)
+        x = sg.bf16_tensor(xb, "cuda")
+        out = torch.empty_like(x)
+        ids = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+        moe.forward(W, x, out, ids, None, moe.new_workspace(T, "cuda"))
+        torch.cuda.synchronize()
+        g = grade(sg.bf16_bits(out), ids.cpu().numpy(), moe_forward(L, xb), tol=TOL_NVFP4)
+        print(g)
+        assert g.ok, f"E={E} k={k} T={T}: {g}"
