@@ -7,10 +7,11 @@
 // RMSNorm of r into the workspace buffer `normed` comes first, one wave per
 // token):
 //   1. router  : logits[32 tokens x 256] = X Wr^T per block (bf16 MFMA, fp32
-//                accumulate, + bias), then in the epilogue the top-k of each
-//                token by sigmoid score (a wave ranks four tokens at a time
-//                from the logits parked in LDS), the routing weights, and the
-//                block's per-expert slot counts.
+//                accumulate, + bias; four waves, four more keeping their
+//                barriers), then in the epilogue the top-k of each token by
+//                sigmoid score (each of the eight waves ranks four tokens at a
+//                time from the logits parked in LDS), the routing weights,
+//                and the block's per-expert slot counts.
 //   2. bucket  : every block sums the router blocks' counts, scans them into
 //                expert offsets and places its own (token, rank) slots in
 //                stable order (ascending slot within an expert); block 0
@@ -19,14 +20,17 @@
 //                stored); the inverse permutation is kept for the combine.
 //   3. gate/up : grouped GEMM per (256-slot tile, 128 h columns): gathered x
 //                rows times the gate and up rows of w13 (bf16 MFMA), SiLU-and-
-//                mul in registers, h stored as fp16 in sorted slot order (the
-//                shared expert's tiles cover the tokens in order).
+//                mul in registers, h parked in LDS and stored as fp16 in
+//                sorted slot order (the shared expert's tiles cover the tokens
+//                in order).
 //   4. down    : grouped GEMM per (routed 256-slot tile, 256 output columns):
 //                h (fp16) times w2 (bf16 converted to fp16 in registers) into
-//                the unweighted fp16 y of each slot.
+//                the unweighted fp16 y of each slot, the whole tile parked in
+//                LDS and stored as 16-byte vectors.
 //   5. shared down + combine : the shared expert's down GEMM per (256
 //                tokens, 256 columns) whose epilogue adds sum_j w_j * y_j in
-//                rank order (+ r for the block) and rounds once to bf16.
+//                rank order (+ r for the block) and rounds once to bf16, the
+//                next 8-column unit's y rows in flight while one is summed.
 // All GEMMs share one block-level scheme (BlockGemm): A and B tiles move
 // from global memory straight into LDS (LDS-direct loads, no register
 // staging) through one ring per operand, with rows' 16-byte chunks
@@ -37,7 +41,8 @@
 // 64-byte chunks with two stages of h and four of w2; the router and the
 // shared-expert down + combine three and three of 64 (router: 128) bytes.
 // The grouped GEMMs run 256 x 256 block tiles on eight waves of 64 x 128
-// (32x32x16 MFMAs); the router 32 x 256 on four waves of 32 x 64.
+// (32x32x16 MFMAs); the router 32 x 256 on four waves of 32 x 64 (of the
+// block's eight).
 // Numerics: fp32 accumulation everywhere.  h and y cross the launches as
 // fp16 (11-bit significand) carrying a power-of-two bias: h is stored as
 // fp16(h * 2^-8), so the down GEMMs produce y * 2^-8, which the routed down
