@@ -26,6 +26,10 @@
 //                read once; the partial dot products meet in LDS and combine
 //                as out = shared + sum_j w_j * routed_j (+ r for the
 //                pre-norm block) in a fixed order, rounded once to bf16.
+//                NVFP4 with 2 <= T <= 8: down_small_kernel, the same blocks
+//                with each wave's share of the table read into registers,
+//                the h rows parked in LDS and all of the wave's experts'
+//                codes in flight at once.
 // The one hand-off inside a launch (router blocks -> routing block) uses a
 // completion ticket in the workspace header and coherent (write-through)
 // stores/loads, never whole-cache flushes; between launches the stream
