@@ -88,6 +88,25 @@ def test_prefill_t8192_full(flint_bf16):
     np.testing.assert_array_equal(r2["out"], r["out"])
 
 
+def test_prefill_ragged_beyond_the_workload(flint_bf16):
+    """T = 12289 = 3 * 4096 + 1: half again the prefill workload and a multiple
+    of no tile (32-token router blocks, 256-slot M-tiles, the bucketing's
+    token parts), so every launch ends on a ragged tile.  Every token against
+    the expert-grouped oracle."""
+    T = 12289
+    say("prefill T=12289: ragged tiles beyond the 8K workload")
+    xb = make_x(T, seed=0, x_seed=7)
+    r = run(flint_bf16, xb, max_tokens=T)
+    G = moe_forward_grouped(flint_bf16["L"], xb)
+    keep = G.gaps >= 1e-5
+    assert np.array_equal(r["ids"][keep], G.ids[keep])
+    np.testing.assert_allclose(r["w"][keep], G.weights[keep], rtol=2e-6, atol=1e-7)
+    g = grade_arrays(r["out"], r["ids"], G.out, G.ids, G.gaps, tol=TOL_BF16)
+    print(g)
+    assert g.ok, str(g)
+    assert g.n_graded == int(keep.sum())
+
+
 def test_prefill_multi_tile_groups(flint_bf16):
     """Skewed routing (the router bias): slot groups that span several
     256-slot M-tiles (the largest has over 1300 slots).  Every token against
