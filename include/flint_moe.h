@@ -172,6 +172,10 @@ flint_status flint_moe_workspace_layout(const flint_moe_ctx* ctx, int32_t T,
  *   workspace device, >= flint_moe_workspace_bytes(ctx, T) bytes, 256-byte aligned
  *   stream    hipStream_t (passed as void*; NULL = the null stream)
  * T == 0 is a no-op returning FLINT_OK.  T < 0 or T > max_tokens: INVALID_ARG.
+ * NULL or misaligned pointers, overlapping x and out, and (NVFP4) a NULL scale
+ * or tensor-scale pointer: INVALID_ARG.  workspace_bytes below
+ * flint_moe_workspace_bytes(ctx, T): FLINT_ERR_WORKSPACE.  NVFP4 weights with
+ * T > 64: FLINT_ERR_UNSUPPORTED (the NVFP4 kernels are the decode-sized ones).
  * NaN/Inf inputs are not checked. */
 flint_status flint_moe_forward(flint_moe_ctx* ctx, const flint_moe_weights* w,
                                const uint16_t* x, int32_t T, uint16_t* out,
