@@ -37,8 +37,11 @@ def forward(sg, moe, W, xb, k):
     return sg.bf16_bits(out), ids.cpu().numpy()
 
 
-@pytest.mark.parametrize("E,k", [(64, 8), (32, 1), (128, 4)])
+@pytest.mark.parametrize("E,k", [(64, 8), (32, 1), (128, 4), (8, 8), (1, 1)])
 def test_other_expert_counts(E, k):
+    """Other (E, k) than Flint's, through every routing path; (8, 8) selects
+    every expert (k = E: the top-k keeps all of them, ranked), (1, 1) has a
+    single routed expert that every token takes with weight 1."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import sparse_expert_gemv_amd as sg
