@@ -153,11 +153,11 @@ def test_nvfp4_block_matches_oracle(dev4, T, x_seed):
     assert g.ok, str(g)
 
 
-@pytest.mark.parametrize("E,k", [(64, 8), (32, 1)])
+@pytest.mark.parametrize("E,k", [(64, 8), (32, 1), (8, 8)])
 def test_nvfp4_other_expert_counts(E, k):
     """Expert counts and top-k other than Flint's with NVFP4 weights, at the
     batch sizes of the small-batch down kernel (eight active experts per
-    wave at T k > 48, six below) and past it."""
+    wave at T k > 48, six below) and past it; (8, 8) selects every expert."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import sparse_expert_gemv_amd as sg
