@@ -25,33 +25,8 @@ def say(msg):
 
 
 @pytest.fixture(scope="module")
-def dev4():
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import sparse_expert_gemv_amd as sg
-    say("generating and encoding the NVFP4 layer")
-    syn = SyntheticLayer(SEED)
-    syn.routed_banks()
-    q = nvfp4_layer(syn)
-    t = upload_nvfp4(syn, q, "cuda", with_bias=True)
-
-    def bank(name):
-        return sg.DeviceBank(t[f"{name}_w13_q"], t[f"{name}_w2_q"], t[f"{name}_w13_s"],
-                             t[f"{name}_w2_s"], t[f"{name}_w13_g"], t[f"{name}_w2_g"])
-
-    W = sg.DeviceWeights(t["router_w"], None, bank("routed"), bank("shared"))
-    Wb = sg.DeviceWeights(t["router_w"], t["router_b"], bank("routed"), bank("shared"))
-
-    def raw(e):
-        b, i = ("shared", 0) if e < 0 else ("routed", e)
-        d = q[b]
-        return ((d["w13_q"][i], d["w13_s"][i], d["w13_g"][i]),
-                (d["w2_q"][i], d["w2_s"][i], d["w2_g"][i]))
-
-    L = OracleLayer(2048, 256, 6, 512, syn.router_w(), None, raw, fmt="nvfp4")
-    Lb = OracleLayer(2048, 256, 6, 512, syn.router_w(), syn.router_bias(), raw, fmt="nvfp4")
-    L16 = OracleLayer(2048, 256, 6, 512, syn.router_w(), None, syn.expert)
-    return dict(sg=sg, W=W, Wb=Wb, L=L, Lb=Lb, L16=L16, t=t)
+def dev4(flint_nvfp4):
+    return flint_nvfp4
 
 
 def run4(dev4, xb, bias=False):
