@@ -10,7 +10,10 @@ process: decode T=1, T=8 (the headline `value`) and T=32 with skewed routing
 (bf16), NVFP4 weights at T=1 and T=8, and the T=8192 prefill.  Each lands in
 `per_config` with its µs per layer, tokens/s, the layer's algorithmic GB/s
 and fraction of the 8 TB/s HBM peak, its per-kernel times and the roofline of
-its dominant launch.  `--workload NAME` measures one configuration alone.
+its dominant launch.  The low-latency decode path (attention output
+projection, residual, norms and the layer; three launches and five) is measured
+at T=1 and T=8 over bf16 and over NVFP4 experts.  `--workload NAME` measures
+one configuration alone.
 
 To measure HBM rather than the 256 MB Infinity Cache, the layer is cloned
 into several device copies and step i runs on copy i mod copies.  The K
@@ -608,17 +611,17 @@ LOWLAT_NAMES = {True: ["oproj_route", "gateup", "down_nextnorm"],
                 False: ["oproj", "route", "gateup", "down", "nextnorm"]}
 
 
-def measure_lowlat(args, T, structs, wo_copies, dev, syn):
+def measure_lowlat(args, T, structs, wo_copies, dev, syn, fmt="bf16"):
     """The low-latency decode path (attention output projection + residual +
     norm + layer + residual + next norm) at T tokens, fused (three launches)
-    and in five launches; returns a per-config entry."""
+    and in five launches, over bf16 or NVFP4 experts; returns a per-config entry."""
     import numpy as np
     import torch
 
     import sparse_expert_gemv_amd as sg
     from synth import make_attn, make_next_gain, make_residual
 
-    moe = sg.FlintMoE(max_tokens=8)
+    moe = sg.FlintMoE(max_tokens=8, fmt=sg.FLINT_W_NVFP4 if fmt == "nvfp4" else sg.FLINT_W_BF16)
     d = lambda b: sg.bf16_tensor(b, dev)
     attn = d(make_attn(T, seed=args.seed, x_seed=0))
     r = d(make_residual(T, seed=args.seed, x_seed=0))
@@ -629,7 +632,8 @@ def measure_lowlat(args, T, structs, wo_copies, dev, syn):
     ws = moe.new_workspace(T, dev)
     P = lambda t: int(t.data_ptr())
     wos = [P(w) for w in wo_copies]
-    entry = {"workload": f"flint_moe_lowlat_t{T}", "T": T, "weights": "bf16",
+    tag = "nvfp4_" if fmt == "nvfp4" else ""
+    entry = {"workload": f"flint_moe_lowlat_{tag}t{T}", "T": T, "weights": fmt,
              "path": "r1 = r + Wo a; n = RMSNorm(r1) g; r_out = r1 + MoE(n); "
                      "n_out = RMSNorm(r_out) g_next"}
     stream = torch.cuda.current_stream(dev)
@@ -661,8 +665,8 @@ def measure_lowlat(args, T, structs, wo_copies, dev, syn):
                       "kernels_us": {n: round(float(v), 3) for n, v in zip(names, kern_us)},
                       "eager_wall_us_per_step": round(eager_us, 2)}
         entry["n_active"] = n_active
-        log(f"lowlat T={T} {key}: {us:.2f} us/step over {len(names)} launches")
-    w13_bytes, w2_bytes = EXPERT_BYTES["bf16"]
+        log(f"lowlat {fmt} T={T} {key}: {us:.2f} us/step over {len(names)} launches")
+    w13_bytes, w2_bytes = EXPERT_BYTES[fmt]
     entry["algorithmic_bytes"] = (H * 4096 * 2 + ROUTER_BYTES + (entry["n_active"] + 1) *
                                   (w13_bytes + w2_bytes) + T * (4096 + 4 * H) * 2 + 2 * H * 2)
     entry["fused_speedup"] = round(entry["unfused"]["us_per_step"] / entry["fused"]["us_per_step"], 3)
@@ -745,13 +749,15 @@ def main():
         for n in todo:
             structs = weight_structs(sg, copies, fmt, WORKLOADS[n]["bias"])
             entries[n] = measure(args, n, structs, dev, gamma, inputs[n])
-        if fmt == "bf16" and (args.workload == "suite" or args.lowlat) and not args.block:
+        if (args.workload == "suite" or args.lowlat) and not args.block:
             from synth import make_o_proj
             wo0 = sg.bf16_tensor(make_o_proj(seed=args.seed), dev)
             wo_copies = [wo0] + [wo0.clone() for _ in range(1, len(copies))]
-            structs = weight_structs(sg, copies, "bf16", False)
+            structs = weight_structs(sg, copies, fmt, False)
+            tag = "nvfp4_" if fmt == "nvfp4" else ""
             for T in (1, 8):
-                entries[f"lowlat_t{T}"] = measure_lowlat(args, T, structs, wo_copies, dev, syn)
+                entries[f"lowlat_{tag}t{T}"] = measure_lowlat(args, T, structs, wo_copies, dev, syn,
+                                                              fmt)
             del wo_copies, wo0
         del copies
         torch.cuda.empty_cache()

@@ -1836,6 +1836,20 @@ hipError_t launch_dense_decode(const DenseArgs& a, hipStream_t stream, Launcher&
   return hipGetLastError();
 }
 
+// The down launch for a decode-sized batch: the small-batch kernel for
+// NVFP4 weights at 2 <= T <= 8, the cached-entry form above T = 8 tokens.
+template <bool kFp4>
+static void launch_down(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
+  if (a.T > kRouteBareMinT)
+    launch(down_kernel<kFp4, true>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  else if (down_small_applies(a.T, kFp4) && down_small_slots(a.T, a.k) == 6)
+    launch(down_small_kernel<6>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  else if (down_small_applies(a.T, kFp4))
+    launch(down_small_kernel<8>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  else
+    launch(down_kernel<kFp4, false>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+}
+
 template <bool kFp4>
 static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Launcher& launch) {
   const int n_router = (a.E + kRouterRows - 1) / kRouterRows;
@@ -1856,14 +1870,7 @@ static hipError_t launch_decode_impl(const LayerArgs& a, hipStream_t stream, Lau
       launch(route_kernel<false, false>, g_route, dim3(route_threads(false, false)), stream, a);
     launch(gateup_kernel<kFp4, false>, g_gateup, dim3(kThreads), stream, a);
   }
-  if (a.T > kRouteBareMinT)
-    launch(down_kernel<kFp4, true>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
-  else if (down_small_applies(a.T, kFp4) && down_small_slots(a.T, a.k) == 6)
-    launch(down_small_kernel<6>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
-  else if (down_small_applies(a.T, kFp4))
-    launch(down_small_kernel<8>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
-  else
-    launch(down_kernel<kFp4, false>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+  launch_down<kFp4>(a, stream, launch);
   return hipGetLastError();
 }
 
@@ -1884,11 +1891,11 @@ static hipError_t launch_lowlat_impl(const LayerArgs& a, bool fused, hipStream_t
   }
   launch(gateup_kernel<kFp4, false>, dim3(kUnitsPerExpert + n_routed), dim3(kThreads), stream, a);
   if (fused) {
-    launch(down_kernel<kFp4, false>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, a);
+    launch_down<kFp4>(a, stream, launch);
   } else {
     LayerArgs b = a;
     b.norm_next_w = nullptr;
-    launch(down_kernel<kFp4, false>, dim3(H / kDownRowsPerBlock), dim3(kDownThreads), stream, b);
+    launch_down<kFp4>(b, stream, launch);
     if (a.norm_next_w) launch_rmsnorm(a.out, a.norm_next_w, a.eps, a.normed_next, a.T, stream, launch);
   }
   return hipGetLastError();
