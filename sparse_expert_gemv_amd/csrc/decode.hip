@@ -1158,7 +1158,6 @@ struct DownRows<true> {
 template <bool kFp4, bool kCached>
 __device__ __forceinline__ void prefetch_entry(DownRows<kFp4>& p, const LayerArgs& a, const DownItem& d,
                                                int r0, const int16_t* s_slots) {
-  const int lane = threadIdx.x & (kWave - 1);
   p.template load<kCached>(a, d, r0);
   // Entries past nj re-read slot 0's h (in bounds, unused).
 #pragma unroll

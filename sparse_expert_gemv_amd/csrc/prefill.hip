@@ -108,8 +108,6 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-
 // Accumulator element r of lane l in a 32x32 MFMA tile: row (r / 4) * 8 +
 // (l / 32) * 4 + r % 4, column l % 32.  A and B operands: lane l supplies row
 // (column) l % 32 with K elements [(l / 32) * 8, +8) of each 16-wide K step.
@@ -466,7 +464,7 @@ __global__ __launch_bounds__(kRouterThreads) void prefill_router_kernel(LayerArg
   __shared__ __attribute__((aligned(16))) uint8_t lds[cmax(RouterGemm::kLds, kMT * kZRow * 4)];
   __shared__ int hist[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = a.T, E = a.E, k = a.k;
+  const int T = a.T, E = a.E;
   const int t0 = blockIdx.x * kMT;
   for (int i = tid; i < kMaxExperts; i += kRouterThreads) hist[i] = 0;
   const bool gemm = wave < RouterGemm::NW;
